@@ -1,0 +1,177 @@
+/*
+ * dynconv.h -- C ABI of the MI355X (gfx950) dynamic short convolution
+ * library, libdynconv.so.
+ *
+ * The layer ("Dynamic Short Convolutions Improve Transformers", gist.science
+ * Technical Summary, Methodology -> Dynamic Short Convolutions):
+ *   - Mechanism: the output at position t is a causal depthwise convolution
+ *     of width k whose taps w_t are specific to position t and channel c;
+ *     tap j multiplies the input j positions back.
+ *   - Parameterization: w_t is a learned linear map of the current hidden
+ *     state h_t, either low-rank (w_t = z_t U with z_t = h_t A) or head-wise
+ *     (one k-tap filter per head, shared by that head's consecutive
+ *     channels).  A static per-channel bias w0[D,k] is added to the
+ *     generated filter, so the layer contains the static short convolution
+ *     as the special case of a zero generator.
+ *   - Placement: the result is added back residually.
+ * Together, for every batch row b, token t and channel c:
+ *
+ *   y[b,t,c] = x[b,t,c] + sum_{j=0}^{k-1} [t-j >= 0] w[b,t,c,j] * x[b,t-j,c]
+ *   w[b,t,c,j] = u[b,t,head(c),j] + w0[c,j]        head-wise, head(c) = c / (D/n_heads)
+ *   w[b,t,c,j] = sum_q z[b,t,q] U[q, c*k+j] + w0[c,j],  z = h A   low-rank
+ *   u[b,t,e,j] = sum_i h[b,t,i] W[i, e*k+j]
+ *
+ * Tokens before the start of each sequence count as zero and nothing
+ * crosses batch rows.  The filter w is never written to memory (the
+ * Efficient Training Implementation section's Fused Low-Rank Kernel item
+ * describes the same: the product zU is formed on chip).
+ *
+ * The backward (dynconv_bwd) is the exact gradient of L = sum(dy * y):
+ *   dx[s,c] = dy[s,c] + sum_j [s+j <= T-1] w[s+j,c,j] dy[s+j,c]
+ *   G[t,c,j] = [t-j >= 0] dy[t,c] x[t-j,c],  dw0 = sum_{b,t} G
+ *   head-wise: du[t,e,j] = sum_{c in e} G[t,c,j], dW = sum_t h_t^T du_t, dh = du W^T
+ *   low-rank : dz[t,q] = sum_{c,j} G[t,c,j] U[q,c*k+j], dU = sum_t z_t^T G_t,
+ *              dA = sum_t h_t^T dz_t, dh = dz A^T
+ *
+ * Layout: every tensor is row-major and contiguous.
+ *   h[B,T,d_model], x, y, dy, dx [B,T,D], W[d_model, n_heads*k] (column e*k+j),
+ *   A[d_model, rank], U[rank, D*k] (column c*k+j), w0[D,k].
+ *   gen_cache: fp32 [B*T, n_heads*k] (u) or [B*T, rank] (z).
+ * Precision: activations, generator weights and w0 are in the I/O dtype
+ *   (fp32 or bf16); every sum accumulates in fp32; dx and dh are written in
+ *   the I/O dtype with round-to-nearest-even; weight gradients are fp32.
+ *
+ * Ownership and execution: the caller owns every buffer; all pointers are
+ * device pointers except the three structs, which are read on the host
+ * during the call only.  The library never allocates or frees device
+ * memory, never copies between host and device and never synchronises: a
+ * call validates its arguments on the host and then only enqueues kernels
+ * on `stream`, so it returns before the work is done.  Inputs are read-only.
+ * Outputs must not overlap any input or each other.  The workspace must
+ * not be used by anything else until the enqueued work has finished.
+ * Results are bitwise deterministic for fixed inputs and shapes (no float
+ * atomics; every reduction runs in a fixed order).  The library is
+ * thread-safe; its only global state is a cached device-property query.
+ *
+ * Errors: every call returns DYNCONV_OK (0) or a negative status.  Argument
+ * errors are detected on the host before anything is enqueued, and the
+ * outputs are then untouched.  DYNCONV_E_HIP reports a failed launch; a
+ * fault during kernel execution surfaces at the caller's next
+ * synchronisation.  B*T == 0 is a no-op returning DYNCONV_OK.  No C++
+ * exception crosses this interface and nothing is printed.
+ */
+#ifndef DYNCONV_H
+#define DYNCONV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DYNCONV_ABI_VERSION 1
+
+#ifndef DYNCONV_API
+#define DYNCONV_API __attribute__((visibility("default")))
+#endif
+
+/* I/O dtype.  Accumulation is fp32 for both. */
+typedef enum { DYNCONV_FP32 = 0, DYNCONV_BF16 = 1 } dynconv_dtype;
+
+/* Filter-generator parameterisation. */
+typedef enum { DYNCONV_HEADWISE = 0, DYNCONV_LOWRANK = 1 } dynconv_kind;
+
+enum {
+  DYNCONV_OK = 0,
+  DYNCONV_E_NULL = -1,      /* a required pointer is NULL                        */
+  DYNCONV_E_SHAPE = -2,     /* a size <= 0 (B, T may be 0), D % n_heads != 0,    */
+                            /* rank <= 0, or D / d_model not a multiple of the    */
+                            /* 16-byte vector (8 bf16 or 4 fp32 channels)         */
+  DYNCONV_E_K = -3,         /* k outside [1, 8]                                   */
+  DYNCONV_E_DTYPE = -4,     /* dtype or kind not one of the enums                 */
+  DYNCONV_E_ALIGN = -5,     /* a tensor pointer not 16-byte aligned               */
+  DYNCONV_E_ALIAS = -6,     /* an output overlaps an input or another output      */
+  DYNCONV_E_WORKSPACE = -7, /* workspace NULL or smaller than required            */
+  DYNCONV_E_HIP = -8,       /* a kernel launch failed                             */
+  DYNCONV_E_LIMIT = -9      /* a size exceeds what the kernels index (see below)  */
+};
+
+/* Problem sizes.  B*T tokens, hidden width d_model, D convolved channels,
+ * filter width k (1..8).  Limits: B*T*max(D, d_model) < 2^31 elements per
+ * tensor; n_heads*k and rank <= 256 (rank <= 64 on the bf16 path). */
+typedef struct {
+  int64_t B, T, d_model, D;
+  int32_t k;
+  int32_t dtype; /* dynconv_dtype */
+} dynconv_problem;
+
+/* Generator weights (device pointers, I/O dtype). */
+typedef struct {
+  int32_t kind;    /* dynconv_kind                                  */
+  int32_t n_heads; /* head-wise: number of heads, D % n_heads == 0  */
+  int32_t rank;    /* low-rank: rank r                              */
+  int32_t reserved;
+  const void *W;  /* head-wise [d_model, n_heads*k]; unused otherwise */
+  const void *A;  /* low-rank [d_model, rank]; unused otherwise       */
+  const void *U;  /* low-rank [rank, D*k]; unused otherwise           */
+  const void *w0; /* static bias [D, k], or NULL for none             */
+} dynconv_gen;
+
+/* Weight gradients, fp32 device pointers, overwritten (not accumulated).
+ * Head-wise needs dW; low-rank needs dA and dU.  dw0 may be NULL to skip. */
+typedef struct {
+  float *dW;  /* [d_model, n_heads*k] */
+  float *dA;  /* [d_model, rank]      */
+  float *dU;  /* [rank, D*k]          */
+  float *dw0; /* [D, k]               */
+} dynconv_gen_grad;
+
+/*
+ * Forward: y = x + dynconv(x) (see the header comment).
+ *   h, x      inputs, I/O dtype, [B,T,d_model] and [B,T,D]
+ *   y         output, I/O dtype, [B,T,D]
+ *   gen_cache NULL, or an fp32 buffer of dynconv_gen_cache_bytes() that
+ *             receives u = h W (head-wise) or z = h A (low-rank) for reuse
+ *             by dynconv_bwd with the same inputs and weights
+ *   workspace device scratch of at least dynconv_workspace_bytes(p, g, 0)
+ */
+DYNCONV_API int dynconv_fwd(const dynconv_problem *p, const dynconv_gen *g, const void *h, const void *x,
+                void *y, void *gen_cache, void *workspace, size_t workspace_bytes,
+                hipStream_t stream);
+
+/*
+ * Backward of L = sum(dy * y) for the forward above.
+ *   h, x, dy  inputs (I/O dtype); dy is [B,T,D]
+ *   gen_cache the cache a dynconv_fwd with the same inputs filled, or NULL
+ *             to recompute it
+ *   dx        output [B,T,D], I/O dtype
+ *   dh        output [B,T,d_model], I/O dtype, or NULL to skip
+ *   gg        weight gradients (fp32), overwritten
+ *   workspace device scratch of at least dynconv_workspace_bytes(p, g, 1)
+ */
+DYNCONV_API int dynconv_bwd(const dynconv_problem *p, const dynconv_gen *g, const void *h, const void *x,
+                const void *dy, const void *gen_cache, void *dx, void *dh,
+                const dynconv_gen_grad *gg, void *workspace, size_t workspace_bytes,
+                hipStream_t stream);
+
+/* Workspace bytes a pass needs (pass 0 = forward, 1 = backward); 0 on
+ * invalid arguments.  Depends only on the sizes, never on pointers. */
+DYNCONV_API size_t dynconv_workspace_bytes(const dynconv_problem *p, const dynconv_gen *g, int pass);
+
+/* Bytes of the fp32 generator cache (B*T * (n_heads*k or rank) * 4). */
+DYNCONV_API size_t dynconv_gen_cache_bytes(const dynconv_problem *p, const dynconv_gen *g);
+
+/* Static description of a status code; never NULL. */
+DYNCONV_API const char *dynconv_status_str(int status);
+
+/* DYNCONV_ABI_VERSION of the built library. */
+DYNCONV_API int dynconv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DYNCONV_H */

@@ -1,0 +1,153 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerance (max relative error, max|gpu - oracle| / max|oracle| per output
+tensor): 1e-5 for fp32 I/O, 2e-2 for bf16 I/O with fp32 accumulation.
+Covers the five workloads at their full sizes (the launch configuration the
+benchmark times), shapes that span several tiles with ragged tails, and the
+degenerate cases (T = 1, T < k, k = 1, heads narrower than a vector, rank 1,
+no bias).  Bitwise invariants: zero filter gives y == x and dx == dy,
+causality, determinism, cache reuse == recompute.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from tests import gpu_util as gu
+from workloads import HEADWISE, LOWRANK, WORKLOADS, Workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _note(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+SMALL = [
+    Workload("hw_bf16_hd72_ragged", B=2, T=300, d=128, D=360, k=4, kind=HEADWISE, n_heads=5, seed=11),
+    Workload("hw_bf16_hd128_k3", B=1, T=257, d=64, D=1024, k=3, kind=HEADWISE, n_heads=8, seed=12),
+    Workload("hw_bf16_hd68", B=2, T=130, d=96, D=544, k=4, kind=HEADWISE, n_heads=8, seed=13),
+    Workload("hw_bf16_hd8_k2", B=3, T=70, d=32, D=128, k=2, kind=HEADWISE, n_heads=16, seed=14),
+    Workload("hw_bf16_hd4", B=1, T=90, d=16, D=64, k=4, kind=HEADWISE, n_heads=16, seed=15),
+    Workload("hw_bf16_k8_nobias", B=2, T=50, d=48, D=256, k=8, kind=HEADWISE, n_heads=4, seed=16,
+             bias_std=0.0),
+    Workload("hw_fp32_k5", B=2, T=100, d=32, D=48, k=5, kind=HEADWISE, n_heads=3, dtype="fp32", seed=17),
+    Workload("lr_bf16_r16_ragged", B=2, T=300, d=128, D=360, k=4, kind=LOWRANK, rank=16, seed=21),
+    Workload("lr_bf16_r32_k3", B=1, T=200, d=256, D=1024, k=3, kind=LOWRANK, rank=32, seed=22,
+             x_dist="silu_gated"),
+    Workload("lr_bf16_r1_k1", B=2, T=64, d=32, D=64, k=1, kind=LOWRANK, rank=1, seed=23),
+    Workload("lr_bf16_r64_k8", B=1, T=150, d=64, D=256, k=8, kind=LOWRANK, rank=64, seed=24),
+    Workload("lr_bf16_r5_k2_nobias", B=2, T=97, d=40, D=200, k=2, kind=LOWRANK, rank=5, seed=25,
+             bias_std=0.0),
+    Workload("lr_fp32_r8", B=2, T=77, d=32, D=64, k=4, kind=LOWRANK, rank=8, dtype="fp32", seed=26),
+    Workload("hw_bf16_T1", B=3, T=1, d=32, D=64, k=4, kind=HEADWISE, n_heads=4, seed=27),
+    Workload("lr_bf16_T3_lt_k", B=2, T=3, d=32, D=64, k=4, kind=LOWRANK, rank=16, seed=28),
+    Workload("lr_fp32_T2", B=4, T=2, d=8, D=8, k=3, kind=LOWRANK, rank=3, dtype="fp32", seed=29),
+]
+
+
+def _run_and_compare(w: Workload, use_cache=True):
+    _note(f"[parity] {w.name} B={w.B} T={w.T} d={w.d} D={w.D} k={w.k} {w.kind} "
+          f"n_heads={w.n_heads} rank={w.rank} {w.dtype} cache={use_cache}")
+    inp = workloads.generate(w)
+    dev = gu.to_dev(inp)
+    got = gu.gpu_run(w, dev, use_cache=use_cache)
+    del dev
+    ref = gu.oracle_run(w, inp)
+    errs = gu.compare(w, got, ref)
+    _note(f"[parity] {w.name} errors {errs}")
+    return errs
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_parity_small(w):
+    _run_and_compare(w)
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS), ids=list(WORKLOADS))
+def test_parity_full_workload(name):
+    w = WORKLOADS[name]
+    _run_and_compare(w)
+    torch.cuda.empty_cache()
+
+
+def test_parity_recompute_cache():
+    """Backward without the forward's cache recomputes it; results are bitwise equal."""
+    for w in (SMALL[0], SMALL[7]):
+        _note(f"[recompute] {w.name}")
+        dev = gu.to_dev(workloads.generate(w))
+        a = gu.gpu_run(w, dev, use_cache=True)
+        b = gu.gpu_run(w, dev, use_cache=False)
+        for k in a:
+            if a[k] is not None:
+                assert torch.equal(a[k], b[k]), k
+
+
+def test_deterministic():
+    for w in (SMALL[2], SMALL[8]):
+        _note(f"[determinism] {w.name}")
+        dev = gu.to_dev(workloads.generate(w))
+        a = gu.gpu_run(w, dev)
+        b = gu.gpu_run(w, dev)
+        for k in a:
+            if a[k] is not None:
+                assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("w", [SMALL[0], SMALL[6], SMALL[7], SMALL[12]],
+                         ids=["hw_bf16", "hw_fp32", "lr_bf16", "lr_fp32"])
+def test_zero_filter_identity(w):
+    """Zero generator and no bias: y == x and dx == dy bitwise."""
+    _note(f"[identity] {w.name}")
+    w = w.with_(bias_std=0.0)
+    inp = workloads.generate(w)
+    for key in ("W", "U"):
+        if inp.get(key) is not None:
+            inp[key] = torch.zeros_like(inp[key])
+    dev = gu.to_dev(inp)
+    got = gu.gpu_run(w, dev)
+    assert torch.equal(got["y"], dev["x"])
+    assert torch.equal(got["dx"], dev["dy"])
+
+
+@pytest.mark.parametrize("w", [SMALL[2], SMALL[7]], ids=["hw", "lr"])
+def test_causality(w):
+    """Perturbing x and h after token t leaves y up to t bitwise unchanged."""
+    _note(f"[causality] {w.name}")
+    inp = workloads.generate(w)
+    dev = gu.to_dev(inp)
+    y0 = gu.gpu_run(w, dev)["y"]
+    for t in (0, 1, w.T // 2, w.T - 2):
+        d2 = dict(dev)
+        x = dev["x"].clone()
+        h = dev["h"].clone()
+        x[:, t + 1:] += 1.0
+        h[:, t + 1:] -= 0.5
+        d2["x"], d2["h"] = x, h
+        y1 = gu.gpu_run(w, d2)["y"]
+        assert torch.equal(y0[:, : t + 1], y1[:, : t + 1]), t
+        assert not torch.equal(y0[:, t + 1:], y1[:, t + 1:]), t
+
+
+def test_empty_batch():
+    """B*T == 0: the forward is a no-op, the backward writes zero weight gradients."""
+    w = SMALL[7].with_(B=0)
+    inp = workloads.generate(SMALL[7])
+    dev = gu.to_dev(inp)
+    h = dev["h"][:0]
+    x = dev["x"][:0]
+    import input_dependent_depthwise_amd as dc
+    y = dc.dynconv_fwd(h, x, k=w.k, A=dev["A"], U=dev["U"], w0=dev["w0"])
+    assert y.shape == x.shape
+    out = {"dA": torch.full((w.d, w.rank), 7.0, device="cuda"),
+           "dU": torch.full((w.rank, w.D * w.k), 7.0, device="cuda"),
+           "dw0": torch.full((w.D, w.k), 7.0, device="cuda")}
+    g = dc.dynconv_bwd(h, x, x, k=w.k, A=dev["A"], U=dev["U"], w0=dev["w0"], out=out)
+    torch.cuda.synchronize()
+    for k in ("dA", "dU", "dw0"):
+        assert torch.count_nonzero(g[k]).item() == 0, k
