@@ -170,6 +170,26 @@ DYNCONV_API const char *dynconv_status_str(int status);
 /* DYNCONV_ABI_VERSION of the built library. */
 DYNCONV_API int dynconv_abi_version(void);
 
+/* Kernels of the path, as named by dynconv_trace_next. */
+typedef enum {
+  DYNCONV_K_GEN_PROJ = 1, /* u = h W or z = h A                              */
+  DYNCONV_K_FWD_CONV = 2, /* filter formation + causal conv + residual (fwd)  */
+  DYNCONV_K_BWD_CONV = 3, /* dx, filter gradient, du / dz, dU and dw0 parts   */
+  DYNCONV_K_GEN_BWD = 4,  /* dh and the dW / dA parts                         */
+  DYNCONV_K_FINALIZE = 5  /* fixed-order sums of the weight-gradient parts    */
+} dynconv_kernel;
+
+/*
+ * Profiling aid for callers that time one kernel with their own HIP events
+ * (not part of the layer's computation).  Arms a one-shot pair for the
+ * calling host thread: the next dynconv_fwd / dynconv_bwd on this thread
+ * that launches `kernel` records `start` on its stream right before that
+ * launch and `stop` right after it, then disarms.  Passing NULL events
+ * disarms.  Returns DYNCONV_OK, or DYNCONV_E_DTYPE for an unknown kernel.
+ * The events belong to the caller.
+ */
+DYNCONV_API int dynconv_trace_next(int kernel, hipEvent_t start, hipEvent_t stop);
+
 #ifdef __cplusplus
 }
 #endif

@@ -52,7 +52,10 @@ class GenGrad(ctypes.Structure):
 
 # names the C header declares; the CPU tests check each is exported
 EXPORTS = ("dynconv_fwd", "dynconv_bwd", "dynconv_workspace_bytes", "dynconv_gen_cache_bytes",
-           "dynconv_status_str", "dynconv_abi_version")
+           "dynconv_status_str", "dynconv_abi_version", "dynconv_trace_next")
+
+# kernel ids for dynconv_trace_next
+DYNCONV_K_GEN_PROJ, DYNCONV_K_FWD_CONV, DYNCONV_K_BWD_CONV, DYNCONV_K_GEN_BWD, DYNCONV_K_FINALIZE = 1, 2, 3, 4, 5
 
 _lib = None
 
@@ -78,6 +81,8 @@ def lib() -> ctypes.CDLL:
         L.dynconv_status_str.argtypes = [ctypes.c_int]
         L.dynconv_status_str.restype = ctypes.c_char_p
         L.dynconv_abi_version.restype = ctypes.c_int
+        L.dynconv_trace_next.argtypes = [ctypes.c_int, P, P]
+        L.dynconv_trace_next.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -130,6 +135,14 @@ def dynconv_status_str(status: int) -> str:
 
 def dynconv_abi_version() -> int:
     return int(lib().dynconv_abi_version())
+
+
+def dynconv_trace_next(kernel: int, start, stop) -> None:
+    """Arm a one-shot event pair around the next launch of ``kernel`` on this
+    thread (torch.cuda.Event objects, or None to disarm)."""
+    a = None if start is None else start.cuda_event
+    b = None if stop is None else stop.cuda_event
+    _check(lib().dynconv_trace_next(int(kernel), a, b), "dynconv_trace_next")
 
 
 def dynconv_workspace_bytes(prob: Problem, gen: Gen, pass_: int) -> int:

@@ -68,24 +68,31 @@ int check_problem(const dynconv_problem *p, const dynconv_gen *g, Shape &s) {
   return DYNCONV_OK;
 }
 
-// Workspace layout of one pass.
+// Workspace layout of one pass.  Regions start on 256-byte boundaries.
 struct Plan {
-  size_t cache = 0, cache_bytes = 0;  // generator cache slot (when the caller gives none)
-  size_t g = 0, g_bytes = 0;          // du or dz [BT, N] fp32 (backward)
+  size_t cache = 0;  // generator cache slot, fp32 [BT, N] (used when the caller gives none)
+  size_t g = 0;      // du or dz, fp32 [BT, N] (backward, simple path)
+  size_t mt = 0;     // transposed, padded generator weight for the MFMA projection (bf16)
+  size_t uf = 0;     // U and w0 in MFMA fragment order (bf16, low-rank)
   size_t total = 0;
 };
 
-Plan plan(const Shape &s, int pass) {
+inline bool fast_lowrank(const Shape &s, int dtype) {
+  return dtype == DYNCONV_BF16 && s.kind == DYNCONV_LOWRANK && fwd_lowrank_supported(s);
+}
+
+Plan plan(const Shape &s, int dtype, int pass) {
   Plan pl;
   size_t off = 0;
-  pl.cache_bytes = (size_t)s.BT * s.N * sizeof(float);
-  pl.cache = off;
-  off += round_up(pl.cache_bytes);
-  if (pass == 1) {
-    pl.g_bytes = (size_t)s.BT * s.N * sizeof(float);
-    pl.g = off;
-    off += round_up(pl.g_bytes);
-  }
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += round_up(bytes);
+    return at;
+  };
+  pl.cache = take((size_t)s.BT * s.N * sizeof(float));
+  if (pass == 1) pl.g = take((size_t)s.BT * s.N * sizeof(float));
+  if (dtype == DYNCONV_BF16) pl.mt = take(gen_proj_mfma_ws_bytes(s));
+  if (fast_lowrank(s, dtype)) pl.uf = take(fwd_lowrank_ws_bytes(s));
   pl.total = off;
   return pl;
 }
@@ -126,13 +133,35 @@ int check_weights(const Shape &s, const dynconv_gen *g) {
 
 // Generator projection (u = h W or z = h A) into `cache`.
 int gen_proj(const Shape &s, int dtype, const dynconv_gen *g, const void *h, float *cache,
-             hipStream_t st) {
+             void *ws, const Plan &pl, hipStream_t st) {
   const void *M = s.kind == DYNCONV_HEADWISE ? g->W : g->A;
-  if (dtype == DYNCONV_BF16) return simple_gen_proj<bf16>(s, h, M, cache, st);
+  if (dtype == DYNCONV_BF16) return gen_proj_mfma(s, h, M, cache, (char *)ws + pl.mt, st);
   return simple_gen_proj<float>(s, h, M, cache, st);
 }
 
 }  // namespace
+
+// One-shot event pair armed by dynconv_trace_next (per host thread).
+namespace {
+struct Trace {
+  int kernel = 0;
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+thread_local Trace g_trace;
+}  // namespace
+
+bool trace_begin(int kernel, hipStream_t st) {
+  if (g_trace.kernel == 0 || g_trace.kernel != kernel) return false;
+  (void)hipEventRecord(g_trace.start, st);
+  return true;
+}
+
+void trace_end(bool armed, hipStream_t st) {
+  if (!armed) return;
+  (void)hipEventRecord(g_trace.stop, st);
+  g_trace = Trace();
+}
+
 }  // namespace dynconv
 
 using namespace dynconv;
@@ -140,6 +169,18 @@ using namespace dynconv;
 extern "C" {
 
 int dynconv_abi_version(void) { return DYNCONV_ABI_VERSION; }
+
+int dynconv_trace_next(int kernel, hipEvent_t start, hipEvent_t stop) {
+  if (!start || !stop) {
+    g_trace = Trace();
+    return DYNCONV_OK;
+  }
+  if (kernel < DYNCONV_K_GEN_PROJ || kernel > DYNCONV_K_FINALIZE) return DYNCONV_E_DTYPE;
+  g_trace.kernel = kernel;
+  g_trace.start = start;
+  g_trace.stop = stop;
+  return DYNCONV_OK;
+}
 
 const char *dynconv_status_str(int status) {
   switch (status) {
@@ -166,7 +207,7 @@ size_t dynconv_gen_cache_bytes(const dynconv_problem *p, const dynconv_gen *g) {
 size_t dynconv_workspace_bytes(const dynconv_problem *p, const dynconv_gen *g, int pass) {
   Shape s;
   if ((pass != 0 && pass != 1) || check_problem(p, g, s) != DYNCONV_OK) return 0;
-  return plan(s, pass).total;
+  return plan(s, p->dtype, pass).total;
 }
 
 int dynconv_fwd(const dynconv_problem *p, const dynconv_gen *g, const void *h, const void *x,
@@ -181,7 +222,7 @@ int dynconv_fwd(const dynconv_problem *p, const dynconv_gen *g, const void *h, c
   const void *ptrs[] = {h, x, y, gen_cache, workspace};
   for (const void *q : ptrs)
     if (q && !aligned16(q)) return DYNCONV_E_ALIGN;
-  const Plan pl = plan(s, 0);
+  const Plan pl = plan(s, p->dtype, 0);
   if (workspace_bytes < pl.total || (pl.total > 0 && !workspace)) return DYNCONV_E_WORKSPACE;
   const int eb = p->dtype == DYNCONV_BF16 ? 2 : 4;
   const Sizes z = sizes(s, eb);
@@ -197,11 +238,18 @@ int dynconv_fwd(const dynconv_problem *p, const dynconv_gen *g, const void *h, c
       if (overlap(outs[a], outs[b])) return DYNCONV_E_ALIAS;
 
   float *cache = gen_cache ? (float *)gen_cache : (float *)((char *)workspace + pl.cache);
-  if ((rc = gen_proj(s, p->dtype, g, h, cache, stream))) return rc;
-  if (p->dtype == DYNCONV_BF16)
+  if ((rc = gen_proj(s, p->dtype, g, h, cache, workspace, pl, stream))) return rc;
+  if (s.kind == DYNCONV_HEADWISE) {
+    rc = p->dtype == DYNCONV_BF16 ? fwd_headwise<bf16>(s, cache, g->w0, x, y, stream)
+                                  : fwd_headwise<float>(s, cache, g->w0, x, y, stream);
+  } else if (fast_lowrank(s, p->dtype)) {
+    void *uf = (char *)workspace + pl.uf;
+    if (!(rc = prep_lowrank_frags(s, g->U, g->w0, uf, stream))) rc = fwd_lowrank(s, cache, uf, x, y, stream);
+  } else if (p->dtype == DYNCONV_BF16) {
     rc = simple_fwd_conv<bf16>(s, cache, g->U, g->w0, x, y, stream);
-  else
+  } else {
     rc = simple_fwd_conv<float>(s, cache, g->U, g->w0, x, y, stream);
+  }
   if (rc) return rc;
   return launch_status();
 }
@@ -234,7 +282,7 @@ int dynconv_bwd(const dynconv_problem *p, const dynconv_gen *g, const void *h, c
   const void *ptrs[] = {h, x, dy, gen_cache, dx, dh, workspace, gg->dW, gg->dA, gg->dU, gg->dw0};
   for (const void *q : ptrs)
     if (q && !aligned16(q)) return DYNCONV_E_ALIGN;
-  const Plan pl = plan(s, 1);
+  const Plan pl = plan(s, p->dtype, 1);
   if (workspace_bytes < pl.total || (pl.total > 0 && !workspace)) return DYNCONV_E_WORKSPACE;
   const int eb = p->dtype == DYNCONV_BF16 ? 2 : 4;
   const Sizes z = sizes(s, eb);
@@ -253,7 +301,7 @@ int dynconv_bwd(const dynconv_problem *p, const dynconv_gen *g, const void *h, c
   const float *cache = (const float *)gen_cache;
   if (!cache) {
     float *c = (float *)((char *)workspace + pl.cache);
-    if ((rc = gen_proj(s, p->dtype, g, h, c, stream))) return rc;
+    if ((rc = gen_proj(s, p->dtype, g, h, c, workspace, pl, stream))) return rc;
     cache = c;
   }
   float *gbuf = (float *)((char *)workspace + pl.g);
