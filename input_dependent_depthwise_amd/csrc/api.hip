@@ -71,14 +71,23 @@ int check_problem(const dynconv_problem *p, const dynconv_gen *g, Shape &s) {
 // Workspace layout of one pass.  Regions start on 256-byte boundaries.
 struct Plan {
   size_t cache = 0;  // generator cache slot, fp32 [BT, N] (used when the caller gives none)
-  size_t g = 0;      // du or dz, fp32 [BT, N] (backward, simple path)
+  size_t g = 0;      // simple path: du or dz, fp32 [BT, N]; fused path: g, bf16 [BT, Np]
   size_t mt = 0;     // transposed, padded generator weight for the MFMA projection (bf16)
-  size_t uf = 0;     // U and w0 in MFMA fragment order (bf16, low-rank)
+  size_t uf = 0;     // U and w0 in filter-MFMA fragment order (bf16, low-rank)
+  size_t udz = 0;    // U in dz-MFMA fragment order (bf16, low-rank backward)
+  size_t gpart = 0;  // per-slice du / dz partials, fp32
+  size_t dup = 0;    // per-range dU partials, fp32
+  size_t dw0p = 0;   // per-range dw0 partials, fp32
+  size_t mp = 0;     // generator weight padded to Np columns (bf16)
+  size_t dmp = 0;    // per-range dW / dA partials, fp32
   size_t total = 0;
 };
 
 inline bool fast_lowrank(const Shape &s, int dtype) {
   return dtype == DYNCONV_BF16 && s.kind == DYNCONV_LOWRANK && fwd_lowrank_supported(s);
+}
+inline bool fast_bwd(const Shape &s, int dtype) {
+  return dtype == DYNCONV_BF16 && bwd_fused_supported(s);
 }
 
 Plan plan(const Shape &s, int dtype, int pass) {
@@ -90,9 +99,22 @@ Plan plan(const Shape &s, int dtype, int pass) {
     return at;
   };
   pl.cache = take((size_t)s.BT * s.N * sizeof(float));
-  if (pass == 1) pl.g = take((size_t)s.BT * s.N * sizeof(float));
   if (dtype == DYNCONV_BF16) pl.mt = take(gen_proj_mfma_ws_bytes(s));
   if (fast_lowrank(s, dtype)) pl.uf = take(fwd_lowrank_ws_bytes(s));
+  if (pass == 1) {
+    if (fast_bwd(s, dtype)) {
+      const BwdLayout L = bwd_layout(s);
+      pl.udz = take(bwd_prep_dz_bytes(s));
+      pl.gpart = take((size_t)L.n_slices * s.BT * L.R * sizeof(float));
+      if (s.kind == DYNCONV_LOWRANK) pl.dup = take((size_t)L.n_ranges * s.N * s.D * s.k * sizeof(float));
+      pl.dw0p = take((size_t)L.n_ranges * s.D * s.k * sizeof(float));
+      pl.g = take(gen_bwd_g_bytes(s));
+      pl.mp = take(gen_bwd_mp_bytes(s));
+      pl.dmp = take(gen_bwd_part_bytes(s));
+    } else {
+      pl.g = take((size_t)s.BT * s.N * sizeof(float));
+    }
+  }
   pl.total = off;
   return pl;
 }
@@ -304,7 +326,30 @@ int dynconv_bwd(const dynconv_problem *p, const dynconv_gen *g, const void *h, c
     if ((rc = gen_proj(s, p->dtype, g, h, c, workspace, pl, stream))) return rc;
     cache = c;
   }
-  float *gbuf = (float *)((char *)workspace + pl.g);
+  char *ws = (char *)workspace;
+  if (fast_bwd(s, p->dtype)) {
+    const BwdLayout L = bwd_layout(s);
+    const GenBwdLayout G = gen_bwd_layout(s);
+    if (s.kind == DYNCONV_LOWRANK) {
+      if ((rc = prep_lowrank_frags(s, g->U, g->w0, ws + pl.uf, stream))) return rc;
+      if ((rc = prep_dz_frags(s, g->U, ws + pl.udz, stream))) return rc;
+    }
+    float *gpart = (float *)(ws + pl.gpart), *dUp = (float *)(ws + pl.dup), *dw0p = (float *)(ws + pl.dw0p);
+    if ((rc = bwd_conv(s, L, cache, ws + pl.uf, ws + pl.udz, g->w0, x, dy, dx, gpart, dUp, dw0p, stream)))
+      return rc;
+    const void *M = s.kind == DYNCONV_HEADWISE ? g->W : g->A;
+    float *dMp = (float *)(ws + pl.dmp);
+    if ((rc = gen_bwd(s, gpart, L.n_slices, L.R, 128, h, M, (bf16 *)(ws + pl.g), (bf16 *)(ws + pl.mp), dh,
+                      dMp, stream)))
+      return rc;
+    const int64_t Dk = s.D * s.k, dN = s.d * s.N;
+    float *dM = s.kind == DYNCONV_HEADWISE ? gg->dW : gg->dA;
+    if ((rc = finalize(dUp, s.kind == DYNCONV_LOWRANK ? gg->dU : nullptr, (int64_t)s.N * Dk, L.n_ranges,
+                       dw0p, gg->dw0, Dk, L.n_ranges, dMp, dM, dN, G.n_ranges, stream)))
+      return rc;
+    return launch_status();
+  }
+  float *gbuf = (float *)(ws + pl.g);
   if (p->dtype == DYNCONV_BF16)
     rc = simple_bwd<bf16>(s, cache, g->W, g->A, g->U, g->w0, h, x, dy, dx, dh, *gg, gbuf, stream);
   else

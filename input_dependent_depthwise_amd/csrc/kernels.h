@@ -39,4 +39,40 @@ size_t fwd_lowrank_ws_bytes(const Shape &s);
 int prep_lowrank_frags(const Shape &s, const void *U, const void *w0, void *Uf, hipStream_t st);
 int fwd_lowrank(const Shape &s, const float *z, const void *Uf, const void *x, void *y, hipStream_t st);
 
+// --- fused backward conv (conv_bwd.hip), bf16 ---
+struct BwdLayout {
+  int KP;        // taps padded to 4 or 8
+  int n_slices;  // 128-channel slices (grid x)
+  int n_tiles;   // 32-token tiles
+  int tpb;       // tiles per block
+  int n_ranges;  // token ranges (grid y)
+  int SL;        // head-wise: head slots per slice
+  int R;         // columns of the per-slice partial (rank, or SL*k)
+};
+BwdLayout bwd_layout(const Shape &s);
+bool bwd_fused_supported(const Shape &s);
+size_t bwd_prep_dz_bytes(const Shape &s);
+int prep_dz_frags(const Shape &s, const void *U, void *Udz, hipStream_t st);
+int bwd_conv(const Shape &s, const BwdLayout &L, const float *gen, const void *Uf, const void *Udz,
+             const void *w0, const void *x, const void *dy, void *dx, float *gpart, float *dUp,
+             float *dw0p, hipStream_t st);
+
+// --- generator gradients (gen_bwd.hip), bf16 ---
+struct GenBwdLayout {
+  int Np;        // N padded to 16
+  int n_tiles;   // 32-token tiles
+  int n_chunks;  // 64-row chunks of d_model
+  int tpb;       // tiles per block of the dM kernel
+  int n_ranges;  // token ranges of the dM kernel (partials)
+};
+GenBwdLayout gen_bwd_layout(const Shape &s);
+size_t gen_bwd_g_bytes(const Shape &s);
+size_t gen_bwd_mp_bytes(const Shape &s);
+size_t gen_bwd_part_bytes(const Shape &s);
+int gen_bwd(const Shape &s, const float *gpart, int n_slices, int R, int Dt, const void *h,
+            const void *M, bf16 *g, bf16 *Mp, void *dh, float *dMp, hipStream_t st);
+// out_i[e] = sum_p part_i[p][e]; an output may be NULL to skip it.
+int finalize(const float *p0, float *o0, int64_t n0, int np0, const float *p1, float *o1, int64_t n1,
+             int np1, const float *p2, float *o2, int64_t n2, int np2, hipStream_t st);
+
 }  // namespace dynconv
