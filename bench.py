@@ -107,7 +107,25 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--roofline-kernel", default="bwd_conv", choices=["bwd_conv", "fwd_conv"],
                     help="kernel whose roofline is reported (the dominant one by default)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the layer, run --steps device copies of MIB MiB (a plain copy "
+                         "kernel of known size, to scale the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
+
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration * 2**20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / args.steps
+        print(json.dumps({"copy_bytes": n, "steps": args.steps, "ms_per_copy": round(dt * 1e3, 4),
+                          "gbs": round(2 * n / dt / 1e9, 1)}), flush=True)
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
