@@ -339,7 +339,7 @@ int dynconv_bwd(const dynconv_problem *p, const dynconv_gen *g, const void *h, c
       return rc;
     const void *M = s.kind == DYNCONV_HEADWISE ? g->W : g->A;
     float *dMp = (float *)(ws + pl.dmp);
-    if ((rc = gen_bwd(s, gpart, L.n_slices, L.R, 128, h, M, (bf16 *)(ws + pl.g), (bf16 *)(ws + pl.mp), dh,
+    if ((rc = gen_bwd(s, gpart, L.n_slices, L.R, L.Dt, h, M, (bf16 *)(ws + pl.g), (bf16 *)(ws + pl.mp), dh,
                       dMp, stream)))
       return rc;
     const int64_t Dk = s.D * s.k, dN = s.d * s.N;

@@ -76,8 +76,7 @@ template <int KIND, int K, int KQ, int NCB>
 __global__ void __launch_bounds__(kW * 64, 2)
 k_bwd(Params P) {
   constexpr int KP = 4;             // taps padded to 4 in the fragment layouts
-  constexpr int KH = K - 1;         // history rows of x (left halo)
-  constexpr int KHA = KH > 0 ? KH : 1;
+  constexpr int KH = K - 1;         // history rows of x (left halo) = lookahead rows of dy, z, u
   constexpr int GROWS = 16 * KP;    // (channel, tap) rows of one 16-channel group
   constexpr bool LR = KIND == DYNCONV_LOWRANK;
   constexpr int ZW = KQ * 16;       // low-rank: z columns used (rank, bias row, zero padding)
@@ -86,16 +85,16 @@ k_bwd(Params P) {
   constexpr int RB = LR ? 2 * NCB : 4;  // 8-row blocks of the 32x32 dz result that are used
   constexpr int RS = RB * 4 + 4;    // padded lane stride of the reduction buffer (floats)
   constexpr int NT = kW * 64;
+  constexpr int TR = 32 + KH;       // rows of each staged tile
   const Shape &s = P.s;
 
-  __shared__ __attribute__((aligned(16))) unsigned char xs[2][(32 + KH) * kRowB];
-  __shared__ __attribute__((aligned(16))) unsigned char dys[2][32 * kRowB];
+  __shared__ __attribute__((aligned(16))) unsigned char xs[2][TR * kRowB];   // x rows t0-KH .. t0+31
+  __shared__ __attribute__((aligned(16))) unsigned char dys[2][TR * kRowB];  // dy rows t0 .. t0+31+KH
   __shared__ __attribute__((aligned(16))) unsigned char gt[kW][GROWS * kGtRowB];
-  __shared__ __attribute__((aligned(16))) bf16 zs[2][LR ? 32 * ZWP : 8];
+  __shared__ __attribute__((aligned(16))) bf16 zs[2][LR ? TR * ZWP : 8];     // z rows t0 .. t0+31+KH
   __shared__ __attribute__((aligned(16))) unsigned char zt[2][LR ? 32 * kGtRowB : 16];
-  __shared__ __attribute__((aligned(16))) float us[2][LR ? 4 : 32 * UWP];
+  __shared__ __attribute__((aligned(16))) float us[2][LR ? 4 : TR * UWP];    // u rows t0 .. t0+31+KH
   __shared__ __attribute__((aligned(16))) float red[kW][64 * RS];
-  __shared__ __attribute__((aligned(16))) float pc[kW][2][KHA][KHA][2][4];
   __shared__ __attribute__((aligned(16))) float w0s[LR ? 4 : kDt * KP];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -115,7 +114,7 @@ k_bwd(Params P) {
       w0s[e] = (P.w0 && c < nch && j < K) ? (float)P.w0[(cblk + c) * K + j] : 0.f;
     }
   } else {
-    for (int e = threadIdx.x; e < 2 * 32 * ZWP; e += NT) {
+    for (int e = threadIdx.x; e < 2 * TR * ZWP; e += NT) {
       const int q = e % ZWP;
       if (q >= s.rank) (&zs[0][0])[e] = (bf16)(q == s.rank ? 1.f : 0.f);
     }
@@ -127,7 +126,6 @@ k_bwd(Params P) {
 
   // ---- per-lane constants ----
   bf16x8 af[LR ? 2 : 1][KQ];  // filter-MFMA A fragments, quads p = 0, 1 (low-rank)
-  bf16x8 adz[LR ? KP : 1];    // dz-MFMA A fragments (low-rank)
   int sa = 0, nxt = 0;        // head-wise: slot of the lane's first head; next-head mask
   {
     const int64_t gg = (cblk >> 4) + wave;
@@ -139,11 +137,6 @@ k_bwd(Params P) {
           af[p][kq] = glive ? as_bf16x8(*reinterpret_cast<const uint4 *>(
                                   P.Uf + ((gg * 2 + p) * 32 + tl) * (KQ * 16) + kq * 16 + hh * 8))
                             : zero_bf16x8();
-#pragma unroll
-      for (int st = 0; st < KP; ++st)
-        adz[st] = glive ? as_bf16x8(*reinterpret_cast<const uint4 *>(
-                              P.Udz + (((gg * KP + st) * 32 + tl) * 2 + hh) * 8))
-                        : zero_bf16x8();
     } else {
       const int c0 = (int)cblk + cl;
       const int ea = c0 / s.hd;
@@ -163,11 +156,37 @@ k_bwd(Params P) {
       for (int cb = 0; cb < NCB; ++cb) dUacc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // ---- prefetch: x rows (with history) and dy rows as 16-byte chunks; z or u ----
+  // ---- per-thread load slots, fixed for the block ----
   constexpr int CH = kDt / 8;  // 16-byte chunks per full row
-  const int ex = (32 + KH) * CH;
-  constexpr int kVLoads = ((32 + KH + 32) * CH + NT - 1) / NT;
-  constexpr int kSLoads = LR ? (32 * ZW + NT - 1) / NT : (32 * 8 * KP + NT - 1) / NT;
+  constexpr int kVLoads = (2 * TR * CH + NT - 1) / NT;
+  constexpr int SW = LR ? ZW : 8 * KP;  // scalar columns staged per row
+  constexpr int kSLoads = (TR * SW + NT - 1) / NT;
+  // per-thread load slots (constant divisors: cheap to recompute each time)
+  auto vslot = [&](int q, bool &isx, bool &ok, int &row, int &goff, int &loff) {
+    const int e = threadIdx.x + q * NT;
+    isx = e < TR * CH;
+    const int e2 = isx ? e : e - TR * CH;
+    const int r = e2 / CH, c16 = e2 % CH;
+    ok = r < TR && c16 * 8 < nch;
+    row = isx ? r - KH : r;
+    goff = c16 * 8;
+    loff = r * kRowB + c16 * 16;
+  };
+  auto sslot = [&](int q, bool &ok, int &tt, int &col, int &loff) {
+    const int e = threadIdx.x + q * NT;
+    tt = e / SW;
+    const int rem = e % SW;
+    if constexpr (LR) {
+      ok = tt < TR && rem < s.rank;
+      col = rem;
+    } else {
+      const int slot = rem / KP, j = rem % KP;
+      ok = tt < TR && j < K && slot < P.SL && e_base + slot < s.n_heads;
+      col = (e_base + slot) * K + j;
+    }
+    loff = rem;
+  };
+  const int scol_stride = LR ? s.rank : s.N;
   uint4 vpre[kVLoads];
   float spre[kSLoads];
 
@@ -175,199 +194,152 @@ k_bwd(Params P) {
     const int64_t t0 = (int64_t)tile * 32;
 #pragma unroll
     for (int q = 0; q < kVLoads; ++q) {
-      const int e = threadIdx.x + q * NT;
+      bool isx, ok;
+      int rr, goff, loff;
+      vslot(q, isx, ok, rr, goff, loff);
+      const int64_t row = t0 + rr;
       vpre[q] = make_uint4(0, 0, 0, 0);
-      const bool isx = e < ex;
-      const int e2 = isx ? e : e - ex;
-      const int r = e2 / CH, c16 = e2 % CH;
-      const int64_t row = isx ? t0 - KH + r : t0 + r;
-      if (r < (isx ? 32 + KH : 32) && c16 * 8 < nch && row >= 0 && row < s.BT)
-        vpre[q] = *reinterpret_cast<const uint4 *>((isx ? P.x : P.dy) + row * s.D + cblk + c16 * 8);
+      if (ok && row >= 0 && row < s.BT)
+        vpre[q] = *reinterpret_cast<const uint4 *>((isx ? P.x : P.dy) + row * s.D + cblk + goff);
     }
 #pragma unroll
     for (int q = 0; q < kSLoads; ++q) {
-      const int e = threadIdx.x + q * NT;
-      spre[q] = 0.f;
-      if constexpr (LR) {
-        const int tt = e / ZW, qq = e % ZW;
-        const int64_t row = t0 + tt;
-        if (tt < 32 && qq < s.rank && row < s.BT) spre[q] = P.gen[row * s.rank + qq];
-      } else {
-        const int tt = e / (8 * KP), rem = e % (8 * KP);
-        const int slot = rem / KP, j = rem % KP;
-        const int64_t row = t0 + tt;
-        if (tt < 32 && j < K && slot < P.SL && e_base + slot < s.n_heads && row < s.BT)
-          spre[q] = P.gen[row * s.N + (e_base + slot) * K + j];
-      }
+      bool ok;
+      int tt, col, loff;
+      sslot(q, ok, tt, col, loff);
+      const int64_t row = t0 + tt;
+      spre[q] = (ok && row < s.BT) ? P.gen[row * scol_stride + col] : 0.f;
     }
   };
   auto stage = [&](int b) {
 #pragma unroll
     for (int q = 0; q < kVLoads; ++q) {
-      const int e = threadIdx.x + q * NT;
-      const bool isx = e < ex;
-      const int e2 = isx ? e : e - ex;
-      const int r = e2 / CH, c16 = e2 % CH;
-      if (r < (isx ? 32 + KH : 32))
-        *reinterpret_cast<uint4 *>((isx ? xs[b] : dys[b]) + r * kRowB + c16 * 16) = vpre[q];
+      bool isx, ok;
+      int rr, goff, loff;
+      vslot(q, isx, ok, rr, goff, loff);
+      if (ok) *reinterpret_cast<uint4 *>((isx ? xs[b] : dys[b]) + loff) = vpre[q];
     }
 #pragma unroll
     for (int q = 0; q < kSLoads; ++q) {
-      const int e = threadIdx.x + q * NT;
+      bool ok;
+      int tt, col, loff;
+      sslot(q, ok, tt, col, loff);
       if constexpr (LR) {
-        const int tt = e / ZW, qq = e % ZW;
-        if (tt < 32 && qq < s.rank) {
+        if (ok) {
           const bf16 v = (bf16)spre[q];
-          zs[b][tt * ZWP + qq] = v;
-          *reinterpret_cast<bf16 *>(zt[b] + qq * kGtRowB + tt * 2) = v;
+          zs[b][tt * ZWP + loff] = v;
+          if (tt < 32) *reinterpret_cast<bf16 *>(zt[b] + loff * kGtRowB + tt * 2) = v;
         }
       } else {
-        const int tt = e / (8 * KP), rem = e % (8 * KP);
-        if (tt < 32) us[b][tt * UWP + rem] = spre[q];
+        if (tt < TR) us[b][tt * UWP + loff] = spre[q];
       }
     }
   };
 
-  // filter taps of channels 4p..4p+3 of the lane's 8, at tile row tt of buffer b: w[b4][j]
-  auto filter_quad = [&](int b, int p, int tt, float (&w)[4][KP]) {
+  // The backward needs the filter only along its diagonal: tap j at token t+j,
+  // wd[b4][j] = w[t+j][channel 4p+b4][j] (dx is the transposed shift).
+  // Low-rank: one MFMA chain whose K block j multiplies z of token t+j by the
+  // rows of tap j (the lane's A fragment is zeroed unless its row's tap is j),
+  // so accumulator element 4*b4 + j is exactly that diagonal value.
+  auto filter_diag = [&](int b, int p, float (&wd)[4][KP]) {
     if constexpr (LR) {
       f32x16 acc = {};
+      const int rtap = tl & 3;  // tap of the MFMA row this lane feeds
 #pragma unroll
-      for (int kq = 0; kq < KQ; ++kq)
-        acc = mfma32(af[p][kq],
-                     as_bf16x8(*reinterpret_cast<const uint4 *>(&zs[b][tt * ZWP + kq * 16 + hh * 8])), acc);
+      for (int j = 0; j <= KH; ++j) {
+#pragma unroll
+        for (int kq = 0; kq < KQ; ++kq) {
+          const bf16x8 a = rtap == j ? af[p][kq] : zero_bf16x8();
+          acc = mfma32(a, as_bf16x8(*reinterpret_cast<const uint4 *>(&zs[b][(tl + j) * ZWP + kq * 16 + hh * 8])),
+                       acc);
+        }
+        // let ALU and MFMA work move across, but keep each block's LDS reads
+        // next to their MFMAs (hoisting them all costs registers)
+        __builtin_amdgcn_sched_barrier(0x000E);
+      }
 #pragma unroll
       for (int b4 = 0; b4 < 4; ++b4)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) w[b4][r] = acc[4 * b4 + r];
+        for (int r = 0; r < 4; ++r) wd[b4][r] = acc[4 * b4 + r];
     } else {
 #pragma unroll
       for (int b4 = 0; b4 < 4; ++b4) {
         const int i = 4 * p + b4;
         const int slot = sa + ((nxt >> i) & 1);
-        const float4 uv = *reinterpret_cast<const float4 *>(&us[b][tt * UWP + slot * KP]);
         const float4 b0 = *reinterpret_cast<const float4 *>(&w0s[(cl + i) * KP]);
-        w[b4][0] = uv.x + b0.x;
-        w[b4][1] = uv.y + b0.y;
-        w[b4][2] = uv.z + b0.z;
-        w[b4][3] = uv.w + b0.w;
+        const float bj[4] = {b0.x, b0.y, b0.z, b0.w};
+#pragma unroll
+        for (int j = 0; j < KP; ++j)
+          wd[b4][j] = j <= KH ? us[b][(tl + j) * UWP + slot * KP + j] + bj[j] : 0.f;
       }
     }
   };
 
-  // ---- right halo: the products of the tile after this block's range ----
-  if (tile_hi < P.n_tiles) {
-    prefetch(tile_hi);
-    stage(1);
-  }
-  __syncthreads();
-  if (KH > 0 && tl < KH) {
-    const bool have = tile_hi < P.n_tiles;
-    float dyv[8];
-    unpack8(*reinterpret_cast<const uint4 *>(dys[1] + tl * kRowB + cl * 2), dyv);
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      float w[4][KP];
-      filter_quad(1, p, tl, w);
-#pragma unroll
-      for (int j = 1; j <= KH; ++j)
-        *reinterpret_cast<float4 *>(&pc[wave][p][j - 1][tl][hh][0]) =
-            have ? make_float4(w[0][j] * dyv[4 * p], w[1][j] * dyv[4 * p + 1], w[2][j] * dyv[4 * p + 2],
-                               w[3][j] * dyv[4 * p + 3])
-                 : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  }
-
-  if (tile_hi > tile_lo) prefetch(tile_hi - 1);
-
+  if (tile_hi > tile_lo) prefetch(tile_lo);
   int buf = 0;
-  for (int tile = tile_hi - 1; tile >= tile_lo; --tile, buf ^= 1) {
+  for (int tile = tile_lo; tile < tile_hi; ++tile, buf ^= 1) {
     const int64_t t0 = (int64_t)tile * 32;
     const int64_t t = t0 + tl;
     const bool tv = t < s.BT;
-    const int pos = (int)(t % s.T);
+    const int pos = (int)((uint32_t)t % (uint32_t)s.T);  // B*T < 2^31
+    // only waves that touch a sequence start / end need the masks
+    const bool edge_lo = __any(KH > 0 && pos < KH);
+    const bool edge_hi = __any(KH > 0 && pos + KH > s.T - 1);
 
     stage(buf);
     __syncthreads();
-    if (tile - 1 >= tile_lo) prefetch(tile - 1);
+    if (tile + 1 < tile_hi) prefetch(tile + 1);
 
     f32x16 dzacc = {};
     if (glive) {
-      // x history rows, masked where they precede this token's sequence
-      uint4 xr[K];
-#pragma unroll
-      for (int j = 0; j < K; ++j) {
-        xr[j] = *reinterpret_cast<const uint4 *>(xs[buf] + (tl + KH - j) * kRowB + cl * 2);
-        if (j > pos) xr[j] = make_uint4(0, 0, 0, 0);
-      }
-      const uint4 dyraw = *reinterpret_cast<const uint4 *>(dys[buf] + tl * kRowB + cl * 2);
-      float dyv[8];
-      unpack8(dyraw, dyv);
-      // dy as bf16 pairs with one half cleared: G = x * dy by a bf16 dot product
-      uint32_t dylo[4], dyhi[4];
-      {
-        const uint32_t d4[4] = {dyraw.x, dyraw.y, dyraw.z, dyraw.w};
-#pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2) {
-          dylo[w2] = d4[w2] & 0x0000ffffu;
-          dyhi[w2] = d4[w2] & 0xffff0000u;
-        }
-      }
-      bool ok[KHA];
-#pragma unroll
-      for (int j = 1; j <= KH; ++j) ok[j - 1] = tv && pos + j <= s.T - 1 && t + j < s.BT;
       float dxv[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) dxv[i] = dyv[i];
       unsigned char *gtw = gt[wave];
 
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
-        float w[4][KP];
-        filter_quad(buf, p, tl, w);
+        // this quad's 4 channels: x history rows (masked before the sequence start),
+        // dy of this token
+        uint2 xr[K];
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+          xr[j] = *reinterpret_cast<const uint2 *>(xs[buf] + (tl + KH - j) * kRowB + (cl + 4 * p) * 2);
+          if (edge_lo && j > pos) xr[j] = make_uint2(0, 0);
+        }
+        const uint2 dy2 = *reinterpret_cast<const uint2 *>(dys[buf] + tl * kRowB + (cl + 4 * p) * 2);
+        const float dyq[4] = {__uint_as_float(dy2.x << 16), __uint_as_float(dy2.x & 0xffff0000u),
+                              __uint_as_float(dy2.y << 16), __uint_as_float(dy2.y & 0xffff0000u)};
+        float wd[4][KP];
+        filter_diag(buf, p, wd);
         float G[4][KP];
-        float pj[4][KP];
 #pragma unroll
         for (int b4 = 0; b4 < 4; ++b4) {
-          const int i = 4 * p + b4;
+          const uint32_t dword = b4 < 2 ? dy2.x : dy2.y;
+          // dy as a bf16 pair with the other half cleared: G = x * dy by a bf16 dot product
+          const uint32_t dw = (b4 & 1) ? (dword & 0xffff0000u) : (dword & 0x0000ffffu);
 #pragma unroll
           for (int j = 0; j < KP; ++j) {
             if (j < K) {
-              const uint32_t xw = (&xr[j].x)[i >> 1];
-              const uint32_t dw = (i & 1) ? dyhi[i >> 1] : dylo[i >> 1];
+              const uint32_t xw = b4 < 2 ? xr[j].x : xr[j].y;
               G[b4][j] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, xw),
                                                          __builtin_bit_cast(bf16x2_t, dw), 0.f, false);
-              pj[b4][j] = w[b4][j] * dyv[i];
             } else {
               G[b4][j] = 0.f;
-              pj[b4][j] = 0.f;
             }
           }
-          dxv[i] += pj[b4][0];
+          dxv[4 * p + b4] = fmaf(wd[b4][0], dyq[b4], dyq[b4]);
         }
-        // products of the next j tokens, by lane shuffles; the last j lanes take
-        // the values carried from the tile above
+        // dx: tap j of the filter at token t+j times dy there (the transposed shift)
 #pragma unroll
         for (int j = 1; j <= KH; ++j) {
-          float4 prev = make_float4(0.f, 0.f, 0.f, 0.f);
-          if (tl < j) prev = *reinterpret_cast<const float4 *>(&pc[wave][p][j - 1][tl][hh][0]);
-          const int src = hh * 32 + ((tl + j) & 31);
-          const float v0 = __shfl(tl < j ? prev.x : pj[0][j], src);
-          const float v1 = __shfl(tl < j ? prev.y : pj[1][j], src);
-          const float v2 = __shfl(tl < j ? prev.z : pj[2][j], src);
-          const float v3 = __shfl(tl < j ? prev.w : pj[3][j], src);
-          if (ok[j - 1]) {
-            dxv[4 * p + 0] += v0;
-            dxv[4 * p + 1] += v1;
-            dxv[4 * p + 2] += v2;
-            dxv[4 * p + 3] += v3;
+          uint2 dyj2 = *reinterpret_cast<const uint2 *>(dys[buf] + (tl + j) * kRowB + (cl + 4 * p) * 2);
+          if (edge_hi && pos + j > s.T - 1) dyj2 = make_uint2(0, 0);  // next sequence
+#pragma unroll
+          for (int b4 = 0; b4 < 4; ++b4) {
+            const uint32_t word = b4 < 2 ? dyj2.x : dyj2.y;
+            const float dyj = __uint_as_float((b4 & 1) ? (word & 0xffff0000u) : (word << 16));
+            dxv[4 * p + b4] = fmaf(wd[b4][j], dyj, dxv[4 * p + b4]);
           }
         }
-        if (tl < KH)
-#pragma unroll
-          for (int j = 1; j <= KH; ++j)
-            *reinterpret_cast<float4 *>(&pc[wave][p][j - 1][tl][hh][0]) =
-                make_float4(pj[0][j], pj[1][j], pj[2][j], pj[3][j]);
 
         // dz / du: G of this quad is the B operand of steps 2p, 2p+1
 #pragma unroll
@@ -378,7 +350,9 @@ k_bwd(Params P) {
           for (int e8 = 0; e8 < 8; ++e8) bv[e8] = G[2 * sq + e8 / KP][e8 % KP];
           bf16x8 a;
           if constexpr (LR) {
-            a = adz[st];
+            // dz-MFMA A fragment (U in fragment order; small, cache-resident)
+            a = as_bf16x8(*reinterpret_cast<const uint4 *>(
+                P.Udz + ((((cblk >> 4) + wave) * KP + st) * 32 + tl) * 16 + hh * 8));
           } else {
             // 0/1 head membership: row tl = slot*KP + jr, column (channel, tap)
             const int slot = tl / KP, jr = tl % KP;
@@ -530,6 +504,7 @@ k_prep_dz(Shape s, const bf16 *__restrict__ U, bf16 *__restrict__ Udz, int KP) {
 BwdLayout bwd_layout(const Shape &s) {
   BwdLayout L;
   L.KP = s.k <= 4 ? 4 : 8;
+  L.Dt = bwd::kDt;
   L.n_slices = (int)ceil_div(s.D, bwd::kDt);
   L.n_tiles = (int)ceil_div(s.BT, 32);
   // token ranges: as few as keep every block resident in one round (one

@@ -67,87 +67,119 @@ k_prep_frag(Shape s, const bf16 *__restrict__ U, const bf16 *__restrict__ w0, bf
 
 constexpr int kCPW = 2;               // 16-channel groups per wave
 constexpr int kDt = 4 * kCPW * 16;    // channels per block (4 waves)
-constexpr int kTilesPerBlock = 4;     // 32-token tiles a block walks
-constexpr int kRowPad = 16;           // LDS row padding (bytes)
+constexpr int kRowB = kDt * 2 + 16;   // LDS row stride of the x tile (bytes, padded)
 
-template <int KP, int KQ>
+template <int K, int KQ>
 __global__ void __launch_bounds__(256)
 k_fwd_lowrank(Shape s, const float *__restrict__ z, const bf16 *__restrict__ Uf,
-              const bf16 *__restrict__ x, bf16 *__restrict__ y) {
-  constexpr int THP = KP / 4;
-  constexpr int KH = KP - 1;                         // halo rows
-  constexpr int ROWB = kDt * 2 + kRowPad;            // LDS row stride (bytes)
-  __shared__ __attribute__((aligned(16))) unsigned char xs[(32 + KH) * ROWB];
+              const bf16 *__restrict__ x, bf16 *__restrict__ y, int tpb, int n_tiles) {
+  constexpr int KP = 4;
+  constexpr int KH = K - 1;             // history rows
+  constexpr int ZW = KQ * 16, ZWP = ZW + 8;
+  constexpr int CH = kDt / 8;           // 16-byte chunks per row
+  constexpr int kVLoads = ((32 + KH) * CH + 255) / 256;
+  constexpr int kSLoads = (32 * ZW + 255) / 256;
+  __shared__ __attribute__((aligned(16))) unsigned char xs[2][(32 + KH) * kRowB];
+  __shared__ __attribute__((aligned(16))) bf16 zs[2][32 * ZWP];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hh = lane >> 5, tl = lane & 31;
-  const int64_t cblk = (int64_t)blockIdx.x * kDt;    // first channel of the block
-  const int nch = (int)min<int64_t>(kDt, s.D - cblk);  // channels present (multiple of 16)
+  const int64_t cblk = (int64_t)blockIdx.x * kDt;
+  const int nch = (int)min<int64_t>(kDt, s.D - cblk);
+  const int tile_lo = blockIdx.y * tpb, tile_hi = min(n_tiles, tile_lo + tpb);
 
-  // A fragments for this wave's groups: [cg][p][th][kq]
-  bf16x8 af[kCPW][2][THP][KQ];
+  // bias / padding columns of the z tile (constant): 1 at q = r, 0 beyond
+  for (int e = threadIdx.x; e < 2 * 32 * ZWP; e += 256) {
+    const int q = e % ZWP;
+    if (q >= s.rank) (&zs[0][0])[e] = (bf16)(q == s.rank ? 1.f : 0.f);
+  }
+
+  // A fragments for this wave's groups: [g][p][kq]
+  bf16x8 af[kCPW][2][KQ];
+  bool glive[kCPW];
 #pragma unroll
-  for (int cg = 0; cg < kCPW; ++cg) {
-    const int64_t g = (cblk >> 4) + wave * kCPW + cg;
-    const bool live = (wave * kCPW + cg) * 16 < nch;
+  for (int g = 0; g < kCPW; ++g) {
+    const int64_t gg = (cblk >> 4) + wave * kCPW + g;
+    glive[g] = (wave * kCPW + g) * 16 < nch;
 #pragma unroll
     for (int p = 0; p < 2; ++p)
 #pragma unroll
-      for (int th = 0; th < THP; ++th)
-#pragma unroll
-        for (int kq = 0; kq < KQ; ++kq) {
-          const int64_t rowf = ((g * 2 + p) * THP + th) * 32 + tl;
-          af[cg][p][th][kq] = live ? as_bf16x8(*reinterpret_cast<const uint4 *>(
-                                         Uf + rowf * (KQ * 16) + kq * 16 + hh * 8))
-                                   : zero_bf16x8();
-        }
+      for (int kq = 0; kq < KQ; ++kq)
+        af[g][p][kq] = glive[g] ? as_bf16x8(*reinterpret_cast<const uint4 *>(
+                                      Uf + ((gg * 2 + p) * 32 + tl) * (KQ * 16) + kq * 16 + hh * 8))
+                                : zero_bf16x8();
   }
 
-  const int64_t tile0 = (int64_t)blockIdx.y * kTilesPerBlock;
-  for (int it = 0; it < kTilesPerBlock; ++it) {
-    const int64_t t0 = (tile0 + it) * 32;
-    if (t0 >= s.BT) break;
-
-    // ---- stage x rows [t0-KH, t0+32) x [cblk, cblk+nch) in LDS ----
-    __syncthreads();
-    {
-      const int chunks = nch / 8;  // 16-byte chunks per row
-      for (int e = threadIdx.x; e < (32 + KH) * chunks; e += 256) {
-        const int r = e / chunks, q = e - r * chunks;
-        const int64_t row = t0 - KH + r;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (row >= 0 && row < s.BT)
-          v = *reinterpret_cast<const uint4 *>(x + row * s.D + cblk + q * 8);
-        *reinterpret_cast<uint4 *>(xs + r * ROWB + q * 16) = v;
-      }
+  // per-thread load slots
+  int v_row[kVLoads], v_col[kVLoads], v_loff[kVLoads];
+  bool v_ok[kVLoads];
+#pragma unroll
+  for (int q = 0; q < kVLoads; ++q) {
+    const int e = threadIdx.x + q * 256;
+    const int r = e / CH, c16 = e % CH;
+    v_ok[q] = r < 32 + KH && c16 * 8 < nch;
+    v_row[q] = r - KH;
+    v_col[q] = c16 * 8;
+    v_loff[q] = r * kRowB + c16 * 16;
+  }
+  int s_tt[kSLoads], s_q[kSLoads];
+  bool s_ok[kSLoads];
+#pragma unroll
+  for (int q = 0; q < kSLoads; ++q) {
+    const int e = threadIdx.x + q * 256;
+    s_tt[q] = e / ZW;
+    s_q[q] = e % ZW;
+    s_ok[q] = s_tt[q] < 32 && s_q[q] < s.rank;
+  }
+  uint4 vpre[kVLoads];
+  float spre[kSLoads];
+  auto prefetch = [&](int tile) {
+    const int64_t t0 = (int64_t)tile * 32;
+#pragma unroll
+    for (int q = 0; q < kVLoads; ++q) {
+      const int64_t row = t0 + v_row[q];
+      vpre[q] = make_uint4(0, 0, 0, 0);
+      if (v_ok[q] && row >= 0 && row < s.BT)
+        vpre[q] = *reinterpret_cast<const uint4 *>(x + row * s.D + cblk + v_col[q]);
     }
+#pragma unroll
+    for (int q = 0; q < kSLoads; ++q) {
+      const int64_t row = t0 + s_tt[q];
+      spre[q] = (s_ok[q] && row < s.BT) ? z[row * s.rank + s_q[q]] : 0.f;
+    }
+  };
 
-    // ---- B operand: z for this tile's tokens, plus the constant-1 bias row ----
-    const int64_t t = t0 + tl;
-    const bool trow = t < s.BT;
+  if (tile_hi > tile_lo) prefetch(tile_lo);
+  int buf = 0;
+  for (int tile = tile_lo; tile < tile_hi; ++tile, buf ^= 1) {
+    // ---- stage this tile, then start loading the next ----
+#pragma unroll
+    for (int q = 0; q < kVLoads; ++q)
+      if (v_ok[q]) *reinterpret_cast<uint4 *>(xs[buf] + v_loff[q]) = vpre[q];
+#pragma unroll
+    for (int q = 0; q < kSLoads; ++q)
+      if (s_ok[q]) zs[buf][s_tt[q] * ZWP + s_q[q]] = (bf16)spre[q];
+    __syncthreads();
+    if (tile + 1 < tile_hi) prefetch(tile + 1);
+
+    const int64_t t = (int64_t)tile * 32 + tl;
+    const bool tv = t < s.BT;
+    const int pos = (int)((uint32_t)t % (uint32_t)s.T);
+    const bool edge = __any(KH > 0 && pos < KH);
     bf16x8 bz[KQ];
 #pragma unroll
-    for (int kq = 0; kq < KQ; ++kq) {
-      float v[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int q = kq * 16 + hh * 8 + i;
-        v[i] = (trow && q < s.rank) ? z[t * s.rank + q] : (q == s.rank ? 1.f : 0.f);
-      }
-      bz[kq] = pack_bf16x8(v);
-    }
-    const int pos = trow ? (int)(t % s.T) : 0;
-    __syncthreads();
+    for (int kq = 0; kq < KQ; ++kq)
+      bz[kq] = as_bf16x8(*reinterpret_cast<const uint4 *>(&zs[buf][tl * ZWP + kq * 16 + hh * 8]));
 
 #pragma unroll
-    for (int cg = 0; cg < kCPW; ++cg) {
-      const int cl = (wave * kCPW + cg) * 16 + hh * 8;  // first of this lane's 8 channels (block-local)
-      if ((wave * kCPW + cg) * 16 >= nch) break;
-      // x[t-j][8 channels] for j = 0..KP-1
-      float xv[KP][8];
+    for (int g = 0; g < kCPW; ++g) {
+      if (!glive[g]) continue;
+      const int cl = (wave * kCPW + g) * 16 + hh * 8;  // block-local first channel of the lane's 8
+      float xv[K][8];
 #pragma unroll
-      for (int j = 0; j < KP; ++j) {
-        const uint4 raw = *reinterpret_cast<const uint4 *>(xs + (tl + KH - j) * ROWB + cl * 2);
+      for (int j = 0; j < K; ++j) {
+        uint4 raw = *reinterpret_cast<const uint4 *>(xs[buf] + (tl + KH - j) * kRowB + cl * 2);
+        if (edge && j > pos) raw = make_uint4(0, 0, 0, 0);
         const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -159,24 +191,20 @@ k_fwd_lowrank(Shape s, const float *__restrict__ z, const bf16 *__restrict__ Uf,
 #pragma unroll
       for (int i = 0; i < 8; ++i) out[i] = xv[0][i];
 #pragma unroll
-      for (int p = 0; p < 2; ++p)
+      for (int p = 0; p < 2; ++p) {
+        f32x16 acc = {};
 #pragma unroll
-        for (int th = 0; th < THP; ++th) {
-          f32x16 acc = {};
+        for (int kq = 0; kq < KQ; ++kq) acc = mfma32(af[g][p][kq], bz[kq], acc);
+        // acc[4b + r] = w[t][channel 4p+b of this half][tap r]
 #pragma unroll
-          for (int kq = 0; kq < KQ; ++kq) acc = mfma32(af[cg][p][th][kq], bz[kq], acc);
-          // acc[4b + r] = w[t][channel 4p+b of this half][tap 4th + r]
+        for (int b4 = 0; b4 < 4; ++b4)
 #pragma unroll
-          for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int j = 4 * th + r;
-              if (j < KP && j <= pos && j < s.k) out[4 * p + b] = fmaf(acc[4 * b + r], xv[j][4 * p + b], out[4 * p + b]);
-            }
-        }
-      if (trow) store_vec(y + t * s.D + cblk + cl, out);
+          for (int j = 0; j < K; ++j) out[4 * p + b4] = fmaf(acc[4 * b4 + j], xv[j][4 * p + b4], out[4 * p + b4]);
+      }
+      if (tv) store_vec(y + t * s.D + cblk + cl, out);
     }
   }
+  (void)KP;
 }
 
 }  // namespace lowrank
@@ -187,7 +215,7 @@ size_t fwd_lowrank_ws_bytes(const Shape &s) {
   return (size_t)(s.D / 16) * 2 * THP * 32 * KQ * 16 * sizeof(bf16);
 }
 
-bool fwd_lowrank_supported(const Shape &s) { return s.D % 16 == 0 && s.rank + 1 <= 64; }
+bool fwd_lowrank_supported(const Shape &s) { return s.D % 16 == 0 && s.rank + 1 <= 64 && s.k <= 4; }
 
 int prep_lowrank_frags(const Shape &s, const void *U, const void *w0, void *Uf, hipStream_t st) {
   const int THP = s.k <= 4 ? 1 : 2;
@@ -201,31 +229,35 @@ int prep_lowrank_frags(const Shape &s, const void *U, const void *w0, void *Uf, 
 int fwd_lowrank(const Shape &s, const float *z, const void *Uf, const void *x, void *y, hipStream_t st) {
   using namespace lowrank;
   const int KQ = (int)ceil_div(s.rank + 1, 16);
-  dim3 grid((unsigned)ceil_div(s.D, kDt), (unsigned)ceil_div(ceil_div(s.BT, 32), kTilesPerBlock));
+  const int n_slices = (int)ceil_div(s.D, kDt);
+  const int n_tiles = (int)ceil_div(s.BT, 32);
+  // enough blocks for ~4 per CU, each walking a run of tiles
+  int tpb = 1;
+  while ((int64_t)n_slices * ceil_div(n_tiles, tpb) > 1024) ++tpb;
+  dim3 grid((unsigned)n_slices, (unsigned)ceil_div(n_tiles, tpb));
   const bool tr = trace_begin(DYNCONV_K_FWD_CONV, st);
-#define LAUNCH(KP_, KQ_)                                                                          \
-  hipLaunchKernelGGL((k_fwd_lowrank<KP_, KQ_>), grid, dim3(256), 0, st, s, z, (const bf16 *)Uf, \
-                     (const bf16 *)x, (bf16 *)y)
-  if (s.k <= 4) {
-    switch (KQ) {
-      case 1: LAUNCH(4, 1); break;
-      case 2: LAUNCH(4, 2); break;
-      case 3: LAUNCH(4, 3); break;
-      case 4: LAUNCH(4, 4); break;
-      default: trace_end(tr, st); return DYNCONV_E_LIMIT;
-    }
-  } else {
-    switch (KQ) {
-      case 1: LAUNCH(8, 1); break;
-      case 2: LAUNCH(8, 2); break;
-      case 3: LAUNCH(8, 3); break;
-      case 4: LAUNCH(8, 4); break;
-      default: trace_end(tr, st); return DYNCONV_E_LIMIT;
-    }
+  int rc = 0;
+#define LAUNCH(K_, KQ_)                                                                             \
+  hipLaunchKernelGGL((k_fwd_lowrank<K_, KQ_>), grid, dim3(256), 0, st, s, z, (const bf16 *)Uf,    \
+                     (const bf16 *)x, (bf16 *)y, tpb, n_tiles)
+#define LAUNCH_K(K_)                          \
+  switch (KQ) {                               \
+    case 1: LAUNCH(K_, 1); break;             \
+    case 2: LAUNCH(K_, 2); break;             \
+    case 3: LAUNCH(K_, 3); break;             \
+    case 4: LAUNCH(K_, 4); break;             \
+    default: rc = DYNCONV_E_LIMIT;            \
   }
+  switch (s.k) {
+    case 1: LAUNCH_K(1) break;
+    case 2: LAUNCH_K(2) break;
+    case 3: LAUNCH_K(3) break;
+    default: LAUNCH_K(4) break;
+  }
+#undef LAUNCH_K
 #undef LAUNCH
   trace_end(tr, st);
-  return 0;
+  return rc;
 }
 
 }  // namespace dynconv

@@ -42,6 +42,7 @@ int fwd_lowrank(const Shape &s, const float *z, const void *Uf, const void *x, v
 // --- fused backward conv (conv_bwd.hip), bf16 ---
 struct BwdLayout {
   int KP;        // taps padded to 4 or 8
+  int Dt;        // channels per slice
   int n_slices;  // 128-channel slices (grid x)
   int n_tiles;   // 32-token tiles
   int tpb;       // tiles per block
