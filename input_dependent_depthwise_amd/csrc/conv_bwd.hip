@@ -502,6 +502,7 @@ k_prep_dz(Shape s, const bf16 *__restrict__ U, bf16 *__restrict__ Udz, int KP) {
 // host side
 // ---------------------------------------------------------------------------
 BwdLayout bwd_layout(const Shape &s) {
+  if (s.kind == DYNCONV_HEADWISE) return bwd_headwise_layout(s);
   BwdLayout L;
   L.KP = s.k <= 4 ? 4 : 8;
   L.Dt = bwd::kDt;
@@ -532,11 +533,9 @@ BwdLayout bwd_layout(const Shape &s) {
 }
 
 bool bwd_fused_supported(const Shape &s) {
+  if (s.kind == DYNCONV_HEADWISE) return bwd_headwise_supported(s);
   if (s.D % 16 != 0 || s.k > 4) return false;
-  const int KP = 4;
-  if (s.kind == DYNCONV_LOWRANK) return s.rank <= 32 && fwd_lowrank_supported(s);
-  if (s.hd < 8) return false;
-  return bwd_layout(s).SL * KP <= 32;
+  return s.rank <= 32 && fwd_lowrank_supported(s);
 }
 
 size_t bwd_prep_dz_bytes(const Shape &s) {
@@ -555,6 +554,7 @@ int prep_dz_frags(const Shape &s, const void *U, void *Udz, hipStream_t st) {
 int bwd_conv(const Shape &s, const BwdLayout &L, const float *gen, const void *Uf, const void *Udz,
              const void *w0, const void *x, const void *dy, void *dx, float *gpart, float *dUp,
              float *dw0p, hipStream_t st) {
+  if (s.kind == DYNCONV_HEADWISE) return bwd_headwise(s, L, gen, w0, x, dy, dx, gpart, dw0p, st);
   bwd::Params P;
   P.s = s;
   P.x = (const bf16 *)x;
@@ -596,13 +596,7 @@ int bwd_conv(const Shape &s, const BwdLayout &L, const float *gen, const void *U
 #undef L_K
 #undef L_LR
   } else {
-    switch (s.k) {
-      case 1: hipLaunchKernelGGL((bwd::k_bwd<DYNCONV_HEADWISE, 1, 1, 1>), grid, block, 0, st, P); break;
-      case 2: hipLaunchKernelGGL((bwd::k_bwd<DYNCONV_HEADWISE, 2, 1, 1>), grid, block, 0, st, P); break;
-      case 3: hipLaunchKernelGGL((bwd::k_bwd<DYNCONV_HEADWISE, 3, 1, 1>), grid, block, 0, st, P); break;
-      case 4: hipLaunchKernelGGL((bwd::k_bwd<DYNCONV_HEADWISE, 4, 1, 1>), grid, block, 0, st, P); break;
-      default: rc = DYNCONV_E_LIMIT;
-    }
+    rc = DYNCONV_E_LIMIT;  // head-wise goes to bwd_headwise
   }
   trace_end(tr, st);
   return rc;

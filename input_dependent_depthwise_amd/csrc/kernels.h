@@ -51,6 +51,13 @@ struct BwdLayout {
   int R;         // columns of the per-slice partial (rank, or SL*k)
 };
 BwdLayout bwd_layout(const Shape &s);
+// head-wise: one lane per 8 (or 4) channels walking along time (conv_bwd_headwise.hip);
+// its layout reuses BwdLayout with Dt = channels per wave span, tpb = tokens per
+// wave and n_ranges = blocks along tokens (dw0 partials)
+bool bwd_headwise_supported(const Shape &s);
+BwdLayout bwd_headwise_layout(const Shape &s);
+int bwd_headwise(const Shape &s, const BwdLayout &L, const float *u, const void *w0, const void *x,
+                 const void *dy, void *dx, float *gpart, float *dw0p, hipStream_t st);
 bool bwd_fused_supported(const Shape &s);
 size_t bwd_prep_dz_bytes(const Shape &s);
 int prep_dz_frags(const Shape &s, const void *U, void *Udz, hipStream_t st);
