@@ -74,7 +74,6 @@ struct Plan {
   size_t g = 0;      // simple path: du or dz, fp32 [BT, N]; fused path: g, bf16 [BT, Np]
   size_t mt = 0;     // transposed, padded generator weight for the MFMA projection (bf16)
   size_t uf = 0;     // U and w0 in filter-MFMA fragment order (bf16, low-rank)
-  size_t udz = 0;    // U in dz-MFMA fragment order (bf16, low-rank backward)
   size_t gpart = 0;  // per-slice du / dz partials, fp32
   size_t dup = 0;    // per-range dU partials, fp32
   size_t dw0p = 0;   // per-range dw0 partials, fp32
@@ -104,7 +103,6 @@ Plan plan(const Shape &s, int dtype, int pass) {
   if (pass == 1) {
     if (fast_bwd(s, dtype)) {
       const BwdLayout L = bwd_layout(s);
-      pl.udz = take(bwd_prep_dz_bytes(s));
       pl.gpart = take((size_t)L.n_slices * s.BT * L.R * sizeof(float));
       if (s.kind == DYNCONV_LOWRANK) pl.dup = take((size_t)L.n_ranges * s.N * s.D * s.k * sizeof(float));
       pl.dw0p = take((size_t)L.n_ranges * s.D * s.k * sizeof(float));
@@ -330,13 +328,11 @@ int dynconv_bwd(const dynconv_problem *p, const dynconv_gen *g, const void *h, c
   if (fast_bwd(s, p->dtype)) {
     const BwdLayout L = bwd_layout(s);
     const GenBwdLayout G = gen_bwd_layout(s);
-    if (s.kind == DYNCONV_LOWRANK) {
-      if ((rc = prep_lowrank_frags(s, g->U, g->w0, ws + pl.uf, stream))) return rc;
-      if ((rc = prep_dz_frags(s, g->U, ws + pl.udz, stream))) return rc;
-    }
     float *gpart = (float *)(ws + pl.gpart), *dUp = (float *)(ws + pl.dup), *dw0p = (float *)(ws + pl.dw0p);
-    if ((rc = bwd_conv(s, L, cache, ws + pl.uf, ws + pl.udz, g->w0, x, dy, dx, gpart, dUp, dw0p, stream)))
-      return rc;
+    rc = s.kind == DYNCONV_HEADWISE
+             ? bwd_headwise(s, L, cache, g->w0, x, dy, dx, gpart, dw0p, stream)
+             : bwd_lowrank(s, L, cache, g->U, g->w0, x, dy, dx, gpart, dUp, dw0p, stream);
+    if (rc) return rc;
     const void *M = s.kind == DYNCONV_HEADWISE ? g->W : g->A;
     float *dMp = (float *)(ws + pl.dmp);
     if ((rc = gen_bwd(s, gpart, L.n_slices, L.R, L.Dt, h, M, (bf16 *)(ws + pl.g), (bf16 *)(ws + pl.mp), dh,

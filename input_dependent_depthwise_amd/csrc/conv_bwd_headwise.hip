@@ -418,7 +418,6 @@ BwdLayout bwd_headwise_layout(const Shape &s) {
   BwdLayout L = {};
   const int cpl = hw_cpl(s);
   const int span = 64 * cpl;
-  L.KP = 4;
   L.Dt = span;
   L.n_slices = (int)ceil_div(s.D, span);
   // tokens per wave: about one round of resident waves over 256 CUs (the

@@ -1,0 +1,446 @@
+// conv_bwd_lowrank.hip -- fused backward of the low-rank dynamic short
+// convolution (bf16 I/O) on matrix cores.
+//
+// Layer (gist.science Technical Summary of "Dynamic Short Convolutions Improve
+// Transformers", Methodology -> Dynamic Short Convolutions: Mechanism,
+// Parameterization): y[t,c] = x[t,c] + sum_j w[t,c,j] x[t-j,c] with the
+// low-rank filter w[t,c,j] = sum_q z[t,q] U[q,c*k+j] + w0[c,j], z = h A.
+// For L = sum(dy * y), one pass over x and dy gives
+//   dx[s,c]   = dy[s,c] + sum_j [s, s+j in one sequence] w[s+j,c,j] dy[s+j,c]
+//   G[t,c,j]  = [t-j in t's sequence] dy[t,c] x[t-j,c]         (never stored)
+//   dz[t,q]   = sum_{c,j} G[t,c,j] U[q,c*k+j]    -> one fp32 partial per 128-channel slice
+//   dU[q,c*k+j] = sum_t z[t,q] G[t,c,j]          -> one fp32 partial per token range
+//   dw0[c,j]  = sum_t G[t,c,j]                   -> one fp32 partial per token range
+//
+// Work split.  A block (8 waves) owns 128 channels and a range of 32-token
+// tiles; wave w owns 16 of the channels.  Per tile the block stages x (rows
+// t0-k+1 .. t0+31), dy and z (rows t0 .. t0+31+k-1) in LDS.  Every product is
+// a v_mfma_f32_16x16x32_bf16; a lane (n = lane%16, g = lane/16) holds tokens
+// n and 16+n of the tile and channels 4g .. 4g+3 of the wave's 16:
+//   * filter, per tap j and 16-token block: D[channel][token] = U^T z with the
+//     z rows shifted by j, so the lane of token s gets w[s+j, c, j] directly
+//     (the diagonal the transposed conv needs); the bias w0 rides as an extra
+//     K row against a constant 1 column of z (K = 32 covers rank <= 31);
+//   * dx accumulates w[s+j,c,j] dy[s+j,c] in registers;
+//   * G for tap j comes from bf16 dot products (v_dot2) of x[s-j] with dy[s]
+//     (one half of each pair cleared); rounded to bf16 once, two taps at a time
+//     are the B operand of D[q][token] = U G (dz, summed over taps and
+//     channels in the accumulator);
+//   * G goes to LDS token-contiguous and is the A operand of
+//     D[channel][q] = G^T z over the tile's 32 tokens (dU); the same fragment
+//     dotted with ones gives dw0.
+// The 8 waves' dz meet in LDS; the block writes one partial per (slice,
+// token).  The next tile's global loads are in flight while a tile is
+// computed.  Matrix-core fragments of U are built by each lane from global
+// memory at start (no separate preparation pass).
+#include "kernels.h"
+#include "mfma.h"
+
+namespace dynconv {
+namespace bwdlr {
+
+constexpr int kW = 8;            // waves per block
+constexpr int kCW = 16;          // channels per wave
+constexpr int kDt = kW * kCW;    // channels per block
+constexpr int kRow = kDt + 8;    // LDS row of the x / dy tiles (bf16 elements)
+constexpr int kGRow = 40;        // LDS row of the token-contiguous tiles: 32 tokens + pad (bf16)
+
+struct Params {
+  Shape s;
+  const bf16 *x, *dy;
+  bf16 *dx;
+  const float *z;   // [BT, r]
+  const bf16 *U;    // [r, D*k]
+  const bf16 *w0;   // [D, k] or NULL
+  float *gpart;     // [n_slices][BT][r]
+  float *dUp;       // [n_ranges][r][D*k]
+  float *dw0p;      // [n_ranges][D*k]
+  int tpb;          // tiles per block
+  int n_tiles;      // ceil(BT / 32)
+};
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                         false);
+}
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  const bf16x2_t p = {(bf16)a, (bf16)b};
+  return __builtin_bit_cast(uint32_t, p);
+}
+
+// K: taps; KQ: 32-row K-steps over rank + bias; NQ: 16-row blocks of rank.
+template <int K, int KQ, int NQ>
+__global__ void __launch_bounds__(kW * 64, 2)
+k_bwd_lr(Params P) {
+  constexpr int KH = K - 1;
+  constexpr int KP = (K + 1) / 2;             // tap pairs
+  constexpr int TR = 32 + KH;                 // rows of a staged tile
+  constexpr int ZW = 32 * KQ + 8;             // z row in LDS (bf16): rank, bias column, zeros, pad
+  constexpr int NT = kW * 64;
+  constexpr int CH = kDt / 8;                 // 16-byte chunks per x / dy row
+  constexpr int kVL = (2 * TR * CH + NT - 1) / NT;
+  constexpr int ZC = 16 * NQ;                 // z columns staged (rank padded)
+  constexpr int kZL = (TR * ZC + NT - 1) / NT;
+  constexpr int RV = 8 * NQ;                  // dz values per lane and tile
+  const Shape &s = P.s;
+  const int rank = s.rank;
+
+  __shared__ __attribute__((aligned(16))) bf16 xs[TR * kRow];          // x rows t0-KH .. t0+31
+  __shared__ __attribute__((aligned(16))) bf16 dys[TR * kRow];         // dy rows t0 .. t0+31+KH
+  __shared__ __attribute__((aligned(16))) bf16 zs[TR * ZW];            // z rows t0 .. t0+31+KH, bf16
+  __shared__ __attribute__((aligned(16))) bf16 zt[ZC * kGRow];         // z^T: rows q, tokens t0 .. t0+31
+  __shared__ __attribute__((aligned(16))) bf16 gt[kW][16 * kGRow];     // per wave: G of one tap, [channel][token]
+  __shared__ __attribute__((aligned(16))) float red[kW][64 * RV];      // per wave: dz partial of a tile
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int64_t cblk = (int64_t)blockIdx.x * kDt;
+  const int64_t cw = cblk + wave * kCW;  // the wave's first channel
+  const int64_t Dk = s.D * K;
+
+  // ---- block constants in LDS: z's bias and zero columns, zero z^T rows ----
+  for (int e = tid; e < TR * ZW; e += NT) {
+    const int q = e % ZW;
+    if (q >= rank) zs[e] = (bf16)(q == rank ? 1.f : 0.f);
+  }
+  for (int e = tid; e < ZC * kGRow; e += NT) zt[e] = (bf16)0.f;
+
+  // ---- matrix-core fragments of U ----
+  // filter A (tap j, K-step kq): A[m = channel cw + n][k = q = 32kq + 8g + i]; bias row q = rank
+  bf16x8 fa[K][KQ];
+#pragma unroll
+  for (int j = 0; j < K; ++j)
+#pragma unroll
+    for (int kq = 0; kq < KQ; ++kq) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int q = 32 * kq + 8 * g + i;
+        const int64_t c = cw + n;
+        float u = 0.f;
+        if (c < s.D) {
+          if (q < rank) u = (float)P.U[(int64_t)q * Dk + c * K + j];
+          else if (q == rank && P.w0) u = (float)P.w0[c * K + j];
+        }
+        v[i] = u;
+      }
+      fa[j][kq] = pack_bf16x8(v);
+    }
+  // dz A (tap pair jp, q block mq): A[m = q = 16mq + n][k = 8g + i],
+  //   k <-> (channel cw + 4g + i/2, tap 2jp + i%2)
+  bf16x8 za[KP][NQ];
+#pragma unroll
+  for (int jp = 0; jp < KP; ++jp)
+#pragma unroll
+    for (int mq = 0; mq < NQ; ++mq) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int q = 16 * mq + n, j = 2 * jp + (i & 1);
+        const int64_t c = cw + 4 * g + (i >> 1);
+        v[i] = (q < rank && j < K && c < s.D) ? (float)P.U[(int64_t)q * Dk + c * K + j] : 0.f;
+      }
+      za[jp][mq] = pack_bf16x8(v);
+    }
+
+  f32x4 dUacc[K][NQ];
+  float dw0acc[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    dw0acc[j] = 0.f;
+#pragma unroll
+    for (int nq = 0; nq < NQ; ++nq) dUacc[j][nq] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // ---- global -> register prefetch of one tile ----
+  const int tile_lo = blockIdx.y * P.tpb;
+  const int tile_hi = min(P.n_tiles, tile_lo + P.tpb);
+  uint4 vpre[kVL];
+  float zpre[kZL];
+  auto prefetch = [&](int tile) {
+    const int64_t t0 = (int64_t)tile * 32;
+#pragma unroll
+    for (int q = 0; q < kVL; ++q) {
+      const int e = tid + q * NT;
+      const bool isx = e < TR * CH;
+      const int e2 = isx ? e : e - TR * CH;
+      const int r = e2 / CH, c16 = e2 % CH;
+      const int64_t row = isx ? t0 - KH + r : t0 + r;
+      vpre[q] = make_uint4(0, 0, 0, 0);
+      if (e < 2 * TR * CH && row >= 0 && row < s.BT && cblk + c16 * 8 < s.D)
+        vpre[q] = *reinterpret_cast<const uint4 *>((isx ? P.x : P.dy) + row * s.D + cblk + c16 * 8);
+    }
+#pragma unroll
+    for (int q = 0; q < kZL; ++q) {
+      const int e = tid + q * NT;
+      const int r = e / ZC, qq = e % ZC;
+      const int64_t row = t0 + r;
+      zpre[q] = (e < TR * ZC && qq < rank && row < s.BT) ? P.z[row * rank + qq] : 0.f;
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int q = 0; q < kVL; ++q) {
+      const int e = tid + q * NT;
+      if (e < 2 * TR * CH) {
+        const bool isx = e < TR * CH;
+        const int e2 = isx ? e : e - TR * CH;
+        const int r = e2 / CH, c16 = e2 % CH;
+        *reinterpret_cast<uint4 *>((isx ? xs : dys) + r * kRow + c16 * 8) = vpre[q];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kZL; ++q) {
+      const int e = tid + q * NT;
+      const int r = e / ZC, qq = e % ZC;
+      if (e < TR * ZC && qq < rank) {
+        const bf16 v = (bf16)zpre[q];
+        zs[r * ZW + qq] = v;
+        if (r < 32) zt[qq * kGRow + r] = v;
+      }
+    }
+  };
+
+  if (tile_hi > tile_lo) prefetch(tile_lo);
+  const uint32_t ones = 0x3f803f80u;     // bf16 pair (1, 1)
+  const int wc = wave * kCW + 4 * g;     // the lane's first channel within the tile rows
+  bf16 *gtw = gt[wave];
+
+  for (int tile = tile_lo; tile < tile_hi; ++tile) {
+    const int64_t t0 = (int64_t)tile * 32;
+    int pos[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) pos[tb] = (int)((uint32_t)(t0 + 16 * tb + n) % (uint32_t)s.T);  // B*T < 2^31
+    // only waves that hold a sequence start / end need the masks
+    const bool edge_lo = __any(KH > 0 && (pos[0] < KH || pos[1] < KH));
+    const bool edge_hi = __any(KH > 0 && (pos[0] + KH > s.T - 1 || pos[1] + KH > s.T - 1));
+
+    __syncthreads();  // the previous tile's LDS reads are done
+    stage();
+    __syncthreads();
+    if (tile + 1 < tile_hi) prefetch(tile + 1);
+
+    // dy of the lane's two tokens: fp32 (dx starts as dy) and bf16 pairs with one half cleared
+    float dxacc[2][4];
+    uint32_t dlo[2][2], dhi[2][2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const uint2 d = *reinterpret_cast<const uint2 *>(&dys[(16 * tb + n) * kRow + wc]);
+      const uint32_t w[2] = {d.x, d.y};
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        dhi[tb][p] = w[p] & 0xffff0000u;
+        dlo[tb][p] = w[p] & 0x0000ffffu;
+        dxacc[tb][2 * p] = __uint_as_float(w[p] << 16);
+        dxacc[tb][2 * p + 1] = __uint_as_float(dhi[tb][p]);
+      }
+    }
+    // z^T fragments for dU: B[k = token 8g + i][n = q - 16nq]
+    bf16x8 zb[NQ];
+#pragma unroll
+    for (int nq = 0; nq < NQ; ++nq)
+      zb[nq] = as_bf16x8(*reinterpret_cast<const uint4 *>(&zt[(16 * nq + n) * kGRow + 8 * g]));
+
+    f32x4 dzacc[2][NQ];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int mq = 0; mq < NQ; ++mq) dzacc[tb][mq] = f32x4{0.f, 0.f, 0.f, 0.f};
+    uint32_t gpair[2][4];  // G of tap 2jp (low half) and 2jp+1 (high half), channel r, per token block
+
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      float gv[2][4];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        // filter diagonal: element r = w[t0 + 16tb + n + j, channel wc + r, j]
+        f32x4 wd = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kq = 0; kq < KQ; ++kq)
+          wd = mfma16(fa[j][kq],
+                      as_bf16x8(*reinterpret_cast<const uint4 *>(&zs[(16 * tb + n + j) * ZW + 32 * kq + 8 * g])), wd);
+        // dx += w[s+j] dy[s+j] (dy past the sequence end is zero)
+        uint32_t w[2];
+        if (j == 0) {
+          w[0] = dlo[tb][0] | dhi[tb][0], w[1] = dlo[tb][1] | dhi[tb][1];
+        } else {
+          const uint2 d = *reinterpret_cast<const uint2 *>(&dys[(16 * tb + n + j) * kRow + wc]);
+          w[0] = d.x, w[1] = d.y;
+          if (edge_hi && pos[tb] + j > s.T - 1) w[0] = 0u, w[1] = 0u;
+        }
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          dxacc[tb][2 * p] = fmaf(wd[2 * p], __uint_as_float(w[p] << 16), dxacc[tb][2 * p]);
+          dxacc[tb][2 * p + 1] = fmaf(wd[2 * p + 1], __uint_as_float(w[p] & 0xffff0000u), dxacc[tb][2 * p + 1]);
+        }
+        // G[s, c, j] = dy[s, c] x[s-j, c] (x before the sequence start is zero)
+        const uint2 xv = *reinterpret_cast<const uint2 *>(&xs[(16 * tb + n + KH - j) * kRow + wc]);
+        uint32_t xw[2] = {xv.x, xv.y};
+        if (edge_lo && j > pos[tb]) xw[0] = 0u, xw[1] = 0u;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          gv[tb][2 * p] = dot2(xw[p], dlo[tb][p], 0.f);
+          gv[tb][2 * p + 1] = dot2(xw[p], dhi[tb][p], 0.f);
+        }
+      }
+      // G of this tap, bf16: into the tap-pair operand and token-contiguous into LDS
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t b = __builtin_bit_cast(uint16_t, (bf16)gv[tb][r]);
+          gpair[tb][r] = (j & 1) ? (gpair[tb][r] | (b << 16)) : b;
+          *reinterpret_cast<uint16_t *>(&gtw[(4 * g + r) * kGRow + 16 * tb + n]) = (uint16_t)b;
+        }
+      // dz, once a tap pair is complete: B[k = 8g + i][token n], k <-> (channel 4g + i/2, tap 2jp + i%2)
+      if ((j & 1) || j == K - 1) {
+        const int jp = j >> 1;
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          const bf16x8 bb = as_bf16x8(make_uint4(gpair[tb][0], gpair[tb][1], gpair[tb][2], gpair[tb][3]));
+#pragma unroll
+          for (int mq = 0; mq < NQ; ++mq) dzacc[tb][mq] = mfma16(za[jp][mq], bb, dzacc[tb][mq]);
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // dU: A[m = channel n][k = token 8g + i] = G; B = z^T.  dw0: the same fragment dotted with ones.
+      {
+        const uint4 raw = *reinterpret_cast<const uint4 *>(&gtw[n * kGRow + 8 * g]);
+#pragma unroll
+        for (int nq = 0; nq < NQ; ++nq) dUacc[j][nq] = mfma16(as_bf16x8(raw), zb[nq], dUacc[j][nq]);
+        dw0acc[j] = dot2(raw.w, ones, dot2(raw.z, ones, dot2(raw.y, ones, dot2(raw.x, ones, dw0acc[j]))));
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+
+    // dx of the lane's two tokens
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const int64_t t = t0 + 16 * tb + n;
+      if (t < s.BT && cw + 4 * g + 4 <= s.D)
+        *reinterpret_cast<uint2 *>(P.dx + t * s.D + cw + 4 * g) =
+            make_uint2(pack2(dxacc[tb][0], dxacc[tb][1]), pack2(dxacc[tb][2], dxacc[tb][3]));
+    }
+    // dz partial of the wave: element (tb*NQ + mq)*4 + r = dz[t0 + 16tb + n][16mq + 4g + r]
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int mq = 0; mq < NQ; ++mq)
+        *reinterpret_cast<float4 *>(&red[wave][lane * RV + (tb * NQ + mq) * 4]) =
+            make_float4(dzacc[tb][mq][0], dzacc[tb][mq][1], dzacc[tb][mq][2], dzacc[tb][mq][3]);
+    __syncthreads();
+    // the 8 waves' sum, one partial per (slice, token): thread -> (token, q), q fastest
+    for (int o = tid; o < 32 * ZC; o += NT) {
+      const int q = o % ZC, sr = o / ZC;
+      const int64_t row = t0 + sr;
+      if (q < rank && row < s.BT) {
+        const int tb = sr >> 4, nn = sr & 15, mq = q >> 4, gg = (q >> 2) & 3, r = q & 3;
+        const int src = (16 * gg + nn) * RV + (tb * NQ + mq) * 4 + r;
+        float v = red[0][src];
+#pragma unroll
+        for (int w = 1; w < kW; ++w) v += red[w][src];
+        P.gpart[((int64_t)blockIdx.x * s.BT + row) * rank + q] = v;
+      }
+    }
+  }
+
+  // ---- block epilogue: dU and dw0 partials of this token range ----
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    // dw0: lanes n, n+16, n+32, n+48 hold the same (channel, tap), different tokens
+    float v = dw0acc[j];
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    const int64_t c = cw + n;
+    if (lane < 16 && c < s.D) P.dw0p[(int64_t)blockIdx.y * Dk + c * K + j] = v;
+    // dU: lane holds D[m = 4g + r][q - 16nq = n] = dU[q][(cw + 4g + r) * k + j]
+#pragma unroll
+    for (int nq = 0; nq < NQ; ++nq)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int q = 16 * nq + n;
+        const int64_t c2 = cw + 4 * g + r;
+        if (q < rank && c2 < s.D) P.dUp[((int64_t)blockIdx.y * rank + q) * Dk + c2 * K + j] = dUacc[j][nq][r];
+      }
+  }
+}
+
+}  // namespace bwdlr
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+bool bwd_fused_supported(const Shape &s) {
+  return s.kind == DYNCONV_HEADWISE ? bwd_headwise_supported(s) : bwd_lowrank_supported(s);
+}
+
+BwdLayout bwd_layout(const Shape &s) {
+  return s.kind == DYNCONV_HEADWISE ? bwd_headwise_layout(s) : bwd_lowrank_layout(s);
+}
+
+bool bwd_lowrank_supported(const Shape &s) {
+  return s.kind == DYNCONV_LOWRANK && s.D % 16 == 0 && s.k <= 4 && s.rank >= 1 && s.rank <= 32;
+}
+
+BwdLayout bwd_lowrank_layout(const Shape &s) {
+  BwdLayout L = {};
+  L.Dt = bwdlr::kDt;
+  L.n_slices = (int)ceil_div(s.D, bwdlr::kDt);
+  L.n_tiles = (int)ceil_div(s.BT, 32);
+  // token ranges: about two resident 8-wave blocks per CU over 256 CUs
+  const int target = 512;
+  int tpb = 1;
+  while ((int64_t)L.n_slices * ceil_div(L.n_tiles, tpb) > target) ++tpb;
+  L.tpb = tpb;
+  L.n_ranges = (int)ceil_div(L.n_tiles, tpb);
+  L.SL = 0;
+  L.R = s.rank;
+  return L;
+}
+
+int bwd_lowrank(const Shape &s, const BwdLayout &L, const float *z, const void *U, const void *w0, const void *x,
+                const void *dy, void *dx, float *gpart, float *dUp, float *dw0p, hipStream_t st) {
+  bwdlr::Params P;
+  P.s = s;
+  P.x = (const bf16 *)x;
+  P.dy = (const bf16 *)dy;
+  P.dx = (bf16 *)dx;
+  P.z = z;
+  P.U = (const bf16 *)U;
+  P.w0 = (const bf16 *)w0;
+  P.gpart = gpart;
+  P.dUp = dUp;
+  P.dw0p = dw0p;
+  P.tpb = L.tpb;
+  P.n_tiles = L.n_tiles;
+  const dim3 grid((unsigned)L.n_slices, (unsigned)L.n_ranges), block(bwdlr::kW * 64);
+  const int KQ = (int)ceil_div(s.rank + 1, 32), NQ = (int)ceil_div(s.rank, 16);
+  const bool tr = trace_begin(DYNCONV_K_BWD_CONV, st);
+  int rc = 0;
+#define LR(K_, KQ_, NQ_) hipLaunchKernelGGL((bwdlr::k_bwd_lr<K_, KQ_, NQ_>), grid, block, 0, st, P)
+#define LR_K(K_)                                  \
+  if (KQ == 1 && NQ == 1) LR(K_, 1, 1);           \
+  else if (KQ == 1 && NQ == 2) LR(K_, 1, 2);      \
+  else if (KQ == 2 && NQ == 2) LR(K_, 2, 2);      \
+  else rc = DYNCONV_E_LIMIT;
+  switch (s.k) {
+    case 1: LR_K(1) break;
+    case 2: LR_K(2) break;
+    case 3: LR_K(3) break;
+    case 4: LR_K(4) break;
+    default: rc = DYNCONV_E_LIMIT;
+  }
+#undef LR_K
+#undef LR
+  trace_end(tr, st);
+  return rc;
+}
+
+}  // namespace dynconv

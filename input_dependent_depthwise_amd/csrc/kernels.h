@@ -39,31 +39,32 @@ size_t fwd_lowrank_ws_bytes(const Shape &s);
 int prep_lowrank_frags(const Shape &s, const void *U, const void *w0, void *Uf, hipStream_t st);
 int fwd_lowrank(const Shape &s, const float *z, const void *Uf, const void *x, void *y, hipStream_t st);
 
-// --- fused backward conv (conv_bwd.hip), bf16 ---
+// --- fused backward conv, bf16 ---
+// Layout of one backward pass over the channels (slices of Dt channels, grid
+// x) and the tokens (n_ranges blocks, grid y), and of its partial sums.
 struct BwdLayout {
-  int KP;        // taps padded to 4 or 8
   int Dt;        // channels per slice
-  int n_slices;  // 128-channel slices (grid x)
-  int n_tiles;   // 32-token tiles
-  int tpb;       // tiles per block
-  int n_ranges;  // token ranges (grid y)
+  int n_slices;  // slices (grid x)
+  int n_tiles;   // low-rank: 32-token tiles
+  int tpb;       // low-rank: tiles per block; head-wise: tokens per wave
+  int n_ranges;  // blocks along the tokens (grid y): rows of the dU / dw0 partials
   int SL;        // head-wise: head slots per slice
   int R;         // columns of the per-slice partial (rank, or SL*k)
 };
+// whether the fused path covers the shape, and its layout (dispatches on kind)
+bool bwd_fused_supported(const Shape &s);
 BwdLayout bwd_layout(const Shape &s);
-// head-wise: one lane per 8 (or 4) channels walking along time (conv_bwd_headwise.hip);
-// its layout reuses BwdLayout with Dt = channels per wave span, tpb = tokens per
-// wave and n_ranges = blocks along tokens (dw0 partials)
+// head-wise: one lane per 8 (or 4) channels walking along time (conv_bwd_headwise.hip)
 bool bwd_headwise_supported(const Shape &s);
 BwdLayout bwd_headwise_layout(const Shape &s);
 int bwd_headwise(const Shape &s, const BwdLayout &L, const float *u, const void *w0, const void *x,
                  const void *dy, void *dx, float *gpart, float *dw0p, hipStream_t st);
-bool bwd_fused_supported(const Shape &s);
-size_t bwd_prep_dz_bytes(const Shape &s);
-int prep_dz_frags(const Shape &s, const void *U, void *Udz, hipStream_t st);
-int bwd_conv(const Shape &s, const BwdLayout &L, const float *gen, const void *Uf, const void *Udz,
-             const void *w0, const void *x, const void *dy, void *dx, float *gpart, float *dUp,
-             float *dw0p, hipStream_t st);
+// low-rank: filter, dz and dU on matrix cores, 8 waves x 16 channels per block
+// (conv_bwd_lowrank.hip); R = rank
+bool bwd_lowrank_supported(const Shape &s);
+BwdLayout bwd_lowrank_layout(const Shape &s);
+int bwd_lowrank(const Shape &s, const BwdLayout &L, const float *z, const void *U, const void *w0, const void *x,
+                const void *dy, void *dx, float *gpart, float *dUp, float *dw0p, hipStream_t st);
 
 // --- generator gradients (gen_bwd.hip), bf16 ---
 struct GenBwdLayout {
