@@ -65,6 +65,9 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
                                          false);
 }
+// a.lo*b.lo + a.hi*b.hi (written with the builtin: hand-issued VALU code
+// would bypass the compiler's hazard tracking)
+__device__ __forceinline__ float dot2z(uint32_t a, uint32_t b) { return dot2(a, b, 0.f); }
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
   const bf16x2_t p = {(bf16)a, (bf16)b};
   return __builtin_bit_cast(uint32_t, p);
@@ -91,7 +94,7 @@ k_bwd_lr(Params P) {
   __shared__ __attribute__((aligned(16))) bf16 dys[TR * kRow];         // dy rows t0 .. t0+31+KH
   __shared__ __attribute__((aligned(16))) bf16 zs[TR * ZW];            // z rows t0 .. t0+31+KH, bf16
   __shared__ __attribute__((aligned(16))) bf16 zt[ZC * kGRow];         // z^T: rows q, tokens t0 .. t0+31
-  __shared__ __attribute__((aligned(16))) bf16 gt[kW][16 * kGRow];     // per wave: G of one tap, [channel][token]
+  __shared__ __attribute__((aligned(16))) bf16 gt[kW][32 * kGRow];     // per wave: G of a tap pair, [tap][channel][token]
   __shared__ __attribute__((aligned(16))) float red[kW][64 * RV];      // per wave: dz partial of a tile
 
   const int tid = threadIdx.x;
@@ -156,50 +159,62 @@ k_bwd_lr(Params P) {
   }
 
   // ---- global -> register prefetch of one tile ----
+  // Each thread's load slots are fixed for the block: precompute their row
+  // offset (relative to t0), global column and LDS offset once.
   const int tile_lo = blockIdx.y * P.tpb;
   const int tile_hi = min(P.n_tiles, tile_lo + P.tpb);
+  const int BT = (int)s.BT, D = (int)s.D;  // B*T*D < 2^31 (host-checked)
+  int v_row[kVL], v_goff[kVL], v_loff[kVL];
+  bool v_isx[kVL], v_ok[kVL];
+#pragma unroll
+  for (int q = 0; q < kVL; ++q) {
+    const int e = tid + q * NT;
+    const bool isx = e < TR * CH;
+    const int e2 = isx ? e : e - TR * CH;
+    const int r = e2 / CH, c16 = e2 % CH;
+    v_isx[q] = isx;
+    v_ok[q] = e < 2 * TR * CH && cblk + c16 * 8 < s.D;
+    v_row[q] = isx ? r - KH : r;
+    v_goff[q] = (int)cblk + c16 * 8;
+    v_loff[q] = r * kRow + c16 * 8;
+  }
+  int z_row[kZL], z_col[kZL];
+  bool z_ok[kZL];
+#pragma unroll
+  for (int q = 0; q < kZL; ++q) {
+    const int e = tid + q * NT;
+    z_row[q] = e / ZC;
+    z_col[q] = e % ZC;
+    z_ok[q] = e < TR * ZC && z_col[q] < rank;
+  }
   uint4 vpre[kVL];
   float zpre[kZL];
   auto prefetch = [&](int tile) {
-    const int64_t t0 = (int64_t)tile * 32;
+    const int t0 = tile * 32;
 #pragma unroll
     for (int q = 0; q < kVL; ++q) {
-      const int e = tid + q * NT;
-      const bool isx = e < TR * CH;
-      const int e2 = isx ? e : e - TR * CH;
-      const int r = e2 / CH, c16 = e2 % CH;
-      const int64_t row = isx ? t0 - KH + r : t0 + r;
+      const int row = t0 + v_row[q];
       vpre[q] = make_uint4(0, 0, 0, 0);
-      if (e < 2 * TR * CH && row >= 0 && row < s.BT && cblk + c16 * 8 < s.D)
-        vpre[q] = *reinterpret_cast<const uint4 *>((isx ? P.x : P.dy) + row * s.D + cblk + c16 * 8);
+      if (v_ok[q] && row >= 0 && row < BT)
+        vpre[q] = *reinterpret_cast<const uint4 *>((v_isx[q] ? P.x : P.dy) + (row * D + v_goff[q]));
     }
 #pragma unroll
     for (int q = 0; q < kZL; ++q) {
-      const int e = tid + q * NT;
-      const int r = e / ZC, qq = e % ZC;
-      const int64_t row = t0 + r;
-      zpre[q] = (e < TR * ZC && qq < rank && row < s.BT) ? P.z[row * rank + qq] : 0.f;
+      const int row = t0 + z_row[q];
+      zpre[q] = (z_ok[q] && row < BT) ? P.z[row * rank + z_col[q]] : 0.f;
     }
   };
   auto stage = [&]() {
 #pragma unroll
-    for (int q = 0; q < kVL; ++q) {
-      const int e = tid + q * NT;
-      if (e < 2 * TR * CH) {
-        const bool isx = e < TR * CH;
-        const int e2 = isx ? e : e - TR * CH;
-        const int r = e2 / CH, c16 = e2 % CH;
-        *reinterpret_cast<uint4 *>((isx ? xs : dys) + r * kRow + c16 * 8) = vpre[q];
-      }
-    }
+    for (int q = 0; q < kVL; ++q)
+      if (v_ok[q] || (tid + q * NT < 2 * TR * CH))
+        *reinterpret_cast<uint4 *>((v_isx[q] ? xs : dys) + v_loff[q]) = vpre[q];
 #pragma unroll
     for (int q = 0; q < kZL; ++q) {
-      const int e = tid + q * NT;
-      const int r = e / ZC, qq = e % ZC;
-      if (e < TR * ZC && qq < rank) {
+      if (z_ok[q]) {
         const bf16 v = (bf16)zpre[q];
-        zs[r * ZW + qq] = v;
-        if (r < 32) zt[qq * kGRow + r] = v;
+        zs[z_row[q] * ZW + z_col[q]] = v;
+        if (z_row[q] < 32) zt[z_col[q] * kGRow + z_row[q]] = v;
       }
     }
   };
@@ -249,7 +264,7 @@ k_bwd_lr(Params P) {
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
       for (int mq = 0; mq < NQ; ++mq) dzacc[tb][mq] = f32x4{0.f, 0.f, 0.f, 0.f};
-    uint32_t gpair[2][4];  // G of tap 2jp (low half) and 2jp+1 (high half), channel r, per token block
+    float gprev[2][4];  // G of the even tap of the current pair (fp32)
 
 #pragma unroll
     for (int j = 0; j < K; ++j) {
@@ -269,7 +284,7 @@ k_bwd_lr(Params P) {
         } else {
           const uint2 d = *reinterpret_cast<const uint2 *>(&dys[(16 * tb + n + j) * kRow + wc]);
           w[0] = d.x, w[1] = d.y;
-          if (edge_hi && pos[tb] + j > s.T - 1) w[0] = 0u, w[1] = 0u;
+          if (__builtin_expect(edge_hi, 0) && pos[tb] + j > s.T - 1) w[0] = 0u, w[1] = 0u;
         }
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
@@ -279,41 +294,56 @@ k_bwd_lr(Params P) {
         // G[s, c, j] = dy[s, c] x[s-j, c] (x before the sequence start is zero)
         const uint2 xv = *reinterpret_cast<const uint2 *>(&xs[(16 * tb + n + KH - j) * kRow + wc]);
         uint32_t xw[2] = {xv.x, xv.y};
-        if (edge_lo && j > pos[tb]) xw[0] = 0u, xw[1] = 0u;
+        if (__builtin_expect(edge_lo, 0) && j > pos[tb]) xw[0] = 0u, xw[1] = 0u;
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-          gv[tb][2 * p] = dot2(xw[p], dlo[tb][p], 0.f);
-          gv[tb][2 * p + 1] = dot2(xw[p], dhi[tb][p], 0.f);
+          gv[tb][2 * p] = dot2z(xw[p], dlo[tb][p]);
+          gv[tb][2 * p + 1] = dot2z(xw[p], dhi[tb][p]);
         }
       }
-      // G of this tap, bf16: into the tap-pair operand and token-contiguous into LDS
+      if (!(j & 1) && j < K - 1) {
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) gprev[tb][r] = gv[tb][r];
+        continue;
+      }
+      // a tap pair (2jp, 2jp+1) is complete (the odd tap is zero past k):
+      // bf16 pairs, the dz MFMA and the token-contiguous copy for dU
+      const int jp = j >> 1;
+      const bool odd = j & 1;
+      uint32_t gpair[2][4];
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const uint32_t b = __builtin_bit_cast(uint16_t, (bf16)gv[tb][r]);
-          gpair[tb][r] = (j & 1) ? (gpair[tb][r] | (b << 16)) : b;
-          *reinterpret_cast<uint16_t *>(&gtw[(4 * g + r) * kGRow + 16 * tb + n]) = (uint16_t)b;
+          gpair[tb][r] = odd ? pack2(gprev[tb][r], gv[tb][r]) : pack2(gv[tb][r], 0.f);
+          asm("" : "+v"(gpair[tb][r]));  // store the halves of this register (no re-rounding)
+          *reinterpret_cast<uint16_t *>(&gtw[(4 * g + r) * kGRow + 16 * tb + n]) = (uint16_t)gpair[tb][r];
+          if (odd)
+            *reinterpret_cast<uint16_t *>(&gtw[(16 + 4 * g + r) * kGRow + 16 * tb + n]) = (uint16_t)(gpair[tb][r] >> 16);
         }
-      // dz, once a tap pair is complete: B[k = 8g + i][token n], k <-> (channel 4g + i/2, tap 2jp + i%2)
-      if ((j & 1) || j == K - 1) {
-        const int jp = j >> 1;
+      // dz: B[k = 8g + i][token n], k <-> (channel 4g + i/2, tap 2jp + i%2)
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-          const bf16x8 bb = as_bf16x8(make_uint4(gpair[tb][0], gpair[tb][1], gpair[tb][2], gpair[tb][3]));
+      for (int tb = 0; tb < 2; ++tb) {
+        const bf16x8 bb = as_bf16x8(make_uint4(gpair[tb][0], gpair[tb][1], gpair[tb][2], gpair[tb][3]));
 #pragma unroll
-          for (int mq = 0; mq < NQ; ++mq) dzacc[tb][mq] = mfma16(za[jp][mq], bb, dzacc[tb][mq]);
-        }
+        for (int mq = 0; mq < NQ; ++mq) dzacc[tb][mq] = mfma16(za[jp][mq], bb, dzacc[tb][mq]);
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // dU: A[m = channel n][k = token 8g + i] = G; B = z^T.  dw0: the same fragment dotted with ones.
-      {
-        const uint4 raw = *reinterpret_cast<const uint4 *>(&gtw[n * kGRow + 8 * g]);
+      // dU: A[m = channel n][k = token 8g + i] = G of the tap; B = z^T.  dw0: the
+      // same fragment dotted with ones.
 #pragma unroll
-        for (int nq = 0; nq < NQ; ++nq) dUacc[j][nq] = mfma16(as_bf16x8(raw), zb[nq], dUacc[j][nq]);
-        dw0acc[j] = dot2(raw.w, ones, dot2(raw.z, ones, dot2(raw.y, ones, dot2(raw.x, ones, dw0acc[j]))));
+      for (int jj = 0; jj < 2; ++jj) {
+        const int jt = 2 * jp + jj;
+        if (jt < K) {
+          const uint4 raw = *reinterpret_cast<const uint4 *>(&gtw[(16 * jj + n) * kGRow + 8 * g]);
+#pragma unroll
+          for (int nq = 0; nq < NQ; ++nq) dUacc[jt][nq] = mfma16(as_bf16x8(raw), zb[nq], dUacc[jt][nq]);
+          dw0acc[jt] = dot2(raw.w, ones, dot2(raw.z, ones, dot2(raw.y, ones, dot2(raw.x, ones, dw0acc[jt]))));
+        }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
