@@ -73,7 +73,6 @@ struct Plan {
   size_t cache = 0;  // generator cache slot, fp32 [BT, N] (used when the caller gives none)
   size_t g = 0;      // simple path: du or dz, fp32 [BT, N]; fused path: g, bf16 [BT, Np]
   size_t mt = 0;     // transposed, padded generator weight for the MFMA projection (bf16)
-  size_t uf = 0;     // U and w0 in filter-MFMA fragment order (bf16, low-rank)
   size_t gpart = 0;  // per-slice du / dz partials, fp32
   size_t dup = 0;    // per-range dU partials, fp32
   size_t dw0p = 0;   // per-range dw0 partials, fp32
@@ -99,7 +98,6 @@ Plan plan(const Shape &s, int dtype, int pass) {
   };
   pl.cache = take((size_t)s.BT * s.N * sizeof(float));
   if (dtype == DYNCONV_BF16) pl.mt = take(gen_proj_mfma_ws_bytes(s));
-  if (fast_lowrank(s, dtype)) pl.uf = take(fwd_lowrank_ws_bytes(s));
   if (pass == 1) {
     if (fast_bwd(s, dtype)) {
       const BwdLayout L = bwd_layout(s);
@@ -263,8 +261,7 @@ int dynconv_fwd(const dynconv_problem *p, const dynconv_gen *g, const void *h, c
     rc = p->dtype == DYNCONV_BF16 ? fwd_headwise<bf16>(s, cache, g->w0, x, y, stream)
                                   : fwd_headwise<float>(s, cache, g->w0, x, y, stream);
   } else if (fast_lowrank(s, p->dtype)) {
-    void *uf = (char *)workspace + pl.uf;
-    if (!(rc = prep_lowrank_frags(s, g->U, g->w0, uf, stream))) rc = fwd_lowrank(s, cache, uf, x, y, stream);
+    rc = fwd_lowrank(s, cache, g->U, g->w0, x, y, stream);
   } else if (p->dtype == DYNCONV_BF16) {
     rc = simple_fwd_conv<bf16>(s, cache, g->U, g->w0, x, y, stream);
   } else {

@@ -1,0 +1,44 @@
+// bufio.h -- raw buffer accesses (MUBUF) for libdynconv's streaming kernels.
+//
+// A buffer resource holds the base address and size of one tensor; an access
+// takes a 32-bit byte offset.  Offsets at or past the size read as zero and
+// drop stores, which lets a kernel issue every load and store of a tile
+// unconditionally (a masked lane gets kOutside as its offset) -- the memory
+// instruction count is then the same on every path, so the compiler's
+// wait-count bookkeeping stays exact instead of draining all loads in flight.
+#pragma once
+
+#include "common.h"
+
+namespace dynconv {
+
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// An offset past every tensor the kernels address this way (callers keep
+// those tensors below 2 GiB).
+constexpr uint32_t kOutside = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  return make_uint2(v[0], v[1]);
+}
+__device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t off, uint2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64((u32x2){v.x, v.y}, r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store_f32(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
+
+}  // namespace dynconv

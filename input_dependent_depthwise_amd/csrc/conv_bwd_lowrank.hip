@@ -30,9 +30,10 @@
 //     D[channel][q] = G^T z over the tile's 32 tokens (dU); the same fragment
 //     dotted with ones gives dw0.
 // The 8 waves' dz meet in LDS; the block writes one partial per (slice,
-// token).  The next tile's global loads are in flight while a tile is
-// computed.  Matrix-core fragments of U are built by each lane from global
+// token).  The global loads of the next tile (or, where registers allow, of
+// the one after) are in flight while a tile is computed.  Matrix-core fragments of U are built by each lane from global
 // memory at start (no separate preparation pass).
+#include "bufio.h"
 #include "kernels.h"
 #include "mfma.h"
 
@@ -87,6 +88,7 @@ k_bwd_lr(Params P) {
   constexpr int ZC = 16 * NQ;                 // z columns staged (rank padded)
   constexpr int kZL = (TR * ZC + NT - 1) / NT;
   constexpr int RV = 8 * NQ;                  // dz values per lane and tile
+  constexpr int NSET = KQ * NQ * K <= 4 ? 2 : 1;  // register sets of prefetched tiles (as registers allow)
   const Shape &s = P.s;
   const int rank = s.rank;
 
@@ -187,44 +189,51 @@ k_bwd_lr(Params P) {
     z_col[q] = e % ZC;
     z_ok[q] = e < TR * ZC && z_col[q] < rank;
   }
-  uint4 vpre[kVL];
-  float zpre[kZL];
-  auto prefetch = [&](int tile) {
+  // NSET register sets: tile i+NSET is loaded while tile i is computed
+  uint4 vpre[NSET][kVL];
+  float zpre[NSET][kZL];
+  // loads are issued unconditionally (masked slots read zeros from outside the buffer)
+  const auto rx = make_rsrc(P.x, (uint32_t)(s.BT * s.D * 2)), rdy = make_rsrc(P.dy, (uint32_t)(s.BT * s.D * 2));
+  const auto rz = make_rsrc(P.z, (uint32_t)(s.BT * rank * 4));
+  auto prefetch = [&](int set, int tile) {
     const int t0 = tile * 32;
 #pragma unroll
     for (int q = 0; q < kVL; ++q) {
       const int row = t0 + v_row[q];
-      vpre[q] = make_uint4(0, 0, 0, 0);
-      if (v_ok[q] && row >= 0 && row < BT)
-        vpre[q] = *reinterpret_cast<const uint4 *>((v_isx[q] ? P.x : P.dy) + (row * D + v_goff[q]));
+      const uint32_t off = (v_ok[q] && row >= 0 && row < BT) ? (uint32_t)(row * D + v_goff[q]) * 2u : kOutside;
+      vpre[set][q] = buf_load16(v_isx[q] ? rx : rdy, off);
     }
 #pragma unroll
     for (int q = 0; q < kZL; ++q) {
       const int row = t0 + z_row[q];
-      zpre[q] = (z_ok[q] && row < BT) ? P.z[row * rank + z_col[q]] : 0.f;
+      const uint32_t off = (z_ok[q] && row < BT) ? (uint32_t)(row * rank + z_col[q]) * 4u : kOutside;
+      zpre[set][q] = buf_load_f32(rz, off);
     }
   };
-  auto stage = [&]() {
+  auto stage = [&](int set) {
 #pragma unroll
     for (int q = 0; q < kVL; ++q)
       if (v_ok[q] || (tid + q * NT < 2 * TR * CH))
-        *reinterpret_cast<uint4 *>((v_isx[q] ? xs : dys) + v_loff[q]) = vpre[q];
+        *reinterpret_cast<uint4 *>((v_isx[q] ? xs : dys) + v_loff[q]) = vpre[set][q];
 #pragma unroll
     for (int q = 0; q < kZL; ++q) {
       if (z_ok[q]) {
-        const bf16 v = (bf16)zpre[q];
+        const bf16 v = (bf16)zpre[set][q];
         zs[z_row[q] * ZW + z_col[q]] = v;
         if (z_row[q] < 32) zt[z_col[q] * kGRow + z_row[q]] = v;
       }
     }
   };
 
-  if (tile_hi > tile_lo) prefetch(tile_lo);
+  if (tile_hi > tile_lo) prefetch(0, tile_lo);
+  if (NSET > 1 && tile_hi > tile_lo + 1) prefetch(NSET - 1, tile_lo + 1);
+  const auto rdx = make_rsrc(P.dx, (uint32_t)(s.BT * s.D * 2));
+  const auto rg = make_rsrc(P.gpart + (int64_t)blockIdx.x * s.BT * rank, (uint32_t)(s.BT * rank * 4));
   const uint32_t ones = 0x3f803f80u;     // bf16 pair (1, 1)
   const int wc = wave * kCW + 4 * g;     // the lane's first channel within the tile rows
   bf16 *gtw = gt[wave];
 
-  for (int tile = tile_lo; tile < tile_hi; ++tile) {
+  auto tile_step = [&](const int set, const int tile) {
     const int64_t t0 = (int64_t)tile * 32;
     int pos[2];
 #pragma unroll
@@ -234,9 +243,9 @@ k_bwd_lr(Params P) {
     const bool edge_hi = __any(KH > 0 && (pos[0] + KH > s.T - 1 || pos[1] + KH > s.T - 1));
 
     __syncthreads();  // the previous tile's LDS reads are done
-    stage();
+    stage(set);
     __syncthreads();
-    if (tile + 1 < tile_hi) prefetch(tile + 1);
+    if (tile + NSET < tile_hi) prefetch(set, tile + NSET);
 
     // dy of the lane's two tokens: fp32 (dx starts as dy) and bf16 pairs with one half cleared
     float dxacc[2][4];
@@ -350,13 +359,13 @@ k_bwd_lr(Params P) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
 
-    // dx of the lane's two tokens
+    // dx of the lane's two tokens (stores issued unconditionally; masked
+    // lanes write outside the buffer, which drops them)
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
       const int64_t t = t0 + 16 * tb + n;
-      if (t < s.BT && cw + 4 * g + 4 <= s.D)
-        *reinterpret_cast<uint2 *>(P.dx + t * s.D + cw + 4 * g) =
-            make_uint2(pack2(dxacc[tb][0], dxacc[tb][1]), pack2(dxacc[tb][2], dxacc[tb][3]));
+      const uint32_t off = (t < s.BT && cw + 4 * g + 4 <= s.D) ? (uint32_t)(t * s.D + cw + 4 * g) * 2u : kOutside;
+      buf_store8(rdx, off, make_uint2(pack2(dxacc[tb][0], dxacc[tb][1]), pack2(dxacc[tb][2], dxacc[tb][3])));
     }
     // dz partial of the wave: element (tb*NQ + mq)*4 + r = dz[t0 + 16tb + n][16mq + 4g + r]
 #pragma unroll
@@ -367,18 +376,24 @@ k_bwd_lr(Params P) {
             make_float4(dzacc[tb][mq][0], dzacc[tb][mq][1], dzacc[tb][mq][2], dzacc[tb][mq][3]);
     __syncthreads();
     // the 8 waves' sum, one partial per (slice, token): thread -> (token, q), q fastest
-    for (int o = tid; o < 32 * ZC; o += NT) {
+#pragma unroll
+    for (int it = 0; it < (32 * ZC + NT - 1) / NT; ++it) {
+      const int o = tid + it * NT;
       const int q = o % ZC, sr = o / ZC;
       const int64_t row = t0 + sr;
-      if (q < rank && row < s.BT) {
-        const int tb = sr >> 4, nn = sr & 15, mq = q >> 4, gg = (q >> 2) & 3, r = q & 3;
-        const int src = (16 * gg + nn) * RV + (tb * NQ + mq) * 4 + r;
-        float v = red[0][src];
+      const bool ok = o < 32 * ZC && q < rank && row < s.BT;
+      const int tb = sr >> 4, nn = sr & 15, mq = q >> 4, gg = (q >> 2) & 3, r = q & 3;
+      const int src = ok ? (16 * gg + nn) * RV + (tb * NQ + mq) * 4 + r : 0;
+      float v = red[0][src];
 #pragma unroll
-        for (int w = 1; w < kW; ++w) v += red[w][src];
-        P.gpart[((int64_t)blockIdx.x * s.BT + row) * rank + q] = v;
-      }
+      for (int w = 1; w < kW; ++w) v += red[w][src];
+      buf_store_f32(rg, ok ? (uint32_t)(row * rank + q) * 4u : kOutside, v);
     }
+  };
+  // unrolled by two so that each register set has fixed registers
+  for (int tile = tile_lo; tile < tile_hi; tile += 2) {
+    tile_step(0, tile);
+    if (tile + 1 < tile_hi) tile_step(NSET - 1, tile + 1);
   }
 
   // ---- block epilogue: dU and dw0 partials of this token range ----
@@ -416,7 +431,9 @@ BwdLayout bwd_layout(const Shape &s) {
 }
 
 bool bwd_lowrank_supported(const Shape &s) {
-  return s.kind == DYNCONV_LOWRANK && s.D % 16 == 0 && s.k <= 4 && s.rank >= 1 && s.rank <= 32;
+  // 32-bit element and byte offsets: x, dy, dx below 2 GiB
+  return s.kind == DYNCONV_LOWRANK && s.D % 16 == 0 && s.k <= 4 && s.rank >= 1 && s.rank <= 32 &&
+         s.BT * s.D * 2 < ((int64_t)1 << 31) - 64;
 }
 
 BwdLayout bwd_lowrank_layout(const Shape &s) {

@@ -17,9 +17,9 @@
 // elements 4b+r.  For k > 4 two more MFMAs give taps 4..7.  The bias w0
 // enters the same MFMA chain as one extra K row: the B operand (z) carries a
 // constant 1 at q = r and the A operand carries w0 there, so the filter
-// leaves the matrix core complete.  The A operand (U, w0 rearranged into
-// fragment order, bf16) is written once per call into the workspace by a
-// prep kernel and held in VGPRs while a block walks its tokens.
+// leaves the matrix core complete.  Each lane gathers its A-operand values
+// (U and w0 in fragment order, bf16) from global memory when the block
+// starts and holds them in VGPRs while the block walks its tokens.
 //
 // x rows t-k+1 .. t are read from an LDS tile (16-byte reads, rows padded
 // to spread banks) that the block fills with coalesced 16-byte loads; y is
@@ -31,47 +31,13 @@
 namespace dynconv {
 namespace lowrank {
 
-// ---------------------------------------------------------------------------
-// prep: A-operand fragments.  For 16-channel group g, quad p, tap half th,
-// MFMA row m, K index q (0 .. KQ*16-1):
-//   channel c = 16g + 8*((m/4)%2) + 4p + m/8,  tap j = 4*th + m%4
-//   value   = U[q, c*k+j] for q < r,  w0[c, j] for q == r,  0 otherwise (and 0 if j >= k)
-// stored as Uf[((g*2 + p)*THP + th)*32 + m][q], bf16, q contiguous.
-// ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256)
-k_prep_frag(Shape s, const bf16 *__restrict__ U, const bf16 *__restrict__ w0, bf16 *__restrict__ Uf,
-            int THP, int KQ) {
-  const int QP = KQ * 16;
-  const int64_t total = (s.D / 16) * 2 * THP * 32 * (int64_t)QP;
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= total) return;
-  const int q = (int)(idx % QP);
-  int64_t rest = idx / QP;
-  const int m = (int)(rest % 32);
-  rest /= 32;
-  const int th = (int)(rest % THP);
-  rest /= THP;
-  const int p = (int)(rest % 2);
-  const int64_t g = rest / 2;
-  const int64_t c = 16 * g + 8 * ((m / 4) % 2) + 4 * p + m / 8;
-  const int j = 4 * th + m % 4;
-  float v = 0.f;
-  if (j < s.k) {
-    if (q < s.rank)
-      v = (float)U[(int64_t)q * s.D * s.k + c * s.k + j];
-    else if (q == s.rank && w0)
-      v = (float)w0[c * s.k + j];
-  }
-  Uf[idx] = (bf16)v;
-}
-
 constexpr int kCPW = 2;               // 16-channel groups per wave
 constexpr int kDt = 4 * kCPW * 16;    // channels per block (4 waves)
 constexpr int kRowB = kDt * 2 + 16;   // LDS row stride of the x tile (bytes, padded)
 
 template <int K, int KQ>
 __global__ void __launch_bounds__(256)
-k_fwd_lowrank(Shape s, const float *__restrict__ z, const bf16 *__restrict__ Uf,
+k_fwd_lowrank(Shape s, const float *__restrict__ z, const bf16 *__restrict__ U, const bf16 *__restrict__ w0,
               const bf16 *__restrict__ x, bf16 *__restrict__ y, int tpb, int n_tiles) {
   constexpr int KP = 4;
   constexpr int KH = K - 1;             // history rows
@@ -94,20 +60,36 @@ k_fwd_lowrank(Shape s, const float *__restrict__ z, const bf16 *__restrict__ Uf,
     if (q >= s.rank) (&zs[0][0])[e] = (bf16)(q == s.rank ? 1.f : 0.f);
   }
 
-  // A fragments for this wave's groups: [g][p][kq]
+  // A fragments for this wave's groups [g][p][kq], gathered by each lane from
+  // U and w0: row m = tl is (channel 16gg + 8((m/4)%2) + 4p + m/8, tap m%4),
+  // K index q = 16kq + 8hh + i is U's row for q < r, the bias w0 for q = r,
+  // zero beyond (and for taps >= k)
   bf16x8 af[kCPW][2][KQ];
   bool glive[kCPW];
 #pragma unroll
   for (int g = 0; g < kCPW; ++g) {
     const int64_t gg = (cblk >> 4) + wave * kCPW + g;
     glive[g] = (wave * kCPW + g) * 16 < nch;
+    const int j = tl % 4;
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
+    for (int p = 0; p < 2; ++p) {
+      const int64_t c = 16 * gg + 8 * ((tl / 4) % 2) + 4 * p + tl / 8;
 #pragma unroll
-      for (int kq = 0; kq < KQ; ++kq)
-        af[g][p][kq] = glive[g] ? as_bf16x8(*reinterpret_cast<const uint4 *>(
-                                      Uf + ((gg * 2 + p) * 32 + tl) * (KQ * 16) + kq * 16 + hh * 8))
-                                : zero_bf16x8();
+      for (int kq = 0; kq < KQ; ++kq) {
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int q = 16 * kq + 8 * hh + i;
+          float u = 0.f;
+          if (glive[g] && j < K) {
+            if (q < s.rank) u = (float)U[(int64_t)q * s.D * K + c * K + j];
+            else if (q == s.rank && w0) u = (float)w0[c * K + j];
+          }
+          v[i] = u;
+        }
+        af[g][p][kq] = pack_bf16x8(v);
+      }
+    }
   }
 
   // per-thread load slots
@@ -209,24 +191,10 @@ k_fwd_lowrank(Shape s, const float *__restrict__ z, const bf16 *__restrict__ Uf,
 
 }  // namespace lowrank
 
-size_t fwd_lowrank_ws_bytes(const Shape &s) {
-  const int THP = s.k <= 4 ? 1 : 2;
-  const int KQ = (int)ceil_div(s.rank + 1, 16);
-  return (size_t)(s.D / 16) * 2 * THP * 32 * KQ * 16 * sizeof(bf16);
-}
-
 bool fwd_lowrank_supported(const Shape &s) { return s.D % 16 == 0 && s.rank + 1 <= 64 && s.k <= 4; }
 
-int prep_lowrank_frags(const Shape &s, const void *U, const void *w0, void *Uf, hipStream_t st) {
-  const int THP = s.k <= 4 ? 1 : 2;
-  const int KQ = (int)ceil_div(s.rank + 1, 16);
-  const int64_t total = (s.D / 16) * 2 * THP * 32 * (int64_t)KQ * 16;
-  hipLaunchKernelGGL(lowrank::k_prep_frag, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0, st, s,
-                     (const bf16 *)U, (const bf16 *)w0, (bf16 *)Uf, THP, KQ);
-  return 0;
-}
-
-int fwd_lowrank(const Shape &s, const float *z, const void *Uf, const void *x, void *y, hipStream_t st) {
+int fwd_lowrank(const Shape &s, const float *z, const void *U, const void *w0, const void *x, void *y,
+                hipStream_t st) {
   using namespace lowrank;
   const int KQ = (int)ceil_div(s.rank + 1, 16);
   const int n_slices = (int)ceil_div(s.D, kDt);
@@ -238,8 +206,8 @@ int fwd_lowrank(const Shape &s, const float *z, const void *Uf, const void *x, v
   const bool tr = trace_begin(DYNCONV_K_FWD_CONV, st);
   int rc = 0;
 #define LAUNCH(K_, KQ_)                                                                             \
-  hipLaunchKernelGGL((k_fwd_lowrank<K_, KQ_>), grid, dim3(256), 0, st, s, z, (const bf16 *)Uf,    \
-                     (const bf16 *)x, (bf16 *)y, tpb, n_tiles)
+  hipLaunchKernelGGL((k_fwd_lowrank<K_, KQ_>), grid, dim3(256), 0, st, s, z, (const bf16 *)U,     \
+                     (const bf16 *)w0, (const bf16 *)x, (bf16 *)y, tpb, n_tiles)
 #define LAUNCH_K(K_)                          \
   switch (KQ) {                               \
     case 1: LAUNCH(K_, 1); break;             \

@@ -23,28 +23,56 @@
 namespace dynconv {
 namespace gbwd {
 
-// g[t, n] for n < N (zero-padded to Np), bf16.
+// g[t, n] for n < N (zero-padded to Np), bf16; four columns per thread.  The
+// slice partials are loaded 6 at a time ahead of the adds, which stay in
+// slice order (fixed-order sums).
 __global__ void __launch_bounds__(256)
 k_combine(Shape s, const float *__restrict__ gpart, int n_slices, int R, int Dt, int Np,
           bf16 *__restrict__ g) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t idx = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
   if (idx >= s.BT * Np) return;
   const int64_t t = idx / Np;
-  const int n = (int)(idx - t * Np);
-  float v = 0.f;
-  if (n < s.N) {
-    if (s.kind == DYNCONV_LOWRANK) {
-      for (int d = 0; d < n_slices; ++d) v += gpart[((int64_t)d * s.BT + t) * R + n];
+  const int n0 = (int)(idx - t * Np);  // Np is a multiple of 16: the four columns share a row
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  if (s.kind == DYNCONV_LOWRANK) {
+    if (n0 + 4 <= s.N && R % 4 == 0) {
+      const float *src = gpart + t * R + n0;
+      const int64_t stride = s.BT * R;
+      int d = 0;
+      for (; d + 6 <= n_slices; d += 6) {
+        float4 a[6];
+#pragma unroll
+        for (int u = 0; u < 6; ++u) a[u] = *reinterpret_cast<const float4 *>(src + (d + u) * stride);
+#pragma unroll
+        for (int u = 0; u < 6; ++u) v[0] += a[u].x, v[1] += a[u].y, v[2] += a[u].z, v[3] += a[u].w;
+      }
+      for (; d < n_slices; ++d) {
+        const float4 a = *reinterpret_cast<const float4 *>(src + d * stride);
+        v[0] += a.x, v[1] += a.y, v[2] += a.z, v[3] += a.w;
+      }
     } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (n0 + c < s.N)
+          for (int d = 0; d < n_slices; ++d) v[c] += gpart[((int64_t)d * s.BT + t) * R + n0 + c];
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int n = n0 + c;
+      if (n >= s.N) continue;
       const int e = n / s.k, j = n - e * s.k;
       const int d0 = (int)((int64_t)e * s.hd / Dt), d1 = (int)(((int64_t)(e + 1) * s.hd - 1) / Dt);
       for (int d = d0; d <= d1; ++d) {
         const int slot = e - (int)((int64_t)d * Dt / s.hd);
-        v += gpart[((int64_t)d * s.BT + t) * R + slot * s.k + j];
+        v[c] += gpart[((int64_t)d * s.BT + t) * R + slot * s.k + j];
       }
     }
   }
-  g[idx] = (bf16)v;
+  uint2 o;
+  o.x = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)v[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)v[1]) << 16);
+  o.y = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)v[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)v[3]) << 16);
+  *reinterpret_cast<uint2 *>(g + idx) = o;
 }
 
 // Mp[i, n] = M[i, n] zero-padded to Np columns (bf16).
@@ -62,7 +90,7 @@ k_pad_cols(const bf16 *__restrict__ M, bf16 *__restrict__ Mp, int64_t rows, int 
 template <int KS>
 __global__ void __launch_bounds__(256)
 k_dh(const bf16 *__restrict__ g, const bf16 *__restrict__ Mp, bf16 *__restrict__ dh, int64_t BT,
-     int d, int Np, int n_ib) {
+     int d, int Np, int n_ib, int Mcols) {
   // XCD-aware mapping: blocks go round-robin over 8 XCDs; keep a token tile's
   // row blocks on one XCD.
   const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
@@ -79,7 +107,10 @@ k_dh(const bf16 *__restrict__ g, const bf16 *__restrict__ Mp, bf16 *__restrict__
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const int n = ks * 16 + hh * 8;
-    const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4 *>(Mp + (int64_t)ia * Np + n));
+    // Mp has Mcols columns: Np (a padded copy) or N itself when N % 8 == 0, so
+    // that each 8-column chunk is all in or all out
+    const bf16x8 a = n < Mcols ? as_bf16x8(*reinterpret_cast<const uint4 *>(Mp + (int64_t)ia * Mcols + n))
+                               : zero_bf16x8();
     const bf16x8 bb = t < BT ? as_bf16x8(*reinterpret_cast<const uint4 *>(g + t * Np + n)) : zero_bf16x8();
     acc = mfma32(a, bb, acc);
   }
@@ -167,22 +198,46 @@ struct Red {
   int np;
 };
 
+// Four consecutive outputs per thread; the partial rows are loaded 8 at a
+// time ahead of the adds, which stay in partial order (fixed-order sums).
 __global__ void __launch_bounds__(256) k_finalize(Red r0, Red r1, Red r2) {
-  int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t idx = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  const int64_t q0 = (r0.n + 3) / 4 * 4, q1 = (r1.n + 3) / 4 * 4, q2 = (r2.n + 3) / 4 * 4;
   const Red *r;
-  if (idx < r0.n) {
+  if (idx < q0) {
     r = &r0;
-  } else if ((idx -= r0.n) < r1.n) {
+  } else if ((idx -= q0) < q1) {
     r = &r1;
-  } else if ((idx -= r1.n) < r2.n) {
+  } else if ((idx -= q1) < q2) {
     r = &r2;
   } else {
     return;
   }
-  if (!r->out) return;
-  float v = 0.f;
-  for (int p = 0; p < r->np; ++p) v += r->part[(int64_t)p * r->n + idx];
-  r->out[idx] = v;
+  if (!r->out || idx >= r->n) return;
+  const int64_t n = r->n;
+  if (idx + 4 <= n && n % 4 == 0) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    const float *src = r->part + idx;
+    int p = 0;
+    for (; p + 8 <= r->np; p += 8) {
+      float4 a[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) a[u] = *reinterpret_cast<const float4 *>(src + (int64_t)(p + u) * n);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v.x += a[u].x, v.y += a[u].y, v.z += a[u].z, v.w += a[u].w;
+    }
+    for (; p < r->np; ++p) {
+      const float4 a = *reinterpret_cast<const float4 *>(src + (int64_t)p * n);
+      v.x += a.x, v.y += a.y, v.z += a.z, v.w += a.w;
+    }
+    *reinterpret_cast<float4 *>(r->out + idx) = v;
+  } else {
+    for (int64_t e = idx; e < idx + 4 && e < n; ++e) {
+      float v = 0.f;
+      for (int p = 0; p < r->np; ++p) v += r->part[(int64_t)p * n + e];
+      r->out[e] = v;
+    }
+  }
 }
 
 }  // namespace gbwd
@@ -208,20 +263,25 @@ size_t gen_bwd_part_bytes(const Shape &s) {
 int gen_bwd(const Shape &s, const float *gpart, int n_slices, int R, int Dt, const void *h,
             const void *M, bf16 *g, bf16 *Mp, void *dh, float *dMp, hipStream_t st) {
   const GenBwdLayout L = gen_bwd_layout(s);
-  hipLaunchKernelGGL(gbwd::k_combine, dim3((unsigned)ceil_div(s.BT * L.Np, 256)), dim3(256), 0, st, s,
+  hipLaunchKernelGGL(gbwd::k_combine, dim3((unsigned)ceil_div(s.BT * L.Np / 4, 256)), dim3(256), 0, st, s,
                      gpart, n_slices, R, Dt, L.Np, g);
   const bool tr = trace_begin(DYNCONV_K_GEN_BWD, st);
   if (dh) {
-    hipLaunchKernelGGL(gbwd::k_pad_cols, dim3((unsigned)ceil_div(s.d * L.Np, 256)), dim3(256), 0, st,
-                       (const bf16 *)M, Mp, s.d, s.N, L.Np);
+    // the weight is read in place when its rows are whole 8-column chunks
+    const bool direct = s.N % 8 == 0;
+    if (!direct)
+      hipLaunchKernelGGL(gbwd::k_pad_cols, dim3((unsigned)ceil_div(s.d * L.Np, 256)), dim3(256), 0, st,
+                         (const bf16 *)M, Mp, s.d, s.N, L.Np);
+    const bf16 *Ma = direct ? (const bf16 *)M : Mp;
+    const int Mcols = direct ? s.N : L.Np;
     const int n_ib = (int)ceil_div(s.d, 128);
     const int tiles8 = (int)ceil_div(L.n_tiles, 8) * 8;
     const unsigned nblk = (unsigned)(tiles8 * n_ib);
     switch (L.Np / 16) {
 #define CASE(ks)                                                                                      \
   case ks:                                                                                            \
-    hipLaunchKernelGGL(gbwd::k_dh<ks>, dim3(nblk), dim3(256), 0, st, g, Mp, (bf16 *)dh, s.BT, (int)s.d, \
-                       L.Np, n_ib);                                                                   \
+    hipLaunchKernelGGL(gbwd::k_dh<ks>, dim3(nblk), dim3(256), 0, st, g, Ma, (bf16 *)dh, s.BT, (int)s.d, \
+                       L.Np, n_ib, Mcols);                                                            \
     break;
       CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)
       CASE(9) CASE(10) CASE(11) CASE(12) CASE(13) CASE(14) CASE(15) CASE(16)
@@ -248,10 +308,10 @@ int gen_bwd(const Shape &s, const float *gpart, int n_slices, int R, int Dt, con
 int finalize(const float *p0, float *o0, int64_t n0, int np0, const float *p1, float *o1, int64_t n1,
              int np1, const float *p2, float *o2, int64_t n2, int np2, hipStream_t st) {
   gbwd::Red r0{p0, o0, o0 ? n0 : 0, np0}, r1{p1, o1, o1 ? n1 : 0, np1}, r2{p2, o2, o2 ? n2 : 0, np2};
-  const int64_t n = r0.n + r1.n + r2.n;
-  if (n == 0) return 0;
+  const int64_t quads = ceil_div(r0.n, 4) + ceil_div(r1.n, 4) + ceil_div(r2.n, 4);
+  if (quads == 0) return 0;
   const bool tr = trace_begin(DYNCONV_K_FINALIZE, st);
-  hipLaunchKernelGGL(gbwd::k_finalize, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st, r0, r1, r2);
+  hipLaunchKernelGGL(gbwd::k_finalize, dim3((unsigned)ceil_div(quads, 256)), dim3(256), 0, st, r0, r1, r2);
   trace_end(tr, st);
   return 0;
 }

@@ -35,9 +35,8 @@ int fwd_headwise(const Shape &s, const float *u, const void *w0, const void *x, 
 
 // --- fused low-rank forward on matrix cores (conv_fwd_lowrank.hip), bf16 ---
 bool fwd_lowrank_supported(const Shape &s);
-size_t fwd_lowrank_ws_bytes(const Shape &s);
-int prep_lowrank_frags(const Shape &s, const void *U, const void *w0, void *Uf, hipStream_t st);
-int fwd_lowrank(const Shape &s, const float *z, const void *Uf, const void *x, void *y, hipStream_t st);
+int fwd_lowrank(const Shape &s, const float *z, const void *U, const void *w0, const void *x, void *y,
+                hipStream_t st);
 
 // --- fused backward conv, bf16 ---
 // Layout of one backward pass over the channels (slices of Dt channels, grid
