@@ -43,7 +43,9 @@ namespace bwdlr {
 constexpr int kW = 8;            // waves per block
 constexpr int kCW = 16;          // channels per wave
 constexpr int kDt = kW * kCW;    // channels per block
-constexpr int kRow = kDt + 8;    // LDS row of the x / dy tiles (bf16 elements)
+// LDS row of the x / dy tiles (bf16 elements): 68 dwords, so that the 8-byte
+// reads of 16 consecutive token rows x 2 channel quads cover all 64 banks once
+constexpr int kRow = kDt + 8;
 constexpr int kGRow = 40;        // LDS row of the token-contiguous tiles: 32 tokens + pad (bf16)
 
 struct Params {
@@ -88,6 +90,7 @@ k_bwd_lr(Params P) {
   constexpr int ZC = 16 * NQ;                 // z columns staged (rank padded)
   constexpr int kZL = (TR * ZC + NT - 1) / NT;
   constexpr int RV = 8 * NQ;                  // dz values per lane and tile
+  constexpr int RVP = RV + 4;                 // lane stride of the dz reduction buffer (bank spread)
   constexpr int NSET = KQ * NQ * K <= 4 ? 2 : 1;  // register sets of prefetched tiles (as registers allow)
   const Shape &s = P.s;
   const int rank = s.rank;
@@ -97,7 +100,7 @@ k_bwd_lr(Params P) {
   __shared__ __attribute__((aligned(16))) bf16 zs[TR * ZW];            // z rows t0 .. t0+31+KH, bf16
   __shared__ __attribute__((aligned(16))) bf16 zt[ZC * kGRow];         // z^T: rows q, tokens t0 .. t0+31
   __shared__ __attribute__((aligned(16))) bf16 gt[kW][32 * kGRow];     // per wave: G of a tap pair, [tap][channel][token]
-  __shared__ __attribute__((aligned(16))) float red[kW][64 * RV];      // per wave: dz partial of a tile
+  __shared__ __attribute__((aligned(16))) float red[kW][64 * RVP];     // per wave: dz partial of a tile
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -372,18 +375,19 @@ k_bwd_lr(Params P) {
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
       for (int mq = 0; mq < NQ; ++mq)
-        *reinterpret_cast<float4 *>(&red[wave][lane * RV + (tb * NQ + mq) * 4]) =
+        *reinterpret_cast<float4 *>(&red[wave][lane * RVP + (tb * NQ + mq) * 4]) =
             make_float4(dzacc[tb][mq][0], dzacc[tb][mq][1], dzacc[tb][mq][2], dzacc[tb][mq][3]);
     __syncthreads();
-    // the 8 waves' sum, one partial per (slice, token): thread -> (token, q), q fastest
+    // the 8 waves' sum, one partial per (slice, token): thread -> (q, token),
+    // token fastest (consecutive threads read consecutive lanes' rows)
 #pragma unroll
     for (int it = 0; it < (32 * ZC + NT - 1) / NT; ++it) {
       const int o = tid + it * NT;
-      const int q = o % ZC, sr = o / ZC;
+      const int sr = o % 32, q = o / 32;
       const int64_t row = t0 + sr;
       const bool ok = o < 32 * ZC && q < rank && row < s.BT;
       const int tb = sr >> 4, nn = sr & 15, mq = q >> 4, gg = (q >> 2) & 3, r = q & 3;
-      const int src = ok ? (16 * gg + nn) * RV + (tb * NQ + mq) * 4 + r : 0;
+      const int src = ok ? (16 * gg + nn) * RVP + (tb * NQ + mq) * 4 + r : 0;
       float v = red[0][src];
 #pragma unroll
       for (int w = 1; w < kW; ++w) v += red[w][src];
