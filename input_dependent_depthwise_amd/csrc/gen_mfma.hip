@@ -8,15 +8,15 @@
 // map's first (dense) factor, a tall-skinny GEMM: rows = tokens (16k-33k),
 // K = d_model (768-2048), N = n_heads*k or rank (16-256).
 //
-// One wave computes 32 rows x Np columns (Np = N rounded up to 16) with
-// v_mfma_f32_16x16x32_bf16: A fragments are 16-byte loads straight from h
-// (rows are K-contiguous), B fragments are 16-byte loads from a transposed,
+// A block of 4 waves computes 64 (or 128) rows x Np columns (Np = N rounded
+// up to 16) with v_mfma_f32_16x16x32_bf16: A fragments are 16-byte loads
+// straight from h (rows are K-contiguous); B comes from a transposed,
 // zero-padded copy Mt[Np][Kp] of the weight that a prep kernel writes into
-// the workspace (Kp = K rounded up to 32), so no bounds checks are needed on
-// B and the weight stays L2-resident.  When N is small the 4 waves of a block
-// split K and reduce through LDS in a fixed order (bitwise deterministic), so
-// that the grid still has several blocks per CU.  h is read once: the kernel
-// is bound by HBM for N <= 64 and near the MFMA/HBM ridge at N = 256.
+// the workspace (Kp = K rounded up to 32), staged one K-slice at a time in
+// LDS and shared by the block's waves, so the weight is read from L2 once
+// per block.  Narrow weights (N <= 32) use a K-split variant instead.  h is
+// read once: the kernel is bound by HBM for N <= 64 and near the MFMA/HBM
+// ridge at N = 256.
 #include "kernels.h"
 #include "mfma.h"
 
@@ -32,23 +32,107 @@ k_transpose_pad(const bf16 *__restrict__ M, bf16 *__restrict__ Mt, int K, int N,
   Mt[idx] = (n < N && k < K) ? M[(int64_t)k * N + n] : (bf16)0.f;
 }
 
-template <int NT, int KS>
+// Block: 4 waves x (16 * RW) rows of h, all Np columns.  Per K-step of 32 the
+// block stages the [Np][32] slice of Mt in LDS (double-buffered, one barrier
+// per step); each wave reads its h rows straight from global memory (16-byte
+// A fragments) and multiplies them against every column tile of the slice.
+// Both operands of the next step are loaded while the current one is used.
+template <int NT, int RW>
 __global__ void __launch_bounds__(256)
 k_gen_proj_mfma(const bf16 *__restrict__ h, const bf16 *__restrict__ Mt, float *__restrict__ out,
                 int64_t M, int K, int Kp, int N) {
-  constexpr int RG = 4 / KS;  // row groups of 32 per block
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int rg = wave % RG;   // row group of this wave
-  const int ks = wave / RG;   // K slice of this wave
-  const int64_t rbase = ((int64_t)blockIdx.x * RG + rg) * 32;
+  constexpr int NP = NT * 16;
+  constexpr int BROW = 40;                       // LDS row of the B slice: 32 k + pad (bf16)
+  constexpr int CHUNKS = NP * 4;                 // 16-byte chunks of a [NP][32] slice
+  constexpr int CPT = (CHUNKS + 255) / 256;      // chunks per thread
+  __shared__ __attribute__((aligned(16))) bf16 bs[2][NP * BROW];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lk = (lane >> 4) * 8;
+  const int64_t rbase = ((int64_t)blockIdx.x * 4 + wave) * 16 * RW;
 
-  // rows this lane feeds as A (clamped: rows >= M are computed but never stored)
-  const int64_t ra = rbase + lr < M ? rbase + lr : M - 1;
+  const bf16 *ha[RW];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const int64_t row = rbase + 16 * r + lr;
+    ha[r] = h + (row < M ? row : M - 1) * K;  // rows >= M are computed but never stored
+  }
+  f32x4 acc[RW][NT];
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[r][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int steps = Kp / 32;
+  uint4 bpre[CPT];
+  bf16x8 apre[RW];
+  auto load = [&](int st) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int e = tid + c * 256;
+      const int n = e >> 2, kc = (e & 3) * 8;
+      bpre[c] = e < CHUNKS ? *reinterpret_cast<const uint4 *>(Mt + (int64_t)n * Kp + st * 32 + kc)
+                           : make_uint4(0, 0, 0, 0);
+    }
+    const int k = st * 32 + lk;
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+      apre[r] = k < K ? as_bf16x8(*reinterpret_cast<const uint4 *>(ha[r] + k)) : zero_bf16x8();
+  };
+  if (steps > 0) load(0);
+  for (int st = 0; st < steps; ++st) {
+    const int buf = st & 1;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int e = tid + c * 256;
+      if (e < CHUNKS) *reinterpret_cast<uint4 *>(&bs[buf][(e >> 2) * BROW + (e & 3) * 8]) = bpre[c];
+    }
+    bf16x8 a[RW];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) a[r] = apre[r];
+    __syncthreads();
+    if (st + 1 < steps) load(st + 1);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const bf16x8 b = as_bf16x8(*reinterpret_cast<const uint4 *>(&bs[buf][(n * 16 + lr) * BROW + lk]));
+#pragma unroll
+      for (int r = 0; r < RW; ++r) acc[r][n] = mfma16(a[r], b, acc[r][n]);
+    }
+  }
+
+  // D fragment: lane holds D[4*(lane/16) + i][lane%16]
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const int col = n * 16 + lr;
+      if (col >= N) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t row = rbase + r * 16 + (lane >> 4) * 4 + i;
+        if (row < M) out[row * N + col] = acc[r][n][i];
+      }
+    }
+}
+
+// Narrow weights (N <= 32): the B slice is too small to be worth staging,
+// and one row tile per wave would leave the chip mostly idle.  A block is 4
+// waves over the same 32 rows, each summing a quarter of K; B fragments are
+// read straight from the (L2-resident) padded weight.  Four K-steps of loads
+// are issued before their MFMAs so that enough of h is in flight.  The K
+// quarters are reduced through LDS in a fixed order (bitwise deterministic).
+template <int NT>
+__global__ void __launch_bounds__(256)
+k_gen_proj_ksplit(const bf16 *__restrict__ h, const bf16 *__restrict__ Mt, float *__restrict__ out,
+                  int64_t M, int K, int Kp, int N) {
+  constexpr int KS = 4, U = 4;
+  const int lane = threadIdx.x & 63, ks = threadIdx.x >> 6;
+  const int lr = lane & 15, lk = (lane >> 4) * 8;
+  const int64_t rbase = (int64_t)blockIdx.x * 32;
+  const int64_t ra = rbase + lr < M ? rbase + lr : M - 1;  // rows >= M are never stored
   const int64_t rb = rbase + 16 + lr < M ? rbase + 16 + lr : M - 1;
-  const bf16 *ha = h + ra * K;
-  const bf16 *hb = h + rb * K;
+  const bf16 *ha = h + ra * K + lk;
+  const bf16 *hb = h + rb * K + lk;
+  const bf16 *mb = Mt + (int64_t)lr * Kp + lk;
 
   f32x4 acc[2][NT];
 #pragma unroll
@@ -56,44 +140,60 @@ k_gen_proj_mfma(const bf16 *__restrict__ h, const bf16 *__restrict__ Mt, float *
 #pragma unroll
     for (int n = 0; n < NT; ++n) acc[r][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int steps = Kp / 32;
+  const int steps = Kp / 32, full = K / 32;
   const int per = (steps + KS - 1) / KS;
   const int s0 = ks * per, s1 = min(steps, s0 + per);
-  for (int s = s0; s < s1; ++s) {
-    const int k = s * 32 + lk;
+  const int s1f = min(s1, full);  // steps whose 32 k all lie below K
+  int s = s0;
+  for (; s + U <= s1f; s += U) {
+    bf16x8 a0[U], a1[U], b[U][NT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = (s + u) * 32;
+      a0[u] = as_bf16x8(*reinterpret_cast<const uint4 *>(ha + k));
+      a1[u] = as_bf16x8(*reinterpret_cast<const uint4 *>(hb + k));
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+        b[u][n] = as_bf16x8(*reinterpret_cast<const uint4 *>(mb + (int64_t)n * 16 * Kp + k));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        acc[0][n] = mfma16(a0[u], b[u][n], acc[0][n]);
+        acc[1][n] = mfma16(a1[u], b[u][n], acc[1][n]);
+      }
+  }
+  for (; s < s1; ++s) {
+    const int k = s * 32;
     bf16x8 a0 = zero_bf16x8(), a1 = zero_bf16x8();
-    if (k < K) {  // K is a multiple of 8, so a fragment is all-in or all-out
+    if (k + lk < K) {  // K is a multiple of 8: a fragment is all-in or all-out
       a0 = as_bf16x8(*reinterpret_cast<const uint4 *>(ha + k));
       a1 = as_bf16x8(*reinterpret_cast<const uint4 *>(hb + k));
     }
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      const bf16x8 b = as_bf16x8(*reinterpret_cast<const uint4 *>(Mt + (int64_t)(n * 16 + lr) * Kp + k));
+      const bf16x8 b = as_bf16x8(*reinterpret_cast<const uint4 *>(mb + (int64_t)n * 16 * Kp + k));
       acc[0][n] = mfma16(a0, b, acc[0][n]);
       acc[1][n] = mfma16(a1, b, acc[1][n]);
     }
   }
 
-  if constexpr (KS > 1) {
-    // fixed-order reduction of the K slices through LDS
-    __shared__ f32x4 red[KS - 1][RG][2][NT][64];
-    if (ks > 0) {
+  __shared__ f32x4 red[KS - 1][2][NT][64];
+  if (ks > 0) {
 #pragma unroll
-      for (int r = 0; r < 2; ++r)
+    for (int r = 0; r < 2; ++r)
 #pragma unroll
-        for (int n = 0; n < NT; ++n) red[ks - 1][rg][r][n][lane] = acc[r][n];
-    }
-    __syncthreads();
-    if (ks > 0) return;
-#pragma unroll
-    for (int q = 0; q < KS - 1; ++q)
-#pragma unroll
-      for (int r = 0; r < 2; ++r)
-#pragma unroll
-        for (int n = 0; n < NT; ++n) acc[r][n] += red[q][rg][r][n][lane];
+      for (int n = 0; n < NT; ++n) red[ks - 1][r][n][lane] = acc[r][n];
   }
-
-  // D fragment: lane holds D[4*(lane/16) + i][lane%16]
+  __syncthreads();
+  if (ks > 0) return;
+#pragma unroll
+  for (int q = 0; q < KS - 1; ++q)
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[r][n] += red[q][r][n][lane];
 #pragma unroll
   for (int r = 0; r < 2; ++r)
 #pragma unroll
@@ -111,17 +211,17 @@ k_gen_proj_mfma(const bf16 *__restrict__ h, const bf16 *__restrict__ Mt, float *
 template <int NT>
 void launch_nt(const bf16 *h, const bf16 *Mt, float *out, int64_t M, int K, int Kp, int N,
                hipStream_t st) {
-  // split K across the block's waves when the row count alone gives too few blocks
-  if constexpr (NT <= 4) {
-    if (M / 128 < 1024) {
-      hipLaunchKernelGGL((k_gen_proj_mfma<NT, 4>), dim3((unsigned)ceil_div(M, 32)), dim3(256), 0, st,
-                         h, Mt, out, M, K, Kp, N);
-      return;
-    }
-  }
-  {
-    hipLaunchKernelGGL((k_gen_proj_mfma<NT, 1>), dim3((unsigned)ceil_div(M, 128)), dim3(256), 0, st, h,
-                       Mt, out, M, K, Kp, N);
+  // two row tiles per wave when the weight is wide (its LDS slice is then
+  // reused twice per read) and the rows still give one block per CU
+  if constexpr (NT <= 2) {
+    hipLaunchKernelGGL((k_gen_proj_ksplit<NT>), dim3((unsigned)ceil_div(M, 32)), dim3(256), 0, st, h, Mt,
+                       out, M, K, Kp, N);
+  } else if (NT >= 4 && M >= 256 * 128) {
+    hipLaunchKernelGGL((k_gen_proj_mfma<NT, 2>), dim3((unsigned)ceil_div(M, 128)), dim3(256), 0, st, h, Mt,
+                       out, M, K, Kp, N);
+  } else {
+    hipLaunchKernelGGL((k_gen_proj_mfma<NT, 1>), dim3((unsigned)ceil_div(M, 64)), dim3(256), 0, st, h, Mt,
+                       out, M, K, Kp, N);
   }
 }
 
