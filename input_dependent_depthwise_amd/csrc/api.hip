@@ -85,7 +85,7 @@ inline bool fast_lowrank(const Shape &s, int dtype) {
   return dtype == DYNCONV_BF16 && s.kind == DYNCONV_LOWRANK && fwd_lowrank_supported(s);
 }
 inline bool fast_bwd(const Shape &s, int dtype) {
-  return dtype == DYNCONV_BF16 && bwd_fused_supported(s);
+  return dtype == DYNCONV_BF16 && bwd_fused_supported(s) && gen_bwd_supported(s);
 }
 
 Plan plan(const Shape &s, int dtype, int pass) {

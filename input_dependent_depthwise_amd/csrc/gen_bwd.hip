@@ -9,70 +9,148 @@
 //   dM[i, n]  = sum_t h[t, i] g[t, n]
 // Kernels:
 //   k_combine  g = fixed-order sum of the conv kernel's per-slice partials,
-//              written once as bf16 [BT, Np] (the MFMA operand precision);
-//   k_dh       dh^T tiles = M . g^T on v_mfma_f32_32x32x16_bf16, blocks of one
-//              32-token tile x 128 rows of d, mapped so that all row blocks of
-//              a token tile run on the same XCD (its g tile stays in that L2);
-//   k_dM       per (64-row chunk of d, token range) partials of h^T g on
-//              v_mfma_f32_16x16x32_bf16, both operands staged transposed in
-//              LDS (token-contiguous);
+//              written as bf16 (the MFMA operand precision) twice: g [BT, Np]
+//              for dh and g^T [Np, BTp] (token-contiguous) for dM;
+//   k_dh       dh^T tiles = M . g^T on v_mfma_f32_32x32x16_bf16; a block holds
+//              256 rows of M in registers and walks a token range with the g
+//              tiles staged in LDS, writing dh rows through LDS;
+//   k_dM       per (128-row chunk of d, token range) partials of h^T g on
+//              v_mfma_f32_16x16x32_bf16, h staged in LDS, g^T tiles as loaded;
+//              the row chunks of one token range share an XCD (and its L2);
 //   k_finalize fixed-order sums of all weight-gradient partials (dU, dw0, dM).
 #include "kernels.h"
+#include "bufio.h"
 #include "mfma.h"
 
 namespace dynconv {
 namespace gbwd {
 
-// g[t, n] for n < N (zero-padded to Np), bf16; four columns per thread.  The
-// slice partials are loaded 6 at a time ahead of the adds, which stay in
-// slice order (fixed-order sums).
+constexpr int kMaxSpan = 16;  // most slices one head's du may be split over
+
+// Block: TT = 2048 / CW tokens x CW columns (CW = 16, 32 or 64; column group
+// blockIdx.y), two quads of four columns per thread.  g = fixed-order sum of
+// the conv kernel's slice partials (low-rank: [slice][BT][R] rows of dz, all
+// slices; head-wise: a head's du lies in the one or few slices its channels
+// fall in, at a slot given by the head's place in the slice; that column ->
+// (slice, slot) table is built once per block in LDS).  The slice loop is
+// outermost so that both quads' loads are in flight together.  g [BT][Np] is
+// written straight from registers (row-major, for dh); the bf16 tile also
+// goes through LDS to write g^T [Np][BTp] (token-contiguous, zero for tokens
+// past BT), the operand layout of the dM kernel.  The LDS row pitch CW + 2
+// puts the eight tokens a column gather reads in distinct banks.
+template <int CW>
 __global__ void __launch_bounds__(256)
-k_combine(Shape s, const float *__restrict__ gpart, int n_slices, int R, int Dt, int Np,
-          bf16 *__restrict__ g) {
-  const int64_t idx = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
-  if (idx >= s.BT * Np) return;
-  const int64_t t = idx / Np;
-  const int n0 = (int)(idx - t * Np);  // Np is a multiple of 16: the four columns share a row
-  float v[4] = {0.f, 0.f, 0.f, 0.f};
-  if (s.kind == DYNCONV_LOWRANK) {
-    if (n0 + 4 <= s.N && R % 4 == 0) {
-      const float *src = gpart + t * R + n0;
-      const int64_t stride = s.BT * R;
+k_combine(Shape s, const float *__restrict__ gpart, int n_slices, int R, int Dt, int Np, int64_t BTp, int span,
+          bf16 *__restrict__ g, bf16 *__restrict__ gT) {
+  constexpr int TT = 2048 / CW, Q = CW / 4, P = CW + 2;
+  __shared__ __attribute__((aligned(16))) uint16_t ct[TT * P];
+  __shared__ int64_t tab[CW][kMaxSpan];  // head-wise: element offset of (slice, slot) in gpart, or -1
+  const int tid = threadIdx.x;
+  const int64_t t0 = (int64_t)blockIdx.x * TT;
+  const int c0 = blockIdx.y * CW;
+  const bool lowrank = s.kind == DYNCONV_LOWRANK;
+  if (!lowrank) {
+    for (int e = tid; e < CW * span; e += 256) {
+      const int nl = e / span, p = e - nl * span, n = c0 + nl;
+      int64_t off = -1;
+      if (n < s.N) {
+        const int eh = n / s.k, j = n - eh * s.k;  // head, tap
+        const int d0 = eh * s.hd / Dt, d1 = ((eh + 1) * s.hd - 1) / Dt, d = d0 + p;
+        if (d <= d1) off = (int64_t)d * s.BT * R + (eh - d * Dt / s.hd) * s.k + j;
+      }
+      tab[nl][p] = off;
+    }
+    __syncthreads();
+  }
+  float v[2][4];
+  int64_t tq[2];
+  int nq[2];
+#pragma unroll
+  for (int qi = 0; qi < 2; ++qi) {
+    const int e = tid + 256 * qi;
+    tq[qi] = t0 + e / Q;
+    nq[qi] = (e % Q) * 4;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v[qi][c] = 0.f;
+  }
+  if (lowrank) {
+    const int64_t stride = s.BT * R;
+    bool vec[2];
+    const float *src[2];
+#pragma unroll
+    for (int qi = 0; qi < 2; ++qi) {
+      const int n0 = c0 + nq[qi];
+      vec[qi] = tq[qi] < s.BT && n0 + 4 <= s.N && R % 4 == 0;
+      src[qi] = gpart + (tq[qi] < s.BT ? tq[qi] : 0) * R + n0;
+    }
+    if (vec[0] && vec[1]) {
       int d = 0;
-      for (; d + 6 <= n_slices; d += 6) {
-        float4 a[6];
+      for (; d + 4 <= n_slices; d += 4) {
+        float4 a[4][2];
 #pragma unroll
-        for (int u = 0; u < 6; ++u) a[u] = *reinterpret_cast<const float4 *>(src + (d + u) * stride);
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int u = 0; u < 6; ++u) v[0] += a[u].x, v[1] += a[u].y, v[2] += a[u].z, v[3] += a[u].w;
+          for (int qi = 0; qi < 2; ++qi) a[u][qi] = *reinterpret_cast<const float4 *>(src[qi] + (d + u) * stride);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int qi = 0; qi < 2; ++qi)
+            v[qi][0] += a[u][qi].x, v[qi][1] += a[u][qi].y, v[qi][2] += a[u][qi].z, v[qi][3] += a[u][qi].w;
       }
-      for (; d < n_slices; ++d) {
-        const float4 a = *reinterpret_cast<const float4 *>(src + d * stride);
-        v[0] += a.x, v[1] += a.y, v[2] += a.z, v[3] += a.w;
-      }
+      for (; d < n_slices; ++d)
+#pragma unroll
+        for (int qi = 0; qi < 2; ++qi) {
+          const float4 a = *reinterpret_cast<const float4 *>(src[qi] + d * stride);
+          v[qi][0] += a.x, v[qi][1] += a.y, v[qi][2] += a.z, v[qi][3] += a.w;
+        }
     } else {
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (n0 + c < s.N)
-          for (int d = 0; d < n_slices; ++d) v[c] += gpart[((int64_t)d * s.BT + t) * R + n0 + c];
+      for (int qi = 0; qi < 2; ++qi)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (tq[qi] < s.BT && c0 + nq[qi] + c < s.N)
+            for (int d = 0; d < n_slices; ++d) v[qi][c] += src[qi][d * stride + c];
     }
   } else {
+    for (int p = 0; p < span; ++p) {
+      float a[2][4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int n = n0 + c;
-      if (n >= s.N) continue;
-      const int e = n / s.k, j = n - e * s.k;
-      const int d0 = (int)((int64_t)e * s.hd / Dt), d1 = (int)(((int64_t)(e + 1) * s.hd - 1) / Dt);
-      for (int d = d0; d <= d1; ++d) {
-        const int slot = e - (int)((int64_t)d * Dt / s.hd);
-        v[c] += gpart[((int64_t)d * s.BT + t) * R + slot * s.k + j];
-      }
+      for (int qi = 0; qi < 2; ++qi)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int64_t off = tab[nq[qi] + c][p];
+          a[qi][c] = (off >= 0 && tq[qi] < s.BT) ? gpart[off + tq[qi] * R] : 0.f;
+        }
+#pragma unroll
+      for (int qi = 0; qi < 2; ++qi)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[qi][c] += a[qi][c];
     }
   }
-  uint2 o;
-  o.x = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)v[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)v[1]) << 16);
-  o.y = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)v[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)v[3]) << 16);
-  *reinterpret_cast<uint2 *>(g + idx) = o;
+#pragma unroll
+  for (int qi = 0; qi < 2; ++qi) {
+    const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)v[qi][0]) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)v[qi][1]) << 16);
+    const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)v[qi][2]) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)v[qi][3]) << 16);
+    const int n0 = c0 + nq[qi];
+    if (tq[qi] < s.BT && n0 < Np) *reinterpret_cast<uint2 *>(g + tq[qi] * Np + n0) = make_uint2(lo, hi);
+    uint32_t *w = reinterpret_cast<uint32_t *>(ct + (tq[qi] - t0) * P + nq[qi]);  // 4-byte aligned
+    w[0] = lo;
+    w[1] = hi;
+  }
+  __syncthreads();
+  {  // one 8-token piece of one column per thread
+    const int nl = tid / (TT / 8), tc = (tid % (TT / 8)) * 8;
+    const int n = c0 + nl;
+    if (n < Np && t0 + tc < BTp) {
+      uint32_t w[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        w[p] = (uint32_t)ct[(tc + 2 * p) * P + nl] | ((uint32_t)ct[(tc + 2 * p + 1) * P + nl] << 16);
+      *reinterpret_cast<uint4 *>(gT + (int64_t)n * BTp + t0 + tc) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
 }
 
 // Mp[i, n] = M[i, n] zero-padded to Np columns (bf16).
@@ -85,108 +163,235 @@ k_pad_cols(const bf16 *__restrict__ M, bf16 *__restrict__ Mp, int64_t rows, int 
   Mp[idx] = n < N ? M[i * N + n] : (bf16)0.f;
 }
 
-// dh^T[i, t] = sum_n Mp[i, n] g[t, n].  Block: 4 waves x 32 rows of d, one
-// 32-token tile.  Lane l holds rows 8b + 4(l/32) + r, token l%32.
+// Blocks of a grid of n_work items run round-robin over the 8 XCDs; item q =
+// xcd * slots + slot makes neighbouring items (the row blocks of one token
+// range) share an XCD and so its L2.
+__device__ __forceinline__ int xcd_item(int slots) {
+  return (int)(blockIdx.x & 7) * slots + (int)(blockIdx.x >> 3);
+}
+
+constexpr int kOP = 36;  // dh staging tile row (one token): 32 rows of d + pad, bf16
+
+// dh[t, i] = sum_n g[t, n] Mp[i, n], as dh^T tiles on v_mfma_f32_32x32x16_bf16
+// (A = 32 rows of Mp, B = 32 tokens of g).  Block: 8 waves x 32 rows of d
+// (256 rows) over a range of 32-token tiles.  A wave keeps its rows' weight
+// fragments in registers for the whole range.  The block stages each g tile
+// [32 tokens][Np] in LDS (double-buffered, one barrier per tile; loaded two
+// tiles ahead in two register sets), and a wave writes its dh tile through a
+// private LDS tile so that every store is a whole 64-byte row segment.
 template <int KS>
-__global__ void __launch_bounds__(256)
-k_dh(const bf16 *__restrict__ g, const bf16 *__restrict__ Mp, bf16 *__restrict__ dh, int64_t BT,
-     int d, int Np, int n_ib, int Mcols) {
-  // XCD-aware mapping: blocks go round-robin over 8 XCDs; keep a token tile's
-  // row blocks on one XCD.
-  const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
-  const int tile = (slot / n_ib) * 8 + xcd, ib = slot % n_ib;
-  const int64_t t0 = (int64_t)tile * 32;
-  if (t0 >= BT) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int hh = lane >> 5, tl = lane & 31;
-  const int i0 = ib * 128 + wave * 32;
-  if (i0 >= d) return;
-  const int64_t t = t0 + tl;
-  const int ia = min(i0 + tl, d - 1);
-  f32x16 acc = {};
+__global__ void __launch_bounds__(512)
+k_dh(const bf16 *__restrict__ g, const bf16 *__restrict__ Mp, bf16 *__restrict__ dh, int64_t BT, int d,
+     int Mcols, int n_rb, int n_tr, int tpr, int n_tiles, int slots) {
+  constexpr int NP = KS * 16;
+  constexpr int GP = NP + 8;            // LDS row of the g tile (one token), bf16
+  constexpr int CH = 4 * NP;            // 16-byte pieces of a g tile
+  constexpr int CPT = (CH + 511) / 512;  // per thread
+  constexpr int GR = (CPT * 512 + NP / 8 - 1) / (NP / 8);  // tile rows incl. spare ones for pieces past CH
+  __shared__ __attribute__((aligned(16))) bf16 gs[2][GR * GP];
+  __shared__ __attribute__((aligned(16))) bf16 ot[8][32 * kOP];
+  const int q = xcd_item(slots);
+  if (q >= n_rb * n_tr) return;
+  const int tr = q / n_rb, rb = q - tr * n_rb;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hh = lane >> 5, l32 = lane & 31;
+  const int i0 = rb * 256 + wave * 32;
+  const bool active = i0 < d;  // idle waves still load g tiles and meet the barriers, store nothing
+  const int tile_lo = tr * tpr, ntl = min(n_tiles, tile_lo + tpr) - tile_lo;
+  const int64_t tok_lo = (int64_t)tile_lo * 32;
+  const int64_t tok_n = min(BT, tok_lo + (int64_t)ntl * 32) - tok_lo;
+
+  bf16x8 mf[KS];
+  {
+    const int ia = min(i0 + l32, d - 1);
+    const __amdgpu_buffer_rsrc_t rm = make_rsrc(Mp, (uint32_t)((int64_t)d * Mcols * 2));
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const int n = ks * 16 + hh * 8;
-    // Mp has Mcols columns: Np (a padded copy) or N itself when N % 8 == 0, so
-    // that each 8-column chunk is all in or all out
-    const bf16x8 a = n < Mcols ? as_bf16x8(*reinterpret_cast<const uint4 *>(Mp + (int64_t)ia * Mcols + n))
-                               : zero_bf16x8();
-    const bf16x8 bb = t < BT ? as_bf16x8(*reinterpret_cast<const uint4 *>(g + t * Np + n)) : zero_bf16x8();
-    acc = mfma32(a, bb, acc);
+    for (int ks = 0; ks < KS; ++ks) {
+      const int n = ks * 16 + hh * 8;  // Mcols is Np or a multiple of 8: chunks are all in or all out
+      mf[ks] = as_bf16x8(buf_load16(rm, n < Mcols ? (uint32_t)((ia * Mcols + n) * 2) : kOutside));
+    }
   }
-  if (t >= BT) return;
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(g + tok_lo * NP, (uint32_t)(tok_n * NP * 2));
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(dh + tok_lo * d, (uint32_t)(tok_n * d * 2));
+  auto goff = [&](int tile, int c) -> uint32_t {
+    const int e = tid + 512 * c;
+    return (tile < ntl && (CH % 512 == 0 || e < CH))
+               ? (uint32_t)(((tile * 32 + e / (NP / 8)) * NP + (e % (NP / 8)) * 8) * 2)
+               : kOutside;
+  };
+  uint4 gr[2][CPT];
+  auto load = [&](int set, int tile) {
 #pragma unroll
-  for (int bq = 0; bq < 4; ++bq) {
-    const int i = i0 + 8 * bq + 4 * hh;
-    if (i >= d) continue;  // d is a multiple of 8, so i..i+3 are all in or all out
-    const bf16 v0 = (bf16)acc[4 * bq], v1 = (bf16)acc[4 * bq + 1], v2 = (bf16)acc[4 * bq + 2],
-               v3 = (bf16)acc[4 * bq + 3];
-    uint2 raw;
-    raw.x = (uint32_t)__builtin_bit_cast(uint16_t, v0) | ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
-    raw.y = (uint32_t)__builtin_bit_cast(uint16_t, v2) | ((uint32_t)__builtin_bit_cast(uint16_t, v3) << 16);
-    *reinterpret_cast<uint2 *>(dh + t * d + i) = raw;
+    for (int c = 0; c < CPT; ++c) gr[set][c] = buf_load16(rg, goff(tile, c));
+  };
+  bf16 *my = ot[wave];
+  const int tok_r = lane >> 2, c8 = (lane & 3) * 8;
+  const uint32_t col_ok = active && i0 + c8 < d;  // d is a multiple of 8
+  auto step = [&](int set, int tile) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {  // pieces past CH (zeros) land in the spare rows
+      const int e = tid + 512 * c;
+      *reinterpret_cast<uint4 *>(gs[set] + (e / (NP / 8)) * GP + (e % (NP / 8)) * 8) = gr[set][c];
+    }
+    __syncthreads();
+    load(set, tile + 2);
+    // computed on every path (an idle wave or a tile past the range stores
+    // nothing): the memory instruction count stays the same on all paths
+    f32x16 acc = {};
+    const bf16 *gb = gs[set] + l32 * GP + hh * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      acc = mfma32(mf[ks], as_bf16x8(*reinterpret_cast<const uint4 *>(gb + ks * 16)), acc);
+    // lane holds dh^T[8b + 4hh + r][l32], b, r = 0..3: four consecutive rows of one token
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)acc[4 * b]) |
+                          ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)acc[4 * b + 1]) << 16);
+      const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)acc[4 * b + 2]) |
+                          ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)acc[4 * b + 3]) << 16);
+      *reinterpret_cast<uint2 *>(my + l32 * kOP + 8 * b + 4 * hh) = make_uint2(lo, hi);
+    }
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int tok = tok_r + 16 * p;
+      const uint2 a = *reinterpret_cast<const uint2 *>(my + tok * kOP + c8);
+      const uint2 bq = *reinterpret_cast<const uint2 *>(my + tok * kOP + c8 + 4);
+      const uint32_t off =
+          col_ok && tile < ntl ? (uint32_t)((((int64_t)tile * 32 + tok) * d + i0 + c8) * 2) : kOutside;
+      buf_store16(rd, off, make_uint4(a.x, a.y, bq.x, bq.y));
+    }
+  };
+  // The loop issues, per tile, the loads two tiles ahead and then two stores.
+  // The prologue keeps that order (with stores that fall outside dh and are
+  // dropped), so the compiler's wait counts at the loop head are the steady
+  // state ones and the second prefetch set stays in flight.
+  load(0, 0);
+  buf_store16(rd, kOutside, make_uint4(0, 0, 0, 0));
+  buf_store16(rd, kOutside, make_uint4(0, 0, 0, 0));
+  load(1, 1);
+  buf_store16(rd, kOutside, make_uint4(0, 0, 0, 0));
+  buf_store16(rd, kOutside, make_uint4(0, 0, 0, 0));
+  for (int tile = 0; tile < ntl; tile += 2) {
+    step(0, tile);
+    step(1, tile + 1);
   }
 }
 
-constexpr int kRowB = 80;  // 32 tokens of bf16, padded
+constexpr int kHP = 132;  // dM h tile row (one token): 128 rows of d + pad, bf16
+constexpr int kGP = 40;   // dM g^T tile row (one column): 32 tokens + pad, bf16
 
-// dMp[range][i, n] = sum over the range's tokens of h[t, i] g[t, n].
-// Block: 64 rows of d (wave w: rows 16w..16w+15) x all Np columns.
-template <int NB>
-__global__ void __launch_bounds__(256)
-k_dM(const bf16 *__restrict__ h, const bf16 *__restrict__ g, float *__restrict__ dMp, int64_t BT,
-     int d, int N, int Np, int tpb, int n_tiles) {
-  __shared__ __attribute__((aligned(16))) unsigned char ht[64 * kRowB];
-  __shared__ __attribute__((aligned(16))) unsigned char gtt[NB * 16 * kRowB];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int i0 = blockIdx.x * 64;
-  const int tile_lo = blockIdx.y * tpb, tile_hi = min(n_tiles, tile_lo + tpb);
-  f32x4 acc[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+// dMp[range][i, n] = sum over the range's tokens of h[t, i] g[t, n], on
+// v_mfma_f32_16x16x32_bf16 with A = h^T (rows of d x tokens) and B = g (tokens
+// x columns).  Block: 128 rows of d (wave w: rows 32w..32w+31) x all Np
+// columns over a range of 32-token tiles.  Per tile the block stages h
+// row-major in LDS (the A fragments are then gathered 16 bits at a time; the
+// 264-byte row pitch spreads the four token groups of a gather over distinct
+// banks) and the g^T tile (16-byte B fragments), double-buffered with one
+// barrier per tile.  h is loaded two tiles ahead in two register sets, g^T one tile
+// ahead; loads are issued g^T first so that waiting for a tile's g^T leaves
+// the later h tile in flight.  Tiles past the range read as zeros.
+template <int NT>
+__global__ void __launch_bounds__(256, 2)
+k_dM(const bf16 *__restrict__ h, const bf16 *__restrict__ gT, float *__restrict__ dMp, int64_t BT, int64_t BTp,
+     int d, int N, int n_chunks, int n_ranges, int tpb, int n_tiles, int slots) {
+  constexpr int CH = NT * 64;            // 16-byte chunks of a g^T tile
+  constexpr int CPT = (CH + 255) / 256;  // per thread
+  constexpr int GR = CPT * 64;           // g^T tile rows incl. spare ones for the pieces past CH
+  __shared__ __attribute__((aligned(16))) bf16 hs[2][32 * kHP];
+  __shared__ __attribute__((aligned(16))) bf16 gs[2][GR * kGP];
+  const int q = xcd_item(slots);
+  if (q >= n_chunks * n_ranges) return;
+  const int range = q / n_chunks, chunk = q - range * n_chunks;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i0 = chunk * 128;
+  const int tile_lo = range * tpb, ntl = min(n_tiles, tile_lo + tpb) - tile_lo;
+  const int64_t tok_lo = (int64_t)tile_lo * 32;
+  const int64_t tok_n = min(BT, tok_lo + (int64_t)ntl * 32) - tok_lo;
+  const __amdgpu_buffer_rsrc_t rh = make_rsrc(h + tok_lo * d, (uint32_t)(tok_n * d * 2));
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(gT + tok_lo, (uint32_t)(((int64_t)NT * 16 * BTp - tok_lo) * 2));
 
-  for (int tile = tile_lo; tile < tile_hi; ++tile) {
-    const int64_t t0 = (int64_t)tile * 32;
+  // this thread's pieces: h chunk c -> token tid/16 + 16c, rows i0 + 8(tid%16)
+  const int h_tok = tid >> 4, h_col = (tid & 15) * 8;
+  const bool h_in = i0 + h_col < d;  // d is a multiple of 8
+  auto hoff = [&](int tile, int c) -> uint32_t {
+    return (tile < ntl && h_in) ? (uint32_t)(((tile * 32 + h_tok + 16 * c) * d + i0 + h_col) * 2) : kOutside;
+  };
+  auto goff = [&](int tile, int c) -> uint32_t {
+    const int e = tid + 256 * c;
+    return (tile < ntl && (CH % 256 == 0 || e < CH)) ? (uint32_t)((((int64_t)(e >> 2)) * BTp + tile * 32 + (e & 3) * 8) * 2)
+                                  : kOutside;
+  };
+
+  f32x4 acc[2][NT];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[r][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  uint4 hr[2][2], gr[CPT];
+  auto load_g = [&](int tile) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) gr[c] = buf_load16(rg, goff(tile, c));
+  };
+  auto load_h = [&](int set, int tile) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) hr[set][c] = buf_load16(rh, hoff(tile, c));
+  };
+  const uint16_t *hsu = reinterpret_cast<const uint16_t *>(&hs[0][0]);
+  auto step = [&](int set, int tile) {
+    bf16 *hb = hs[set];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {  // rows of 264 bytes: two 8-byte writes per piece
+      uint2 *dst = reinterpret_cast<uint2 *>(hb + (h_tok + 16 * c) * kHP + h_col);
+      dst[0] = make_uint2(hr[set][c].x, hr[set][c].y);
+      dst[1] = make_uint2(hr[set][c].z, hr[set][c].w);
+    }
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {  // pieces past CH (zeros) land in the spare rows
+      const int e = tid + 256 * c;
+      *reinterpret_cast<uint4 *>(gs[set] + (e >> 2) * kGP + (e & 3) * 8) = gr[c];
+    }
     __syncthreads();
-    // h tile transposed: thread -> (token tt, 8 consecutive rows i)
-    {
-      const int tt = threadIdx.x >> 3, c8 = (threadIdx.x & 7) * 8;
-      const int64_t row = t0 + tt;
-      uint4 raw = make_uint4(0, 0, 0, 0);
-      if (row < BT && i0 + c8 < d) raw = *reinterpret_cast<const uint4 *>(h + row * d + i0 + c8);
-      const uint16_t *hv = reinterpret_cast<const uint16_t *>(&raw);
+    load_g(tile + 1);
+    load_h(set, tile + 2);
+    // A fragment r: rows 32w + 16r + lane%16, tokens 8(lane/16) .. +7
+    const uint16_t *ha = hsu + set * 32 * kHP + 8 * (lane >> 4) * kHP + 32 * wave + (lane & 15);
+    bf16x8 a[2];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) *reinterpret_cast<uint16_t *>(ht + (c8 + e) * kRowB + tt * 2) = hv[e];
-    }
-    // g tile transposed: thread -> (token, 8 consecutive columns)
-    for (int e = threadIdx.x; e < 32 * (Np / 8); e += 256) {
-      const int tt = e / (Np / 8), n8 = (e - tt * (Np / 8)) * 8;
-      const int64_t row = t0 + tt;
-      uint4 raw = make_uint4(0, 0, 0, 0);
-      if (row < BT) raw = *reinterpret_cast<const uint4 *>(g + row * Np + n8);
-      const uint16_t *gv = reinterpret_cast<const uint16_t *>(&raw);
+    for (int r = 0; r < 2; ++r) {
+      uint32_t w[4];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) *reinterpret_cast<uint16_t *>(gtt + (n8 + q) * kRowB + tt * 2) = gv[q];
+      for (int p = 0; p < 4; ++p)
+        w[p] = (uint32_t)ha[2 * p * kHP + 16 * r] | ((uint32_t)ha[(2 * p + 1) * kHP + 16 * r] << 16);
+      a[r] = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
     }
-    __syncthreads();
-    const bf16x8 a = as_bf16x8(
-        *reinterpret_cast<const uint4 *>(ht + (wave * 16 + (lane & 15)) * kRowB + (lane >> 4) * 16));
+    const bf16 *gb = gs[set] + (lane & 15) * kGP + 8 * (lane >> 4);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const bf16x8 b = as_bf16x8(
-          *reinterpret_cast<const uint4 *>(gtt + (nb * 16 + (lane & 15)) * kRowB + (lane >> 4) * 16));
-      acc[nb] = mfma16(a, b, acc[nb]);
+    for (int n = 0; n < NT; ++n) {
+      const bf16x8 b = as_bf16x8(*reinterpret_cast<const uint4 *>(gb + n * 16 * kGP));
+      acc[0][n] = mfma16(a[0], b, acc[0][n]);
+      acc[1][n] = mfma16(a[1], b, acc[1][n]);
     }
+  };
+  load_g(0);
+  load_h(0, 0);
+  load_h(1, 1);
+  for (int tile = 0; tile < ntl; tile += 2) {
+    step(0, tile);
+    step(1, tile + 1);
   }
-  // D fragment: lane holds D[4(l/16) + r][l%16] of each 16x16 block
+  // D fragment: lane holds D[4(lane/16) + r][lane%16] of each 16x16 block
+  float *out = dMp + (int64_t)range * d * N;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
+  for (int r = 0; r < 2; ++r)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = i0 + wave * 16 + (lane >> 4) * 4 + r;
-      const int n = nb * 16 + (lane & 15);
-      if (i < d && n < N) dMp[((int64_t)blockIdx.y * d + i) * N + n] = acc[nb][r];
-    }
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int i = i0 + 32 * wave + 16 * r + 4 * (lane >> 4) + k;
+        const int col = n * 16 + (lane & 15);
+        if (i < d && col < N) out[(int64_t)i * N + col] = acc[r][n][k];
+      }
 }
 
 // out[e] = sum_p part[p][e] for e < n, p < np (fixed order), for up to three
@@ -242,19 +447,56 @@ __global__ void __launch_bounds__(256) k_finalize(Red r0, Red r1, Red r2) {
 
 }  // namespace gbwd
 
+// Head-wise: the most conv-kernel slices (Dt channels each) one head's
+// channels fall in.
+static int combine_span(const Shape &s, int Dt) {
+  int span = 1;
+  for (int e = 0; e < s.n_heads; ++e) {
+    const int64_t d0 = (int64_t)e * s.hd / Dt, d1 = ((int64_t)(e + 1) * s.hd - 1) / Dt;
+    span = std::max<int>(span, (int)(d1 - d0 + 1));
+  }
+  return span;
+}
+
 GenBwdLayout gen_bwd_layout(const Shape &s) {
   GenBwdLayout L;
   L.Np = (int)ceil_div(s.N, 16) * 16;
   L.n_tiles = (int)ceil_div(s.BT, 32);
-  L.n_chunks = (int)ceil_div(s.d, 64);
-  int tpb = 1;
-  while ((int64_t)L.n_chunks * ceil_div(L.n_tiles, tpb) > 512) ++tpb;
+  L.BTp = (int64_t)L.n_tiles * 32;
+  L.n_chunks = (int)ceil_div(s.d, 128);
+  // about two blocks per CU; an even tile count per range (the dM loop takes
+  // tiles in pairs); a range's slice of h stays below 1 GiB (32-bit offsets)
+  int tpb = (int)ceil_div(L.n_tiles, std::max<int64_t>(1, 512 / L.n_chunks));
+  tpb += tpb & 1;
+  while ((int64_t)tpb * 32 * s.d * 2 >= ((int64_t)1 << 30) && tpb > 2) tpb -= 2;
   L.tpb = tpb;
   L.n_ranges = (int)ceil_div(L.n_tiles, tpb);
+  L.n_rb = (int)ceil_div(s.d, 256);
+  int tpr = (int)ceil_div(L.n_tiles, std::max<int64_t>(1, 512 / L.n_rb));
+  tpr += tpr & 1;
+  while ((int64_t)tpr * 32 * std::max<int64_t>(s.d, L.Np) * 2 >= ((int64_t)1 << 30) && tpr > 2) tpr -= 2;
+  L.tpr = tpr;
+  L.n_tr = (int)ceil_div(L.n_tiles, tpr);
   return L;
 }
 
-size_t gen_bwd_g_bytes(const Shape &s) { return (size_t)s.BT * gen_bwd_layout(s).Np * sizeof(bf16); }
+bool gen_bwd_supported(const Shape &s) {
+  // g and g^T are addressed with 32-bit byte offsets; head-wise column ->
+  // slice tables hold at most kMaxSpan slices per head
+  const GenBwdLayout L = gen_bwd_layout(s);
+  if (s.kind == DYNCONV_HEADWISE && combine_span(s, bwd_layout(s).Dt) > gbwd::kMaxSpan) return false;
+  return L.Np <= 256 && (int64_t)L.Np * L.BTp * 2 < ((int64_t)1 << 31) - 64;
+}
+
+// g [BT, Np] then g^T [Np, BTp], the latter on a 256-byte boundary
+static size_t g_rows_bytes(const Shape &s, const GenBwdLayout &L) {
+  return ((size_t)s.BT * L.Np * sizeof(bf16) + 255) / 256 * 256;
+}
+
+size_t gen_bwd_g_bytes(const Shape &s) {
+  const GenBwdLayout L = gen_bwd_layout(s);
+  return g_rows_bytes(s, L) + (size_t)L.Np * L.BTp * sizeof(bf16);
+}
 size_t gen_bwd_mp_bytes(const Shape &s) { return (size_t)s.d * gen_bwd_layout(s).Np * sizeof(bf16); }
 size_t gen_bwd_part_bytes(const Shape &s) {
   return (size_t)gen_bwd_layout(s).n_ranges * s.d * s.N * sizeof(float);
@@ -263,8 +505,23 @@ size_t gen_bwd_part_bytes(const Shape &s) {
 int gen_bwd(const Shape &s, const float *gpart, int n_slices, int R, int Dt, const void *h,
             const void *M, bf16 *g, bf16 *Mp, void *dh, float *dMp, hipStream_t st) {
   const GenBwdLayout L = gen_bwd_layout(s);
-  hipLaunchKernelGGL(gbwd::k_combine, dim3((unsigned)ceil_div(s.BT * L.Np / 4, 256)), dim3(256), 0, st, s,
-                     gpart, n_slices, R, Dt, L.Np, g);
+  bf16 *gT = (bf16 *)((char *)g + g_rows_bytes(s, L));
+  const int span = s.kind == DYNCONV_HEADWISE ? combine_span(s, Dt) : 0;
+  if (span > gbwd::kMaxSpan) return DYNCONV_E_LIMIT;
+  if (L.Np <= 32) {
+    const int cw = L.Np;  // 16 or 32
+    const dim3 grid((unsigned)ceil_div(L.BTp, 2048 / cw));
+    if (cw == 16)
+      hipLaunchKernelGGL(gbwd::k_combine<16>, grid, dim3(256), 0, st, s, gpart, n_slices, R, Dt, L.Np, L.BTp,
+                         span, g, gT);
+    else
+      hipLaunchKernelGGL(gbwd::k_combine<32>, grid, dim3(256), 0, st, s, gpart, n_slices, R, Dt, L.Np, L.BTp,
+                         span, g, gT);
+  } else {
+    const dim3 grid((unsigned)ceil_div(L.BTp, 32), (unsigned)ceil_div(L.Np, 64));
+    hipLaunchKernelGGL(gbwd::k_combine<64>, grid, dim3(256), 0, st, s, gpart, n_slices, R, Dt, L.Np, L.BTp, span,
+                       g, gT);
+  }
   const bool tr = trace_begin(DYNCONV_K_GEN_BWD, st);
   if (dh) {
     // the weight is read in place when its rows are whole 8-column chunks
@@ -274,14 +531,12 @@ int gen_bwd(const Shape &s, const float *gpart, int n_slices, int R, int Dt, con
                          (const bf16 *)M, Mp, s.d, s.N, L.Np);
     const bf16 *Ma = direct ? (const bf16 *)M : Mp;
     const int Mcols = direct ? s.N : L.Np;
-    const int n_ib = (int)ceil_div(s.d, 128);
-    const int tiles8 = (int)ceil_div(L.n_tiles, 8) * 8;
-    const unsigned nblk = (unsigned)(tiles8 * n_ib);
+    const int slots = (int)ceil_div((int64_t)L.n_rb * L.n_tr, 8);
     switch (L.Np / 16) {
-#define CASE(ks)                                                                                      \
-  case ks:                                                                                            \
-    hipLaunchKernelGGL(gbwd::k_dh<ks>, dim3(nblk), dim3(256), 0, st, g, Ma, (bf16 *)dh, s.BT, (int)s.d, \
-                       L.Np, n_ib, Mcols);                                                            \
+#define CASE(ks)                                                                                        \
+  case ks:                                                                                              \
+    hipLaunchKernelGGL(gbwd::k_dh<ks>, dim3((unsigned)(8 * slots)), dim3(512), 0, st, g, Ma, (bf16 *)dh, \
+                       s.BT, (int)s.d, Mcols, L.n_rb, L.n_tr, L.tpr, L.n_tiles, slots);                 \
     break;
       CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)
       CASE(9) CASE(10) CASE(11) CASE(12) CASE(13) CASE(14) CASE(15) CASE(16)
@@ -289,12 +544,13 @@ int gen_bwd(const Shape &s, const float *gpart, int n_slices, int R, int Dt, con
       default: trace_end(tr, st); return DYNCONV_E_LIMIT;
     }
   }
-  dim3 grid((unsigned)L.n_chunks, (unsigned)L.n_ranges);
+  const int slots = (int)ceil_div((int64_t)L.n_chunks * L.n_ranges, 8);
   switch (L.Np / 16) {
-#define CASE(nb)                                                                                  \
-  case nb:                                                                                        \
-    hipLaunchKernelGGL(gbwd::k_dM<nb>, grid, dim3(256), 0, st, (const bf16 *)h, g, dMp, s.BT,     \
-                       (int)s.d, s.N, L.Np, L.tpb, L.n_tiles);                                    \
+#define CASE(nb)                                                                                      \
+  case nb:                                                                                            \
+    hipLaunchKernelGGL(gbwd::k_dM<nb>, dim3((unsigned)(8 * slots)), dim3(256), 0, st, (const bf16 *)h, \
+                       gT, dMp, s.BT, L.BTp, (int)s.d, s.N, L.n_chunks, L.n_ranges, L.tpb, L.n_tiles, \
+                       slots);                                                                        \
     break;
     CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)
     CASE(9) CASE(10) CASE(11) CASE(12) CASE(13) CASE(14) CASE(15) CASE(16)

@@ -69,11 +69,16 @@ int bwd_lowrank(const Shape &s, const BwdLayout &L, const float *z, const void *
 struct GenBwdLayout {
   int Np;        // N padded to 16
   int n_tiles;   // 32-token tiles
-  int n_chunks;  // 64-row chunks of d_model
-  int tpb;       // tiles per block of the dM kernel
+  int64_t BTp;   // tokens padded to whole tiles (row length of g^T)
+  int n_chunks;  // 128-row chunks of d_model (dM)
+  int tpb;       // tiles per block of the dM kernel (even)
   int n_ranges;  // token ranges of the dM kernel (partials)
+  int n_rb;      // 256-row blocks of d_model (dh)
+  int tpr;       // tiles per token range of the dh kernel (even)
+  int n_tr;      // token ranges of the dh kernel
 };
 GenBwdLayout gen_bwd_layout(const Shape &s);
+bool gen_bwd_supported(const Shape &s);
 size_t gen_bwd_g_bytes(const Shape &s);
 size_t gen_bwd_mp_bytes(const Shape &s);
 size_t gen_bwd_part_bytes(const Shape &s);
