@@ -26,6 +26,7 @@
 // written as 16-byte stores.  HBM roofline: per token 2*D*2 bytes of x and y
 // plus 4*r bytes of z.
 #include "kernels.h"
+#include "bufio.h"
 #include "mfma.h"
 
 namespace dynconv {
@@ -35,29 +36,34 @@ constexpr int kCPW = 2;               // 16-channel groups per wave
 constexpr int kDt = 4 * kCPW * 16;    // channels per block (4 waves)
 constexpr int kRowB = kDt * 2 + 16;   // LDS row stride of the x tile (bytes, padded)
 
+// Loads and stores are raw buffer accesses issued on every path (a masked
+// slot gets an offset outside the buffer: zeros in, nothing out), so the
+// compiler's wait counts stay exact: tile i+2 is in flight while tile i is
+// computed (two register sets, tiles taken in pairs).
 template <int K, int KQ>
 __global__ void __launch_bounds__(256)
 k_fwd_lowrank(Shape s, const float *__restrict__ z, const bf16 *__restrict__ U, const bf16 *__restrict__ w0,
               const bf16 *__restrict__ x, bf16 *__restrict__ y, int tpb, int n_tiles) {
-  constexpr int KP = 4;
   constexpr int KH = K - 1;             // history rows
   constexpr int ZW = KQ * 16, ZWP = ZW + 8;
   constexpr int CH = kDt / 8;           // 16-byte chunks per row
   constexpr int kVLoads = ((32 + KH) * CH + 255) / 256;
+  constexpr int kXRows = kVLoads * 256 / CH;  // x tile rows incl. spare ones for unused load slots
   constexpr int kSLoads = (32 * ZW + 255) / 256;
-  __shared__ __attribute__((aligned(16))) unsigned char xs[2][(32 + KH) * kRowB];
-  __shared__ __attribute__((aligned(16))) bf16 zs[2][32 * ZWP];
+  __shared__ __attribute__((aligned(16))) unsigned char xs[2][kXRows * kRowB];
+  __shared__ __attribute__((aligned(16))) bf16 zs[2][32 * ZWP + 8];  // + a spare slot for unused z loads
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, tl = lane & 31;
-  const int64_t cblk = (int64_t)blockIdx.x * kDt;
-  const int nch = (int)min<int64_t>(kDt, s.D - cblk);
+  const int cblk = blockIdx.x * kDt;
+  const int D = (int)s.D, BT = (int)s.BT, rank = s.rank;  // BT*D and BT*rank*2 < 2^30 (host-checked)
+  const int nch = min(kDt, D - cblk);
   const int tile_lo = blockIdx.y * tpb, tile_hi = min(n_tiles, tile_lo + tpb);
 
   // bias / padding columns of the z tile (constant): 1 at q = r, 0 beyond
-  for (int e = threadIdx.x; e < 2 * 32 * ZWP; e += 256) {
-    const int q = e % ZWP;
-    if (q >= s.rank) (&zs[0][0])[e] = (bf16)(q == s.rank ? 1.f : 0.f);
+  for (int e = tid; e < 2 * (32 * ZWP + 8); e += 256) {
+    const int q = (e % (32 * ZWP + 8)) % ZWP;
+    if (q >= rank) (&zs[0][0])[e] = (bf16)(q == rank ? 1.f : 0.f);
   }
 
   // A fragments for this wave's groups [g][p][kq], gathered by each lane from
@@ -66,102 +72,106 @@ k_fwd_lowrank(Shape s, const float *__restrict__ z, const bf16 *__restrict__ U, 
   // zero beyond (and for taps >= k)
   bf16x8 af[kCPW][2][KQ];
   bool glive[kCPW];
-#pragma unroll
-  for (int g = 0; g < kCPW; ++g) {
-    const int64_t gg = (cblk >> 4) + wave * kCPW + g;
-    glive[g] = (wave * kCPW + g) * 16 < nch;
+  {
+    const auto ru = make_rsrc(U, (uint32_t)((int64_t)rank * D * K * 2));
+    const auto rw = make_rsrc(w0, w0 ? (uint32_t)(D * K * 2) : 0u);  // no bias: every load reads 0
     const int j = tl % 4;
+    const int kqb = rank / 16, ib = rank % 8, hb = (rank / 8) % 2;  // where q = rank sits
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int64_t c = 16 * gg + 8 * ((tl / 4) % 2) + 4 * p + tl / 8;
+    for (int g = 0; g < kCPW; ++g) {
+      const int gl = wave * kCPW + g;
+      glive[g] = gl * 16 < nch;
 #pragma unroll
-      for (int kq = 0; kq < KQ; ++kq) {
-        float v[8];
+      for (int p = 0; p < 2; ++p) {
+        const int c = cblk + 16 * gl + 8 * ((tl / 4) % 2) + 4 * p + tl / 8;
+        const bool ok = glive[g] && j < K;
+        const float bias =
+            bf16_bits_to_float(__builtin_amdgcn_raw_buffer_load_b16(rw, ok && hh == hb ? (uint32_t)((c * K + j) * 2) : kOutside, 0, 0));
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int q = 16 * kq + 8 * hh + i;
-          float u = 0.f;
-          if (glive[g] && j < K) {
-            if (q < s.rank) u = (float)U[(int64_t)q * s.D * K + c * K + j];
-            else if (q == s.rank && w0) u = (float)w0[c * K + j];
+        for (int kq = 0; kq < KQ; ++kq) {
+          float v[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int q = 16 * kq + 8 * hh + i;
+            const uint32_t off = ok && q < rank ? (uint32_t)((q * D * K + c * K + j) * 2) : kOutside;
+            v[i] = bf16_bits_to_float(__builtin_amdgcn_raw_buffer_load_b16(ru, off, 0, 0)) +
+                   (kq == kqb && i == ib ? bias : 0.f);
           }
-          v[i] = u;
+          af[g][p][kq] = pack_bf16x8(v);
         }
-        af[g][p][kq] = pack_bf16x8(v);
       }
     }
   }
 
-  // per-thread load slots
+  // per-thread load slots (fixed for the block)
   int v_row[kVLoads], v_col[kVLoads], v_loff[kVLoads];
   bool v_ok[kVLoads];
 #pragma unroll
   for (int q = 0; q < kVLoads; ++q) {
-    const int e = threadIdx.x + q * 256;
+    const int e = tid + q * 256;
     const int r = e / CH, c16 = e % CH;
     v_ok[q] = r < 32 + KH && c16 * 8 < nch;
     v_row[q] = r - KH;
-    v_col[q] = c16 * 8;
+    v_col[q] = cblk + c16 * 8;
     v_loff[q] = r * kRowB + c16 * 16;
   }
-  int s_tt[kSLoads], s_q[kSLoads];
+  int s_tt[kSLoads], s_q[kSLoads], s_loff[kSLoads];
   bool s_ok[kSLoads];
 #pragma unroll
   for (int q = 0; q < kSLoads; ++q) {
-    const int e = threadIdx.x + q * 256;
+    const int e = tid + q * 256;
     s_tt[q] = e / ZW;
     s_q[q] = e % ZW;
-    s_ok[q] = s_tt[q] < 32 && s_q[q] < s.rank;
+    s_ok[q] = s_tt[q] < 32 && s_q[q] < rank;
+    s_loff[q] = s_ok[q] ? s_tt[q] * ZWP + s_q[q] : 32 * ZWP;  // unused slots write the spare element
   }
-  uint4 vpre[kVLoads];
-  float spre[kSLoads];
-  auto prefetch = [&](int tile) {
-    const int64_t t0 = (int64_t)tile * 32;
+  const auto rx = make_rsrc(x, (uint32_t)(BT * D * 2));
+  const auto rz = make_rsrc(z, (uint32_t)(BT * rank * 4));
+  const auto ry = make_rsrc(y, (uint32_t)(BT * D * 2));
+  uint4 vpre[2][kVLoads];
+  float spre[2][kSLoads];
+  auto prefetch = [&](int set, int tile) {
+    const int t0 = tile * 32;
+    const bool tin = tile < tile_hi;
 #pragma unroll
     for (int q = 0; q < kVLoads; ++q) {
-      const int64_t row = t0 + v_row[q];
-      vpre[q] = make_uint4(0, 0, 0, 0);
-      if (v_ok[q] && row >= 0 && row < s.BT)
-        vpre[q] = *reinterpret_cast<const uint4 *>(x + row * s.D + cblk + v_col[q]);
+      const int row = t0 + v_row[q];
+      const uint32_t off = (tin && v_ok[q] && row >= 0 && row < BT) ? (uint32_t)(row * D + v_col[q]) * 2u : kOutside;
+      vpre[set][q] = buf_load16(rx, off);
     }
 #pragma unroll
     for (int q = 0; q < kSLoads; ++q) {
-      const int64_t row = t0 + s_tt[q];
-      spre[q] = (s_ok[q] && row < s.BT) ? z[row * s.rank + s_q[q]] : 0.f;
+      const int row = t0 + s_tt[q];
+      const uint32_t off = (tin && s_ok[q] && row < BT) ? (uint32_t)(row * rank + s_q[q]) * 4u : kOutside;
+      spre[set][q] = buf_load_f32(rz, off);
     }
   };
 
-  if (tile_hi > tile_lo) prefetch(tile_lo);
-  int buf = 0;
-  for (int tile = tile_lo; tile < tile_hi; ++tile, buf ^= 1) {
-    // ---- stage this tile, then start loading the next ----
+  auto step = [&](const int set, const int tile) {
+    // ---- stage this tile, then start loading the one two ahead ----
 #pragma unroll
-    for (int q = 0; q < kVLoads; ++q)
-      if (v_ok[q]) *reinterpret_cast<uint4 *>(xs[buf] + v_loff[q]) = vpre[q];
+    for (int q = 0; q < kVLoads; ++q) *reinterpret_cast<uint4 *>(xs[set] + v_loff[q]) = vpre[set][q];
 #pragma unroll
-    for (int q = 0; q < kSLoads; ++q)
-      if (s_ok[q]) zs[buf][s_tt[q] * ZWP + s_q[q]] = (bf16)spre[q];
+    for (int q = 0; q < kSLoads; ++q) zs[set][s_loff[q]] = (bf16)spre[set][q];
     __syncthreads();
-    if (tile + 1 < tile_hi) prefetch(tile + 1);
+    prefetch(set, tile + 2);
 
-    const int64_t t = (int64_t)tile * 32 + tl;
-    const bool tv = t < s.BT;
+    const int t = tile * 32 + tl;
+    const bool tv = tile < tile_hi && t < BT;
     const int pos = (int)((uint32_t)t % (uint32_t)s.T);
-    const bool edge = __any(KH > 0 && pos < KH);
     bf16x8 bz[KQ];
 #pragma unroll
     for (int kq = 0; kq < KQ; ++kq)
-      bz[kq] = as_bf16x8(*reinterpret_cast<const uint4 *>(&zs[buf][tl * ZWP + kq * 16 + hh * 8]));
+      bz[kq] = as_bf16x8(*reinterpret_cast<const uint4 *>(&zs[set][tl * ZWP + kq * 16 + hh * 8]));
 
 #pragma unroll
     for (int g = 0; g < kCPW; ++g) {
-      if (!glive[g]) continue;
       const int cl = (wave * kCPW + g) * 16 + hh * 8;  // block-local first channel of the lane's 8
       float xv[K][8];
 #pragma unroll
       for (int j = 0; j < K; ++j) {
-        uint4 raw = *reinterpret_cast<const uint4 *>(xs[buf] + (tl + KH - j) * kRowB + cl * 2);
-        if (edge && j > pos) raw = make_uint4(0, 0, 0, 0);
+        uint4 raw = *reinterpret_cast<const uint4 *>(xs[set] + (tl + KH - j) * kRowB + cl * 2);
+        if (j > pos) raw = make_uint4(0, 0, 0, 0);  // x[t-j] belongs to the previous sequence
         const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -183,15 +193,32 @@ k_fwd_lowrank(Shape s, const float *__restrict__ z, const bf16 *__restrict__ U, 
 #pragma unroll
           for (int j = 0; j < K; ++j) out[4 * p + b4] = fmaf(acc[4 * b4 + j], xv[j][4 * p + b4], out[4 * p + b4]);
       }
-      if (tv) store_vec(y + t * s.D + cblk + cl, out);
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[i] = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)out[2 * i]) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)out[2 * i + 1]) << 16);
+      const uint32_t off = (tv && glive[g]) ? (uint32_t)(t * D + cblk + cl) * 2u : kOutside;
+      buf_store16(ry, off, make_uint4(w[0], w[1], w[2], w[3]));
     }
+  };
+
+  prefetch(0, tile_lo);
+  prefetch(1, tile_lo + 1);
+  for (int tile = tile_lo; tile < tile_hi; tile += 2) {
+    step(0, tile);
+    step(1, tile + 1);
   }
-  (void)KP;
 }
 
 }  // namespace lowrank
 
-bool fwd_lowrank_supported(const Shape &s) { return s.D % 16 == 0 && s.rank + 1 <= 64 && s.k <= 4; }
+bool fwd_lowrank_supported(const Shape &s) {
+  // 32-bit element and byte offsets into x, y and z
+  const int64_t lim = ((int64_t)1 << 31) - 64;
+  return s.D % 16 == 0 && s.rank + 1 <= 64 && s.k <= 4 && s.BT * s.D * 2 < lim && s.BT * s.rank * 4 < lim &&
+         (int64_t)s.rank * s.D * s.k * 2 < lim;
+}
 
 int fwd_lowrank(const Shape &s, const float *z, const void *U, const void *w0, const void *x, void *y,
                 hipStream_t st) {
@@ -199,9 +226,9 @@ int fwd_lowrank(const Shape &s, const float *z, const void *U, const void *w0, c
   const int KQ = (int)ceil_div(s.rank + 1, 16);
   const int n_slices = (int)ceil_div(s.D, kDt);
   const int n_tiles = (int)ceil_div(s.BT, 32);
-  // enough blocks for ~4 per CU, each walking a run of tiles
-  int tpb = 1;
-  while ((int64_t)n_slices * ceil_div(n_tiles, tpb) > 1024) ++tpb;
+  // about two blocks per CU, each walking an even run of tiles
+  int tpb = 2;
+  while ((int64_t)n_slices * ceil_div(n_tiles, tpb) > 512) tpb += 2;
   dim3 grid((unsigned)n_slices, (unsigned)ceil_div(n_tiles, tpb));
   const bool tr = trace_begin(DYNCONV_K_FWD_CONV, st);
   int rc = 0;

@@ -32,6 +32,9 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4 &r) { return __builtin_b
 __device__ __forceinline__ bf16x8 zero_bf16x8() { return as_bf16x8(make_uint4(0, 0, 0, 0)); }
 
 // Round 8 fp32 values to bf16 (nearest even) as an MFMA operand.
+// the fp32 value of a bf16 bit pattern
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits) { return __uint_as_float(bits << 16); }
+
 __device__ __forceinline__ bf16x8 pack_bf16x8(const float (&v)[8]) {
   bf16x8 r;
 #pragma unroll
