@@ -17,9 +17,152 @@
 // The HBM roofline bounds it: per token it moves 2*D*eb bytes of x and y plus
 // the n_heads*k*4 bytes of u (a broadcast read, cached).
 #include "kernels.h"
+#include "bufio.h"
 
 namespace dynconv {
 namespace {
+
+// bf16 path.  A lane owns 8 channels (16 bytes), a wave 512 consecutive
+// channels, and walks a run of tokens.  x rows and the lane's u values are
+// loaded PD = 4 tokens ahead into register rings; the k-1 previous rows are
+// kept converted to fp32.  Every load and store is a raw buffer access issued
+// on every path (masked ones fall outside the buffer), so the compiler's wait
+// counts keep the ring in flight; a sequence start clears the history in a
+// uniform branch that holds no memory access.  S2: a vector may straddle two
+// heads (head width not a multiple of 8, at least 8).
+template <int K, bool S2>
+__global__ void __launch_bounds__(256)
+k_fwd_hw_ring(Shape s, const float *__restrict__ u, const bf16 *__restrict__ w0, const bf16 *__restrict__ x,
+              bf16 *__restrict__ y, int n_vg, int n_runs, int tpw) {
+  constexpr int PD = 4;
+  const int lane = threadIdx.x & 63;
+  // wave-uniform (scalar) run bounds and sequence position
+  const int gw = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (gw >= n_vg * n_runs) return;  // whole waves only; no block-wide synchronisation
+  const int run = gw / n_vg, vg = gw - run * n_vg;
+  const int D = (int)s.D, BT = (int)s.BT, N = s.N, T = (int)s.T;  // BT*D, BT*N*2 < 2^30 (host-checked)
+  const int c0 = vg * 512 + lane * 8;
+  const bool act = c0 < D;
+  const int t_lo = run * tpw, t_hi = min(BT, t_lo + tpw);
+  const int ea = act ? c0 / s.hd : 0;
+  const int eb = S2 ? min(ea + 1, s.n_heads - 1) : ea;
+  int second = 0;  // channels of the later head
+  if (S2) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) second |= ((c0 + i) / s.hd != ea) << i;
+  }
+  const auto rx = make_rsrc(x, (uint32_t)(BT * D * 2));
+  const auto ry = make_rsrc(y, (uint32_t)(BT * D * 2));
+  const auto ru = make_rsrc(u, (uint32_t)(BT * N * 4));
+
+  float b[8][K];  // bias of the lane's channels: w0[c0 + i][j], contiguous 16 * K bytes
+  {
+    const auto rw = make_rsrc(w0, w0 ? (uint32_t)(D * K * 2) : 0u);  // no bias: zeros
+    uint32_t wv[4 * K];
+#pragma unroll
+    for (int q = 0; q < K; ++q) {
+      const uint4 r = buf_load16(rw, act ? (uint32_t)(c0 * K * 2 + 16 * q) : kOutside);
+      wv[4 * q] = r.x, wv[4 * q + 1] = r.y, wv[4 * q + 2] = r.z, wv[4 * q + 3] = r.w;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        const int e = i * K + j;
+        b[i][j] = __uint_as_float((e & 1) ? (wv[e >> 1] & 0xffff0000u) : (wv[e >> 1] << 16));
+      }
+  }
+
+  auto xoff = [&](int t) -> uint32_t {
+    return (act && t >= 0 && t < t_hi) ? (uint32_t)(t * D + c0) * 2u : kOutside;
+  };
+  auto uoff = [&](int t, int e, int j) -> uint32_t {
+    return (act && t < t_hi) ? (uint32_t)(t * N + e * K + j) * 4u : kOutside;
+  };
+  uint4 xr[PD];
+  float ua[PD][K], ub[PD][K];
+  auto load_tok = [&](int slot, int t) {
+    xr[slot] = buf_load16(rx, xoff(t));
+    if constexpr (K == 4) {
+      const uint4 a = buf_load16(ru, uoff(t, ea, 0));
+      ua[slot][0] = __uint_as_float(a.x), ua[slot][1] = __uint_as_float(a.y);
+      ua[slot][2] = __uint_as_float(a.z), ua[slot][3] = __uint_as_float(a.w);
+      if constexpr (S2) {
+        const uint4 c = buf_load16(ru, uoff(t, eb, 0));
+        ub[slot][0] = __uint_as_float(c.x), ub[slot][1] = __uint_as_float(c.y);
+        ub[slot][2] = __uint_as_float(c.z), ub[slot][3] = __uint_as_float(c.w);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        ua[slot][j] = buf_load_f32(ru, uoff(t, ea, j));
+        if constexpr (S2) ub[slot][j] = buf_load_f32(ru, uoff(t, eb, j));
+      }
+    }
+  };
+  auto cvt = [&](const uint4 r, float (&f)[8]) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  };
+
+  // history: xf[(i - j) & 3] holds x[t - j] (fp32) at step i; rows of the
+  // previous sequence read as zero
+  float xf[4][8];
+  int pos = t_lo % T;
+#pragma unroll
+  for (int j = 1; j < 4; ++j) {
+    const uint4 r = buf_load16(rx, (j < K && pos - j >= 0) ? xoff(t_lo - j) : kOutside);
+    cvt(r, xf[(4 - j) & 3]);
+  }
+  // the loop issues, per token, a store and then the loads PD tokens ahead;
+  // the prologue keeps that order (its stores fall outside y and are
+  // dropped) so the wait counts at the loop head are the steady-state ones
+#pragma unroll
+  for (int q = 0; q < PD; ++q) {
+    __builtin_amdgcn_sched_barrier(0);
+    buf_store16(ry, kOutside + 16 * q, make_uint4(0, 0, 0, 0));  // distinct, so none is folded away
+    load_tok(q, t_lo + q);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  const int n_iter = (t_hi - t_lo + 3) & ~3;
+  for (int it = 0; it < n_iter; it += 4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t_lo + it + i;
+      cvt(xr[i], xf[i]);
+      if (pos == 0) {  // a new sequence starts: no history
+#pragma unroll
+        for (int j = 1; j < 4; ++j)
+#pragma unroll
+          for (int c = 0; c < 8; ++c) xf[(i + 4 - j) & 3][c] = 0.f;
+      }
+      float out[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        float a = xf[i][c];
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+          const float uj = S2 ? (((second >> c) & 1) ? ub[i][j] : ua[i][j]) : ua[i][j];
+          a = fmaf(uj + b[c][j], xf[(i + 4 - j) & 3][c], a);
+        }
+        out[c] = a;
+      }
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        w[q] = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)out[2 * q]) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)out[2 * q + 1]) << 16);
+      buf_store16(ry, xoff(t), make_uint4(w[0], w[1], w[2], w[3]));
+      load_tok(i, t + PD);
+      pos = pos + 1 == T ? 0 : pos + 1;
+    }
+  }
+}
 
 constexpr int kFwdChunk = 32;  // tokens per thread
 
@@ -117,11 +260,42 @@ void launch(const Shape &s, const float *u, const void *w0, const void *x, void 
 
 }  // namespace
 
+// the ring kernel: bf16, k <= 4, at most two heads per 8-channel vector,
+// 32-bit offsets
+static bool ring_ok(const Shape &s) {
+  const int64_t lim = ((int64_t)1 << 30);
+  return s.k <= 4 && s.hd >= 8 && s.D % 8 == 0 && s.BT * s.D < lim && s.BT * s.N * 2 < lim;
+}
+
+template <int K, bool S2>
+static void launch_ring(const Shape &s, const float *u, const void *w0, const void *x, void *y, hipStream_t st) {
+  const int n_vg = (int)ceil_div(s.D, 512);
+  // about three waves per SIMD, runs of a multiple of 4 tokens
+  int tpw = (int)ceil_div(s.BT * n_vg, 3 * 4 * 256);
+  tpw = std::max(16, (tpw + 3) & ~3);
+  const int n_runs = (int)ceil_div(s.BT, tpw);
+  const int waves = n_vg * n_runs;
+  hipLaunchKernelGGL((k_fwd_hw_ring<K, S2>), dim3((unsigned)ceil_div(waves, 4)), dim3(256), 0, st, s, u,
+                     (const bf16 *)w0, (const bf16 *)x, (bf16 *)y, n_vg, n_runs, tpw);
+}
+
 template <typename T>
 int fwd_headwise(const Shape &s, const float *u, const void *w0, const void *x, void *y,
                  hipStream_t st) {
   const bool tr = trace_begin(DYNCONV_K_FWD_CONV, st);
-  if (s.k <= 4)
+  if (std::is_same<T, bf16>::value && ring_ok(s)) {
+    const bool s2 = s.hd % 8 != 0;
+    switch (s.k * 2 + (s2 ? 1 : 0)) {
+      case 2: launch_ring<1, false>(s, u, w0, x, y, st); break;
+      case 3: launch_ring<1, true>(s, u, w0, x, y, st); break;
+      case 4: launch_ring<2, false>(s, u, w0, x, y, st); break;
+      case 5: launch_ring<2, true>(s, u, w0, x, y, st); break;
+      case 6: launch_ring<3, false>(s, u, w0, x, y, st); break;
+      case 7: launch_ring<3, true>(s, u, w0, x, y, st); break;
+      case 8: launch_ring<4, false>(s, u, w0, x, y, st); break;
+      default: launch_ring<4, true>(s, u, w0, x, y, st); break;
+    }
+  } else if (s.k <= 4)
     launch<T, 4>(s, u, w0, x, y, st);
   else
     launch<T, 8>(s, u, w0, x, y, st);

@@ -265,12 +265,18 @@ k_dh(const bf16 *__restrict__ g, const bf16 *__restrict__ Mp, bf16 *__restrict__
   // The prologue keeps that order (with stores that fall outside dh and are
   // dropped), so the compiler's wait counts at the loop head are the steady
   // state ones and the second prefetch set stays in flight.
+  // (distinct offsets, so that none of these stores is folded away)
+  __builtin_amdgcn_sched_barrier(0);
   load(0, 0);
+  __builtin_amdgcn_sched_barrier(0);
   buf_store16(rd, kOutside, make_uint4(0, 0, 0, 0));
-  buf_store16(rd, kOutside, make_uint4(0, 0, 0, 0));
+  buf_store16(rd, kOutside + 16, make_uint4(0, 0, 0, 0));
+  __builtin_amdgcn_sched_barrier(0);
   load(1, 1);
-  buf_store16(rd, kOutside, make_uint4(0, 0, 0, 0));
-  buf_store16(rd, kOutside, make_uint4(0, 0, 0, 0));
+  __builtin_amdgcn_sched_barrier(0);
+  buf_store16(rd, kOutside + 32, make_uint4(0, 0, 0, 0));
+  buf_store16(rd, kOutside + 48, make_uint4(0, 0, 0, 0));
+  __builtin_amdgcn_sched_barrier(0);
   for (int tile = 0; tile < ntl; tile += 2) {
     step(0, tile);
     step(1, tile + 1);
