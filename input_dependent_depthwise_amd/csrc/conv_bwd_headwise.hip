@@ -168,12 +168,23 @@ k_bwd_hw(Params P) {
   const int BT = (int)s.BT;  // the host keeps every tensor below 4 GiB (32-bit byte offsets)
   const int T = s.T;
 
-  // per-lane bias
+  // per-lane bias: CPL*K contiguous bf16 at w0[cc*K], read as dwords with
+  // unconditional buffer loads (no bias: an empty buffer, every load reads 0)
   float w0r[CPL][4];
+  {
+    const auto rw = rsrc(P.w0, P.w0 ? (uint32_t)(Dc * K * 2) : 0u);
+    constexpr int NW = CPL * K / 2;
+    uint32_t wv[NW];
 #pragma unroll
-  for (int i = 0; i < CPL; ++i)
+    for (int q = 0; q < NW; ++q) wv[q] = __builtin_amdgcn_raw_buffer_load_b32(rw, (uint32_t)(cc * K * 2 + 4 * q), 0, 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) w0r[i][j] = (P.w0 && j < K) ? (float)P.w0[(size_t)(cc + i) * K + j] : 0.f;
+    for (int i = 0; i < CPL; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int el = i * K + j;
+        w0r[i][j] = j < K ? __uint_as_float((el & 1) ? (wv[el >> 1] & 0xffff0000u) : (wv[el >> 1] << 16)) : 0.f;
+      }
+  }
 
   float dwacc[CPL][K];
 #pragma unroll
