@@ -86,7 +86,9 @@ k_bwd_lr(Params P) {
   constexpr int ZW = 32 * KQ + 8;             // z row in LDS (bf16): rank, bias column, zeros, pad
   constexpr int NT = kW * 64;
   constexpr int CH = kDt / 8;                 // 16-byte chunks per x / dy row
-  constexpr int kVL = (2 * TR * CH + NT - 1) / NT;
+  constexpr int CHX = TR * CH;                 // 16-byte chunks of one staged tensor (x or dy)
+  constexpr int CHXP = (CHX + 63) / 64 * 64;  // padded to whole waves: a load slot's tensor is wave-uniform
+  constexpr int kVL = (2 * CHXP + NT - 1) / NT;
   constexpr int ZC = 16 * NQ;                 // z columns staged (rank padded)
   constexpr int kZL = (TR * ZC + NT - 1) / NT;
   constexpr int RV = 8 * NQ;                  // dz values per lane and tile
@@ -169,16 +171,21 @@ k_bwd_lr(Params P) {
   const int tile_lo = blockIdx.y * P.tpb;
   const int tile_hi = min(P.n_tiles, tile_lo + P.tpb);
   const int BT = (int)s.BT, D = (int)s.D;  // B*T*D < 2^31 (host-checked)
+  // slot q of a thread: chunk e of the virtual list [x chunks, padded][dy
+  // chunks, padded]; whether it is x or dy is the same for the whole wave (a
+  // scalar choice of buffer resource, not a per-lane one)
+  const int wave_base = __builtin_amdgcn_readfirstlane(tid & ~63);
   int v_row[kVL], v_goff[kVL], v_loff[kVL];
-  bool v_isx[kVL], v_ok[kVL];
+  bool v_isx[kVL], v_in[kVL], v_ok[kVL];
 #pragma unroll
   for (int q = 0; q < kVL; ++q) {
+    const bool isx = q * NT + wave_base < CHXP;
     const int e = tid + q * NT;
-    const bool isx = e < TR * CH;
-    const int e2 = isx ? e : e - TR * CH;
+    const int e2 = isx ? e : e - CHXP;
     const int r = e2 / CH, c16 = e2 % CH;
     v_isx[q] = isx;
-    v_ok[q] = e < 2 * TR * CH && cblk + c16 * 8 < s.D;
+    v_in[q] = e2 < CHX;                            // the slot has a place in the tile
+    v_ok[q] = v_in[q] && cblk + c16 * 8 < s.D;     // ... and its channels exist (else zeros)
     v_row[q] = isx ? r - KH : r;
     v_goff[q] = (int)cblk + c16 * 8;
     v_loff[q] = r * kRow + c16 * 8;
@@ -216,7 +223,7 @@ k_bwd_lr(Params P) {
   auto stage = [&](int set) {
 #pragma unroll
     for (int q = 0; q < kVL; ++q)
-      if (v_ok[q] || (tid + q * NT < 2 * TR * CH))
+      if (v_in[q])
         *reinterpret_cast<uint4 *>((v_isx[q] ? xs : dys) + v_loff[q]) = vpre[set][q];
 #pragma unroll
     for (int q = 0; q < kZL; ++q) {
