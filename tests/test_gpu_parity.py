@@ -48,6 +48,13 @@ SMALL = [
     Workload("hw_bf16_T1", B=3, T=1, d=32, D=64, k=4, kind=HEADWISE, n_heads=4, seed=27),
     Workload("lr_bf16_T3_lt_k", B=2, T=3, d=32, D=64, k=4, kind=LOWRANK, rank=16, seed=28),
     Workload("lr_fp32_T2", B=4, T=2, d=8, D=8, k=3, kind=LOWRANK, rank=3, dtype="fp32", seed=29),
+    # head widths that are not a multiple of 8 (a 16-byte channel vector straddles two heads)
+    Workload("hw_bf16_hd12_k1", B=2, T=77, d=32, D=96, k=1, kind=HEADWISE, n_heads=8, seed=31),
+    Workload("hw_bf16_hd20_k3", B=1, T=129, d=48, D=160, k=3, kind=HEADWISE, n_heads=8, seed=32),
+    Workload("hw_bf16_hd36_k2_nobias", B=2, T=65, d=32, D=144, k=2, kind=HEADWISE, n_heads=4, seed=33,
+             bias_std=0.0),
+    # rank past one 16-row block (two dz / dU blocks)
+    Workload("lr_bf16_r20_k3", B=1, T=200, d=256, D=1024, k=3, kind=LOWRANK, rank=20, seed=34),
 ]
 
 
