@@ -8,12 +8,12 @@
 // For L = sum(dy * y), one pass over x and dy gives
 //   dx[s,c]   = dy[s,c] + sum_j [s, s+j in one sequence] w[s+j,c,j] dy[s+j,c]
 //   G[t,c,j]  = [t-j in t's sequence] dy[t,c] x[t-j,c]         (never stored)
-//   dz[t,q]   = sum_{c,j} G[t,c,j] U[q,c*k+j]    -> one fp32 partial per 128-channel slice
+//   dz[t,q]   = sum_{c,j} G[t,c,j] U[q,c*k+j]    -> one fp32 partial per 64/128-channel slice
 //   dU[q,c*k+j] = sum_t z[t,q] G[t,c,j]          -> one fp32 partial per token range
 //   dw0[c,j]  = sum_t G[t,c,j]                   -> one fp32 partial per token range
 //
-// Work split.  A block (8 waves) owns 128 channels and a range of 32-token
-// tiles; wave w owns 16 of the channels.  Per tile the block stages x (rows
+// Work split.  A block (4 waves for rank <= 16, else 8) owns 64 or 128
+// channels and a range of 32-token tiles; wave w owns 16 of the channels.  Per tile the block stages x (rows
 // t0-k+1 .. t0+31), dy and z (rows t0 .. t0+31+k-1) in LDS.  Every product is
 // a v_mfma_f32_16x16x32_bf16; a lane (n = lane%16, g = lane/16) holds tokens
 // n and 16+n of the tile and channels 4g .. 4g+3 of the wave's 16:
@@ -29,7 +29,7 @@
 //   * G goes to LDS token-contiguous and is the A operand of
 //     D[channel][q] = G^T z over the tile's 32 tokens (dU); the same fragment
 //     dotted with ones gives dw0.
-// The 8 waves' dz meet in LDS; the block writes one partial per (slice,
+// The block's waves' dz meet in LDS; the block writes one partial per (slice,
 // token).  The global loads of the next tile (or, where registers allow, of
 // the one after) are in flight while a tile is computed.  Matrix-core fragments of U are built by each lane from global
 // memory at start (no separate preparation pass).
@@ -40,12 +40,12 @@
 namespace dynconv {
 namespace bwdlr {
 
-constexpr int kW = 8;            // waves per block
 constexpr int kCW = 16;          // channels per wave
-constexpr int kDt = kW * kCW;    // channels per block
-// LDS row of the x / dy tiles (bf16 elements): 68 dwords, so that the 8-byte
-// reads of 16 consecutive token rows x 2 channel quads cover all 64 banks once
-constexpr int kRow = kDt + 8;
+// Waves per block: 4 (64 channels) when rank <= 16, else 8 (128 channels).
+// Two 4-wave blocks share a CU, so one block's barriers overlap the other's
+// work; with a larger rank the per-slice dz partials (rank floats per token
+// and slice) grow too much for the narrower slices.
+inline int waves_for(const Shape &s) { return s.rank <= 16 ? 4 : 8; }
 constexpr int kGRow = 40;        // LDS row of the token-contiguous tiles: 32 tokens + pad (bf16)
 
 struct Params {
@@ -77,9 +77,14 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 }
 
 // K: taps; KQ: 32-row K-steps over rank + bias; NQ: 16-row blocks of rank.
-template <int K, int KQ, int NQ>
+template <int K, int KQ, int NQ, int kW>
 __global__ void __launch_bounds__(kW * 64, 2)
 k_bwd_lr(Params P) {
+  constexpr int kDt = kW * kCW;    // channels per block
+  // LDS row of the x / dy tiles (bf16 elements): 36 or 68 dwords, so that the
+  // 8-byte reads of 16 consecutive token rows x 2 channel quads cover all 64
+  // banks once
+  constexpr int kRow = kDt + 8;
   constexpr int KH = K - 1;
   constexpr int KP = (K + 1) / 2;             // tap pairs
   constexpr int TR = 32 + KH;                 // rows of a staged tile
@@ -385,7 +390,7 @@ k_bwd_lr(Params P) {
         *reinterpret_cast<float4 *>(&red[wave][lane * RVP + (tb * NQ + mq) * 4]) =
             make_float4(dzacc[tb][mq][0], dzacc[tb][mq][1], dzacc[tb][mq][2], dzacc[tb][mq][3]);
     __syncthreads();
-    // the 8 waves' sum, one partial per (slice, token): thread -> (q, token),
+    // the waves' sum, one partial per (slice, token): thread -> (q, token),
     // token fastest (consecutive threads read consecutive lanes' rows)
 #pragma unroll
     for (int it = 0; it < (32 * ZC + NT - 1) / NT; ++it) {
@@ -449,10 +454,11 @@ bool bwd_lowrank_supported(const Shape &s) {
 
 BwdLayout bwd_lowrank_layout(const Shape &s) {
   BwdLayout L = {};
-  L.Dt = bwdlr::kDt;
-  L.n_slices = (int)ceil_div(s.D, bwdlr::kDt);
+  L.Dt = bwdlr::waves_for(s) * bwdlr::kCW;
+  L.n_slices = (int)ceil_div(s.D, L.Dt);
   L.n_tiles = (int)ceil_div(s.BT, 32);
-  // token ranges: about two resident 8-wave blocks per CU over 256 CUs
+  // token ranges: 512 blocks (one round of two resident 4-wave blocks per CU,
+  // or two rounds of one 8-wave block)
   const int target = 512;
   int tpb = 1;
   while ((int64_t)L.n_slices * ceil_div(L.n_tiles, tpb) > target) ++tpb;
@@ -478,15 +484,17 @@ int bwd_lowrank(const Shape &s, const BwdLayout &L, const float *z, const void *
   P.dw0p = dw0p;
   P.tpb = L.tpb;
   P.n_tiles = L.n_tiles;
-  const dim3 grid((unsigned)L.n_slices, (unsigned)L.n_ranges), block(bwdlr::kW * 64);
+  const int kw = bwdlr::waves_for(s);
+  const dim3 grid((unsigned)L.n_slices, (unsigned)L.n_ranges), block(kw * 64);
   const int KQ = (int)ceil_div(s.rank + 1, 32), NQ = (int)ceil_div(s.rank, 16);
   const bool tr = trace_begin(DYNCONV_K_BWD_CONV, st);
   int rc = 0;
-#define LR(K_, KQ_, NQ_) hipLaunchKernelGGL((bwdlr::k_bwd_lr<K_, KQ_, NQ_>), grid, block, 0, st, P)
-#define LR_K(K_)                                  \
-  if (KQ == 1 && NQ == 1) LR(K_, 1, 1);           \
-  else if (KQ == 1 && NQ == 2) LR(K_, 1, 2);      \
-  else if (KQ == 2 && NQ == 2) LR(K_, 2, 2);      \
+  // one 16-row block of rank (NQ = 1) <=> rank <= 16 <=> 4 waves per block
+#define LR(K_, KQ_, NQ_, W_) hipLaunchKernelGGL((bwdlr::k_bwd_lr<K_, KQ_, NQ_, W_>), grid, block, 0, st, P)
+#define LR_K(K_)                                            \
+  if (KQ == 1 && NQ == 1 && kw == 4) LR(K_, 1, 1, 4);       \
+  else if (KQ == 1 && NQ == 2 && kw == 8) LR(K_, 1, 2, 8);  \
+  else if (KQ == 2 && NQ == 2 && kw == 8) LR(K_, 2, 2, 8);  \
   else rc = DYNCONV_E_LIMIT;
   switch (s.k) {
     case 1: LR_K(1) break;
