@@ -18,6 +18,7 @@
 // read once: the kernel is bound by HBM for N <= 64 and near the MFMA/HBM
 // ridge at N = 256.
 #include "kernels.h"
+#include "bufio.h"
 #include "mfma.h"
 
 namespace dynconv {
@@ -32,30 +33,34 @@ k_transpose_pad(const bf16 *__restrict__ M, bf16 *__restrict__ Mt, int K, int N,
   Mt[idx] = (n < N && k < K) ? M[(int64_t)k * N + n] : (bf16)0.f;
 }
 
-// Block: 4 waves x (16 * RW) rows of h, all Np columns.  Per K-step of 32 the
-// block stages the [Np][32] slice of Mt in LDS (double-buffered, one barrier
-// per step); each wave reads its h rows straight from global memory (16-byte
-// A fragments) and multiplies them against every column tile of the slice.
-// Both operands of the next step are loaded while the current one is used.
-template <int NT, int RW>
+// Block: 4 waves = (4 / KS) row groups x KS slices of K; a row group covers
+// 16 * RW rows of h, all Np columns.  Per K-step of 32 the block stages the
+// KS [Np][32] slices of Mt it needs in LDS (double-buffered, one barrier per
+// step); each wave reads its h rows straight from global memory (16-byte A
+// fragments) and multiplies them against every column tile of its slice.
+// Both operands of the next step are loaded while the current one is used;
+// loads are buffer accesses on every path (masked: outside the buffer).  With
+// KS = 2 the two K halves meet in LDS at the end in a fixed order.
+template <int NT, int RW, int KS>
 __global__ void __launch_bounds__(256)
 k_gen_proj_mfma(const bf16 *__restrict__ h, const bf16 *__restrict__ Mt, float *__restrict__ out,
                 int64_t M, int K, int Kp, int N) {
   constexpr int NP = NT * 16;
   constexpr int BROW = 40;                       // LDS row of the B slice: 32 k + pad (bf16)
-  constexpr int CHUNKS = NP * 4;                 // 16-byte chunks of a [NP][32] slice
-  constexpr int CPT = (CHUNKS + 255) / 256;      // chunks per thread
-  __shared__ __attribute__((aligned(16))) bf16 bs[2][NP * BROW];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int SCH = NP * 4;                    // 16-byte chunks of one [NP][32] slice
+  constexpr int CPT = (KS * SCH + 255) / 256;    // chunks per thread
+  constexpr int RG = 4 / KS;                     // row groups
+  constexpr int ROWS = RG * 16 * RW;             // rows per block
+  __shared__ __attribute__((aligned(16))) bf16 bs[2][KS][NP * BROW];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rg = wave % RG, ks = wave / RG;
   const int lr = lane & 15, lk = (lane >> 4) * 8;
-  const int64_t rbase = ((int64_t)blockIdx.x * 4 + wave) * 16 * RW;
+  const int64_t rblk = (int64_t)blockIdx.x * ROWS;
+  const int nrows = (int)min<int64_t>(ROWS, M - rblk);
+  const auto rh = make_rsrc(h + rblk * K, (uint32_t)((int64_t)nrows * K * 2));
+  const auto rb = make_rsrc(Mt, (uint32_t)((int64_t)NP * Kp * 2));
 
-  const bf16 *ha[RW];
-#pragma unroll
-  for (int r = 0; r < RW; ++r) {
-    const int64_t row = rbase + 16 * r + lr;
-    ha[r] = h + (row < M ? row : M - 1) * K;  // rows >= M are computed but never stored
-  }
   f32x4 acc[RW][NT];
 #pragma unroll
   for (int r = 0; r < RW; ++r)
@@ -63,40 +68,69 @@ k_gen_proj_mfma(const bf16 *__restrict__ h, const bf16 *__restrict__ Mt, float *
     for (int n = 0; n < NT; ++n) acc[r][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int steps = Kp / 32;
+  const int S = (steps + KS - 1) / KS;  // K-steps per slice (the last slice may run past K: zeros)
   uint4 bpre[CPT];
   bf16x8 apre[RW];
   auto load = [&](int st) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int e = tid + c * 256;
-      const int n = e >> 2, kc = (e & 3) * 8;
-      bpre[c] = e < CHUNKS ? *reinterpret_cast<const uint4 *>(Mt + (int64_t)n * Kp + st * 32 + kc)
-                           : make_uint4(0, 0, 0, 0);
+      const int sl = e / SCH, e2 = e - sl * SCH;
+      const int n = e2 >> 2, kc = (e2 & 3) * 8;
+      const int kst = sl * S + st;
+      const uint32_t off = ((KS * SCH) % 256 == 0 || e < KS * SCH) && kst < steps
+                               ? (uint32_t)(((int64_t)n * Kp + kst * 32 + kc) * 2)
+                               : kOutside;
+      bpre[c] = buf_load16(rb, off);
     }
-    const int k = st * 32 + lk;
+    const int k = (ks * S + st) * 32 + lk;
 #pragma unroll
-    for (int r = 0; r < RW; ++r)
-      apre[r] = k < K ? as_bf16x8(*reinterpret_cast<const uint4 *>(ha[r] + k)) : zero_bf16x8();
+    for (int r = 0; r < RW; ++r) {
+      const int row = (rg * RW + r) * 16 + lr;  // rows past the matrix read zeros and are never stored
+      apre[r] = as_bf16x8(buf_load16(rh, k < K ? (uint32_t)((row * K + k) * 2) : kOutside));
+    }
   };
-  if (steps > 0) load(0);
-  for (int st = 0; st < steps; ++st) {
+  load(0);
+  for (int st = 0; st < S; ++st) {
     const int buf = st & 1;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int e = tid + c * 256;
-      if (e < CHUNKS) *reinterpret_cast<uint4 *>(&bs[buf][(e >> 2) * BROW + (e & 3) * 8]) = bpre[c];
+      if ((KS * SCH) % 256 == 0 || e < KS * SCH) {
+        const int sl = e / SCH, e2 = e - sl * SCH;
+        *reinterpret_cast<uint4 *>(&bs[buf][sl][(e2 >> 2) * BROW + (e2 & 3) * 8]) = bpre[c];
+      }
     }
     bf16x8 a[RW];
 #pragma unroll
     for (int r = 0; r < RW; ++r) a[r] = apre[r];
     __syncthreads();
-    if (st + 1 < steps) load(st + 1);
+    load(st + 1);
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      const bf16x8 b = as_bf16x8(*reinterpret_cast<const uint4 *>(&bs[buf][(n * 16 + lr) * BROW + lk]));
+      const bf16x8 b = as_bf16x8(*reinterpret_cast<const uint4 *>(&bs[buf][ks][(n * 16 + lr) * BROW + lk]));
 #pragma unroll
       for (int r = 0; r < RW; ++r) acc[r][n] = mfma16(a[r], b, acc[r][n]);
     }
+  }
+
+  if constexpr (KS == 2) {
+    // the second K half hands its sums to the first through LDS
+    f32x4 *red = reinterpret_cast<f32x4 *>(&bs[0][0][0]);
+    static_assert(sizeof(bs) >= RG * RW * NT * 64 * sizeof(f32x4), "reduction buffer");
+    __syncthreads();
+    if (ks == 1) {
+#pragma unroll
+      for (int r = 0; r < RW; ++r)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) red[((rg * RW + r) * NT + n) * 64 + lane] = acc[r][n];
+    }
+    __syncthreads();
+    if (ks == 1) return;
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[r][n] += red[((rg * RW + r) * NT + n) * 64 + lane];
   }
 
   // D fragment: lane holds D[4*(lane/16) + i][lane%16]
@@ -108,7 +142,7 @@ k_gen_proj_mfma(const bf16 *__restrict__ h, const bf16 *__restrict__ Mt, float *
       if (col >= N) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int64_t row = rbase + r * 16 + (lane >> 4) * 4 + i;
+        const int64_t row = rblk + (rg * RW + r) * 16 + (lane >> 4) * 4 + i;
         if (row < M) out[row * N + col] = acc[r][n][i];
       }
     }
@@ -211,17 +245,19 @@ k_gen_proj_ksplit(const bf16 *__restrict__ h, const bf16 *__restrict__ Mt, float
 template <int NT>
 void launch_nt(const bf16 *h, const bf16 *Mt, float *out, int64_t M, int K, int Kp, int N,
                hipStream_t st) {
-  // two row tiles per wave when the weight is wide (its LDS slice is then
-  // reused twice per read) and the rows still give one block per CU
   if constexpr (NT <= 2) {
     hipLaunchKernelGGL((k_gen_proj_ksplit<NT>), dim3((unsigned)ceil_div(M, 32)), dim3(256), 0, st, h, Mt,
                        out, M, K, Kp, N);
-  } else if (NT >= 4 && M >= 256 * 128) {
-    hipLaunchKernelGGL((k_gen_proj_mfma<NT, 2>), dim3((unsigned)ceil_div(M, 128)), dim3(256), 0, st, h, Mt,
-                       out, M, K, Kp, N);
   } else {
-    hipLaunchKernelGGL((k_gen_proj_mfma<NT, 1>), dim3((unsigned)ceil_div(M, 64)), dim3(256), 0, st, h, Mt,
-                       out, M, K, Kp, N);
+    // about two blocks per CU: 64-row blocks when the rows give 512 of them,
+    // else 32-row blocks with K split in two
+    if (M >= 512 * 64) {
+      hipLaunchKernelGGL((k_gen_proj_mfma<NT, 1, 1>), dim3((unsigned)ceil_div(M, 64)), dim3(256), 0, st, h, Mt,
+                         out, M, K, Kp, N);
+    } else {
+      hipLaunchKernelGGL((k_gen_proj_mfma<NT, 1, 2>), dim3((unsigned)ceil_div(M, 32)), dim3(256), 0, st, h, Mt,
+                         out, M, K, Kp, N);
+    }
   }
 }
 
