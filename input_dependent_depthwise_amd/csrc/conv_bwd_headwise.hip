@@ -26,6 +26,7 @@
 // Loads run 4 tokens ahead, into 8-slot rings (for x the ring doubles as the
 // k-tap history).
 #include "kernels.h"
+#include "bufio.h"
 
 namespace dynconv {
 namespace bwdhw {
@@ -52,6 +53,26 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_rows(float v) {
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWS, 0xf, false));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4 and 8
+// within each row of 16 lanes (lanes whose source lies before their row add
+// 0), then rows 1 and 3 add the last lane of the row before them (row_bcast:15)
+// and rows 2 and 3 the last lane of row 1 (row_bcast:31).
+__device__ __forceinline__ float wave_prefix(float v) {
+  v += dpp<0x111>(v);
+  v += dpp<0x112>(v);
+  v += dpp<0x114>(v);
+  v += dpp<0x118>(v);
+  v += dpp_rows<0x142, 0xa>(v);
+  v += dpp_rows<0x143, 0xc>(v);
+  return v;
 }
 
 // DPP partner patterns, by the highest lane-index bit they flip: xor 15
@@ -151,7 +172,6 @@ k_bwd_hw(Params P) {
   constexpr int PD = 4;              // tokens loaded ahead
   const Shape &s = P.s;
 
-  __shared__ __attribute__((aligned(16))) float dured[S == 0 ? 4 : 1][S == 0 ? 64 * 16 : 4];
   __shared__ __attribute__((aligned(16))) float dwred[4][64 * CPL * K];
 
   const int lane = threadIdx.x & 63;
@@ -206,6 +226,17 @@ k_bwd_hw(Params P) {
   const uint32_t row_g = (uint32_t)P.R * 4u;
   const auto rg = rsrc(P.gpart + (size_t)span * BT * P.R, (uint32_t)BT * row_g);
   const uint32_t voff_g = (uint32_t)(e - e_lo) * K * 4u;
+  // any head width (S = 0): this lane's head covers lanes [hla, lb) of the
+  // span (heads are whole lanes: hd is a multiple of CPL); its last lane
+  // writes the head's sums
+  int hla = 0;
+  bool hlast = false;
+  if constexpr (S == 0) {
+    const int nact = all_act ? 64 : (Dc - span_c0) / CPL;
+    hla = max(0, (e * s.hd - span_c0) / CPL);
+    const int lb = min(nact, ((e + 1) * s.hd - span_c0) / CPL);
+    hlast = act && lane == lb - 1;
+  }
 
   if (t_a < BT) {
     // token rings: x in 8 slots (slot = (t - t_a) mod 8) holding tokens
@@ -254,44 +285,10 @@ k_bwd_hw(Params P) {
 #pragma unroll
     for (int p = 0; p < NP + 4; ++p) held[p] = 0u;
 
-    // generic head widths: du of 4 tokens at a time through LDS
-    auto du_lds = [&](const float (&vals)[16], int t4) {
-      float *red = dured[wave];
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<float4 *>(&red[lane * 16 + 4 * q]) =
-            make_float4(vals[4 * q], vals[4 * q + 1], vals[4 * q + 2], vals[4 * q + 3]);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const int nact = all_act ? 64 : (Dc - span_c0) / CPL;
-      const int last_c = span_c0 + nact * CPL - 1;
-      const int n_slots = (int)(last_c / s.hd) - e_lo + 1;
-      const int v = lane & 15, tok = v >> 2, j = v & 3;
-      for (int rd = 0; rd * 4 < n_slots; ++rd) {
-        const int slot = rd * 4 + (lane >> 4);
-        const int eh = e_lo + slot;
-        int la = (int)((eh * s.hd - span_c0) / CPL);
-        int lb = (int)(((eh + 1) * s.hd - span_c0) / CPL);
-        la = la < 0 ? 0 : la;
-        lb = lb > nact ? nact : lb;
-        float sum = 0.f;
-        for (int l = la; l < lb; ++l) sum += red[l * 16 + v];
-        const int t = t4 + tok;
-        if (slot < n_slots && j < K && t < t_b)
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sum), rg, (uint32_t)(slot * K + j) * 4u,
-                                                (uint32_t)t * row_g, 0);
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    };
-
     // one block of 8 tokens from tg.  The tests on t and pos are wave-uniform
     // (scalar branches); keeping them in every block rather than compiling a
     // second, test-free copy keeps the register allocation of the rings simple.
     auto block = [&](int tg) {
-      float vals16[S == 0 ? 16 : 1];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int t = tg + i;
@@ -390,9 +387,29 @@ k_bwd_hw(Params P) {
             }
           }
         } else {
+          // any head width: head sums as differences of the wave's prefix sums
+          if (t < t_b) {
+            float hs[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) vals16[(i & 3) * 4 + j] = vals[j];
-          if ((i & 3) == 3 && tg + (i - 3) < t_b) du_lds(vals16, tg + (i - 3));
+            for (int j = 0; j < 4; ++j) {
+              const float pre = wave_prefix(vals[j]);
+              const float before = __builtin_bit_cast(
+                  float, __builtin_amdgcn_ds_bpermute(4 * (hla > 0 ? hla - 1 : 0), __builtin_bit_cast(int, pre)));
+              hs[j] = hla > 0 ? pre - before : pre;
+            }
+            // (the partials stay below 2 GiB, so kOutside lies past them)
+            const uint32_t og = (uint32_t)t * row_g + voff_g;
+            if constexpr (K == 4) {
+              buf_store16(rg, hlast ? og : kOutside,
+                          make_uint4(__float_as_uint(hs[0]), __float_as_uint(hs[1]), __float_as_uint(hs[2]),
+                                     __float_as_uint(hs[3])));
+            } else {
+#pragma unroll
+              for (int j = 0; j < K; ++j) buf_store_f32(rg, hlast ? og + (uint32_t)j * 4u : kOutside, hs[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) held[NP + j] = __float_as_uint(hs[j]);
+          }
         }
         // keep each token's work in its own scheduling region: interleaving
         // tokens only raises register pressure (the loads are already ahead)
@@ -458,7 +475,7 @@ bool bwd_headwise_supported(const Shape &s) {
   const int64_t lim = (int64_t)1 << 32;
   if (s.BT * s.D * 2 >= lim || s.BT * s.N * 4 >= lim) return false;
   const BwdLayout L = bwd_headwise_layout(s);
-  return s.BT * L.R * 4 < lim;
+  return s.BT * L.R * 4 < ((int64_t)1 << 31) - 64;
 }
 
 int bwd_headwise(const Shape &s, const BwdLayout &L, const float *u, const void *w0, const void *x,
