@@ -400,54 +400,73 @@ k_dM(const bf16 *__restrict__ h, const bf16 *__restrict__ gT, float *__restrict_
       }
 }
 
-// out[e] = sum_p part[p][e] for e < n, p < np (fixed order), for up to three
-// independent reductions packed into one launch.
+// out[e] = sum_p part[p][e] for e < n, p < np, for up to three independent
+// reductions packed into one launch.
 struct Red {
   const float *part;
   float *out;
   int64_t n;
   int np;
+  int lp;         // lanes per output quad (1, 2, 4 or 8): each sums every lp-th partial
+  int64_t lanes;  // threads of this reduction, a whole number of waves
 };
 
-// Four consecutive outputs per thread; the partial rows are loaded 8 at a
-// time ahead of the adds, which stay in partial order (fixed-order sums).
+// Four consecutive outputs per group of lp adjacent lanes.  Lane `sub` of a
+// group sums partials sub, sub + lp, ... in ascending order (loads issued 8
+// at a time ahead of the adds); the group then adds its lanes' sums with an
+// xor butterfly, which gives every lane the same bits (each step adds the
+// same two values), so the result is fixed-order and deterministic.
 __global__ void __launch_bounds__(256) k_finalize(Red r0, Red r1, Red r2) {
-  int64_t idx = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
-  const int64_t q0 = (r0.n + 3) / 4 * 4, q1 = (r1.n + 3) / 4 * 4, q2 = (r2.n + 3) / 4 * 4;
+  int64_t th = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const Red *r;
-  if (idx < q0) {
+  if (th < r0.lanes) {
     r = &r0;
-  } else if ((idx -= q0) < q1) {
+  } else if ((th -= r0.lanes) < r1.lanes) {
     r = &r1;
-  } else if ((idx -= q1) < q2) {
+  } else if ((th -= r1.lanes) < r2.lanes) {
     r = &r2;
   } else {
-    return;
+    return;  // whole waves: a reduction's lanes never share a wave with another's
   }
-  if (!r->out || idx >= r->n) return;
+  const int lp = r->lp, np = r->np;
+  const int sub = (int)(th & (lp - 1));
+  const int64_t idx = (th / lp) * 4;
   const int64_t n = r->n;
-  if (idx + 4 <= n && n % 4 == 0) {
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  const bool vec = n % 4 == 0;
+  if (idx < n && vec) {
     const float *src = r->part + idx;
-    int p = 0;
-    for (; p + 8 <= r->np; p += 8) {
+    int p = sub;
+    for (; p + 7 * lp < np; p += 8 * lp) {
       float4 a[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) a[u] = *reinterpret_cast<const float4 *>(src + (int64_t)(p + u) * n);
+      for (int u = 0; u < 8; ++u) a[u] = *reinterpret_cast<const float4 *>(src + (int64_t)(p + u * lp) * n);
 #pragma unroll
       for (int u = 0; u < 8; ++u) v.x += a[u].x, v.y += a[u].y, v.z += a[u].z, v.w += a[u].w;
     }
-    for (; p < r->np; ++p) {
+    for (; p < np; p += lp) {
       const float4 a = *reinterpret_cast<const float4 *>(src + (int64_t)p * n);
       v.x += a.x, v.y += a.y, v.z += a.z, v.w += a.w;
     }
+  } else if (idx < n) {
+    float w[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < 4; ++c)
+      if (idx + c < n)
+        for (int p = sub; p < np; p += lp) w[c] += r->part[(int64_t)p * n + idx + c];
+    v = make_float4(w[0], w[1], w[2], w[3]);
+  }
+  for (int m = 1; m < lp; m <<= 1) {
+    v.x += __shfl_xor(v.x, m);
+    v.y += __shfl_xor(v.y, m);
+    v.z += __shfl_xor(v.z, m);
+    v.w += __shfl_xor(v.w, m);
+  }
+  if (sub != 0 || idx >= n || !r->out) return;
+  if (vec) {
     *reinterpret_cast<float4 *>(r->out + idx) = v;
   } else {
-    for (int64_t e = idx; e < idx + 4 && e < n; ++e) {
-      float v = 0.f;
-      for (int p = 0; p < r->np; ++p) v += r->part[(int64_t)p * n + e];
-      r->out[e] = v;
-    }
+    const float w[4] = {v.x, v.y, v.z, v.w};
+    for (int c = 0; c < 4 && idx + c < n; ++c) r->out[idx + c] = w[c];
   }
 }
 
@@ -567,13 +586,21 @@ int gen_bwd(const Shape &s, const float *gpart, int n_slices, int R, int Dt, con
   return 0;
 }
 
+// lanes per output quad: enough that each lane sums at most 8 partials
+static gbwd::Red make_red(const float *p, float *o, int64_t n, int np) {
+  gbwd::Red r{p, o, o ? n : 0, np, 1, 0};
+  while (r.lp < 8 && r.lp * 8 < np) r.lp *= 2;
+  r.lanes = ceil_div(ceil_div(r.n, 4) * r.lp, 64) * 64;
+  return r;
+}
+
 int finalize(const float *p0, float *o0, int64_t n0, int np0, const float *p1, float *o1, int64_t n1,
              int np1, const float *p2, float *o2, int64_t n2, int np2, hipStream_t st) {
-  gbwd::Red r0{p0, o0, o0 ? n0 : 0, np0}, r1{p1, o1, o1 ? n1 : 0, np1}, r2{p2, o2, o2 ? n2 : 0, np2};
-  const int64_t quads = ceil_div(r0.n, 4) + ceil_div(r1.n, 4) + ceil_div(r2.n, 4);
-  if (quads == 0) return 0;
+  const gbwd::Red r0 = make_red(p0, o0, n0, np0), r1 = make_red(p1, o1, n1, np1), r2 = make_red(p2, o2, n2, np2);
+  const int64_t lanes = r0.lanes + r1.lanes + r2.lanes;
+  if (lanes == 0) return 0;
   const bool tr = trace_begin(DYNCONV_K_FINALIZE, st);
-  hipLaunchKernelGGL(gbwd::k_finalize, dim3((unsigned)ceil_div(quads, 256)), dim3(256), 0, st, r0, r1, r2);
+  hipLaunchKernelGGL(gbwd::k_finalize, dim3((unsigned)ceil_div(lanes, 256)), dim3(256), 0, st, r0, r1, r2);
   trace_end(tr, st);
   return 0;
 }
