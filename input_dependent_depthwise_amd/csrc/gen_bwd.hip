@@ -111,6 +111,21 @@ k_combine(Shape s, const float *__restrict__ gpart, int n_slices, int R, int Dt,
           if (tq[qi] < s.BT && c0 + nq[qi] + c < s.N)
             for (int d = 0; d < n_slices; ++d) v[qi][c] += src[qi][d * stride + c];
     }
+  } else if (s.k == 4) {
+    // a quad is one head's four taps: contiguous (and 16-byte aligned, R being
+    // a multiple of 4) in each slice's partial row
+    for (int p = 0; p < span; ++p) {
+      float4 a[2];
+#pragma unroll
+      for (int qi = 0; qi < 2; ++qi) {
+        const int64_t off = tab[nq[qi]][p];
+        a[qi] = (off >= 0 && tq[qi] < s.BT) ? *reinterpret_cast<const float4 *>(gpart + off + tq[qi] * R)
+                                            : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int qi = 0; qi < 2; ++qi)
+        v[qi][0] += a[qi].x, v[qi][1] += a[qi].y, v[qi][2] += a[qi].z, v[qi][3] += a[qi].w;
+    }
   } else {
     for (int p = 0; p < span; ++p) {
       float a[2][4];
