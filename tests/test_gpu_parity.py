@@ -55,6 +55,10 @@ SMALL = [
              bias_std=0.0),
     # rank past one 16-row block (two dz / dU blocks)
     Workload("lr_bf16_r20_k3", B=1, T=200, d=256, D=1024, k=3, kind=LOWRANK, rank=20, seed=34),
+    # sequence length a multiple of the 32-token tile (the backward's halo rows
+    # across a sequence start are cut at load time), several sequences
+    Workload("lr_bf16_r16_T96", B=3, T=96, d=64, D=192, k=4, kind=LOWRANK, rank=16, seed=35),
+    Workload("lr_bf16_r32_k3_T64", B=3, T=64, d=64, D=256, k=3, kind=LOWRANK, rank=32, seed=36),
 ]
 
 
