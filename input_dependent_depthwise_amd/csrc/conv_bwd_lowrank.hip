@@ -26,9 +26,10 @@
 //     (one half of each pair cleared); rounded to bf16 once, two taps at a time
 //     are the B operand of D[q][token] = U G (dz, summed over taps and
 //     channels in the accumulator);
-//   * G goes to LDS token-contiguous and is the A operand of
-//     D[channel][q] = G^T z over the tile's 32 tokens (dU); the same fragment
-//     dotted with ones gives dw0.
+//   * G goes to LDS token-major (8-byte writes) and comes back transposed
+//     (ds_read_b64_tr_b16, four tokens of one channel per lane) as the A
+//     operand of D[channel][q] = G^T z over the tile's 32 tokens (dU); the
+//     same fragment dotted with ones gives dw0.
 // The block's waves' dz meet in LDS; the block writes one partial per (slice,
 // token).  The global loads of the next tile (or, where registers allow, of
 // the one after) are in flight while a tile is computed.  Matrix-core fragments of U are built by each lane from global
@@ -46,7 +47,23 @@ constexpr int kCW = 16;          // channels per wave
 // work; with a larger rank the per-slice dz partials (rank floats per token
 // and slice) grow too much for the narrower slices.
 inline int waves_for(const Shape &s) { return s.rank <= 16 ? 4 : 8; }
-constexpr int kGRow = 40;        // LDS row of the token-contiguous tiles: 32 tokens + pad (bf16)
+constexpr int kGRow = 40;        // LDS row of the token-contiguous z^T tile: 32 tokens + pad (bf16)
+// G of one tap in LDS: 32 token rows of 16 channels (32 bytes), 128 bytes of
+// pad after every 8 rows and the row's four 8-byte channel quads swapped in
+// pairs on rows 8..15 and 24..31, so that both the writes (16 rows x 2 quads
+// per 32 lanes) and the transposed reads (4 rows x 4 quads per 16 lanes) use
+// 64 distinct banks
+constexpr int kGTap = 32 * 32 + 4 * 128;
+__device__ __forceinline__ int g_off(int t, int quad) {
+  return 32 * t + 128 * (t >> 3) + 8 * (quad ^ (2 * ((t >> 3) & 1)));
+}
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+// four bf16 of one channel from four token rows (lane l%16 = channel)
+__device__ __forceinline__ uint2 read_tr16(const unsigned char *p) {
+  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p));
+  return __builtin_bit_cast(uint2, v);
+}
 
 struct Params {
   Shape s;
@@ -106,7 +123,7 @@ k_bwd_lr(Params P) {
   __shared__ __attribute__((aligned(16))) bf16 dys[TR * kRow];         // dy rows t0 .. t0+31+KH
   __shared__ __attribute__((aligned(16))) bf16 zs[TR * ZW];            // z rows t0 .. t0+31+KH, bf16
   __shared__ __attribute__((aligned(16))) bf16 zt[ZC * kGRow];         // z^T: rows q, tokens t0 .. t0+31
-  __shared__ __attribute__((aligned(16))) bf16 gt[kW][32 * kGRow];     // per wave: G of a tap pair, [tap][channel][token]
+  __shared__ __attribute__((aligned(16))) unsigned char gt[kW][2 * kGTap];  // per wave: G of a tap pair
   __shared__ __attribute__((aligned(16))) float red[kW][64 * RVP];     // per wave: dz partial of a tile
 
   const int tid = threadIdx.x;
@@ -145,7 +162,7 @@ k_bwd_lr(Params P) {
       fa[j][kq] = pack_bf16x8(v);
     }
   // dz A (tap pair jp, q block mq): A[m = q = 16mq + n][k = 8g + i],
-  //   k <-> (channel cw + 4g + i/2, tap 2jp + i%2)
+  //   k <-> (channel cw + 4g + i%4, tap 2jp + i/4)
   bf16x8 za[KP][NQ];
 #pragma unroll
   for (int jp = 0; jp < KP; ++jp)
@@ -154,8 +171,8 @@ k_bwd_lr(Params P) {
       float v[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int q = 16 * mq + n, j = 2 * jp + (i & 1);
-        const int64_t c = cw + 4 * g + (i >> 1);
+        const int q = 16 * mq + n, j = 2 * jp + (i >> 2);
+        const int64_t c = cw + 4 * g + (i & 3);
         v[i] = (q < rank && j < K && c < s.D) ? (float)P.U[(int64_t)q * Dk + c * K + j] : 0.f;
       }
       za[jp][mq] = pack_bf16x8(v);
@@ -246,7 +263,12 @@ k_bwd_lr(Params P) {
   const auto rg = make_rsrc(P.gpart + (int64_t)blockIdx.x * s.BT * rank, (uint32_t)(s.BT * rank * 4));
   const uint32_t ones = 0x3f803f80u;     // bf16 pair (1, 1)
   const int wc = wave * kCW + 4 * g;     // the lane's first channel within the tile rows
-  bf16 *gtw = gt[wave];
+  unsigned char *gtw = gt[wave];
+  // G writes: token row 16tb + n, channel quad g; transposed reads for the
+  // dU A operand: lane (channel n, token group g) supplies row 8g + 4h + n/4,
+  // quad n%4 and receives tokens 8g+4h .. +3 of channel n
+  const int gw_off[2] = {g_off(n, g), g_off(16 + n, g)};
+  const int gr_off[2] = {g_off(8 * g + n / 4, n % 4), g_off(8 * g + 4 + n / 4, n % 4)};
 
   auto tile_step = [&](const int set, const int tile) {
     const int64_t t0 = (int64_t)tile * 32;
@@ -288,7 +310,7 @@ k_bwd_lr(Params P) {
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
       for (int mq = 0; mq < NQ; ++mq) dzacc[tb][mq] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float gprev[2][4];  // G of the even tap of the current pair (fp32)
+    uint32_t gev[2][2];  // G of the even tap of the current pair: bf16 pairs of channels 4g.. 4g+3
 
 #pragma unroll
     for (int j = 0; j < K; ++j) {
@@ -325,32 +347,30 @@ k_bwd_lr(Params P) {
           gv[tb][2 * p + 1] = dot2z(xw[p], dhi[tb][p]);
         }
       }
-      if (!(j & 1) && j < K - 1) {
+      // G of tap j rounded to bf16 once, channel pairs; token-major copy in LDS
+      const bool odd = j & 1;
+      uint32_t gq[2][2];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) gq[tb][h] = pack2(gv[tb][2 * h], gv[tb][2 * h + 1]);
+        *reinterpret_cast<uint2 *>(gtw + (odd ? kGTap : 0) + gw_off[tb]) = make_uint2(gq[tb][0], gq[tb][1]);
+      }
+      if (!odd && j < K - 1) {
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) gprev[tb][r] = gv[tb][r];
+          for (int h = 0; h < 2; ++h) gev[tb][h] = gq[tb][h];
         continue;
       }
       // a tap pair (2jp, 2jp+1) is complete (the odd tap is zero past k):
-      // bf16 pairs, the dz MFMA and the token-contiguous copy for dU
+      // the dz MFMA, then dU from the transposed copy
       const int jp = j >> 1;
-      const bool odd = j & 1;
-      uint32_t gpair[2][4];
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          gpair[tb][r] = odd ? pack2(gprev[tb][r], gv[tb][r]) : pack2(gv[tb][r], 0.f);
-          asm("" : "+v"(gpair[tb][r]));  // store the halves of this register (no re-rounding)
-          *reinterpret_cast<uint16_t *>(&gtw[(4 * g + r) * kGRow + 16 * tb + n]) = (uint16_t)gpair[tb][r];
-          if (odd)
-            *reinterpret_cast<uint16_t *>(&gtw[(16 + 4 * g + r) * kGRow + 16 * tb + n]) = (uint16_t)(gpair[tb][r] >> 16);
-        }
-      // dz: B[k = 8g + i][token n], k <-> (channel 4g + i/2, tap 2jp + i%2)
+      // dz: B[k = 8g + i][token n], k <-> (channel 4g + i%4, tap 2jp + i/4)
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
-        const bf16x8 bb = as_bf16x8(make_uint4(gpair[tb][0], gpair[tb][1], gpair[tb][2], gpair[tb][3]));
+        const bf16x8 bb = odd ? as_bf16x8(make_uint4(gev[tb][0], gev[tb][1], gq[tb][0], gq[tb][1]))
+                              : as_bf16x8(make_uint4(gq[tb][0], gq[tb][1], 0u, 0u));
 #pragma unroll
         for (int mq = 0; mq < NQ; ++mq) dzacc[tb][mq] = mfma16(za[jp][mq], bb, dzacc[tb][mq]);
       }
@@ -363,7 +383,9 @@ k_bwd_lr(Params P) {
       for (int jj = 0; jj < 2; ++jj) {
         const int jt = 2 * jp + jj;
         if (jt < K) {
-          const uint4 raw = *reinterpret_cast<const uint4 *>(&gtw[(16 * jj + n) * kGRow + 8 * g]);
+          const uint2 lo = read_tr16(gtw + jj * kGTap + gr_off[0]);
+          const uint2 hi = read_tr16(gtw + jj * kGTap + gr_off[1]);
+          const uint4 raw = make_uint4(lo.x, lo.y, hi.x, hi.y);
 #pragma unroll
           for (int nq = 0; nq < NQ; ++nq) dUacc[jt][nq] = mfma16(as_bf16x8(raw), zb[nq], dUacc[jt][nq]);
           dw0acc[jt] = dot2(raw.w, ones, dot2(raw.z, ones, dot2(raw.y, ones, dot2(raw.x, ones, dw0acc[jt]))));
