@@ -119,10 +119,11 @@ k_bwd_lr(Params P) {
   const Shape &s = P.s;
   const int rank = s.rank;
 
-  __shared__ __attribute__((aligned(16))) bf16 xs[TR * kRow];          // x rows t0-KH .. t0+31
-  __shared__ __attribute__((aligned(16))) bf16 dys[TR * kRow];         // dy rows t0 .. t0+31+KH
-  __shared__ __attribute__((aligned(16))) bf16 zs[TR * ZW];            // z rows t0 .. t0+31+KH, bf16
-  __shared__ __attribute__((aligned(16))) bf16 zt[ZC * kGRow];         // z^T: rows q, tokens t0 .. t0+31
+  // (each with a spare row or element that unused load slots write to)
+  __shared__ __attribute__((aligned(16))) bf16 xs[(TR + 1) * kRow];    // x rows t0-KH .. t0+31
+  __shared__ __attribute__((aligned(16))) bf16 dys[(TR + 1) * kRow];   // dy rows t0 .. t0+31+KH
+  __shared__ __attribute__((aligned(16))) bf16 zs[TR * ZW + 8];        // z rows t0 .. t0+31+KH, bf16
+  __shared__ __attribute__((aligned(16))) bf16 zt[ZC * kGRow + 8];     // z^T: rows q, tokens t0 .. t0+31
   __shared__ __attribute__((aligned(16))) unsigned char gt[kW][2 * kGTap];  // per wave: G of a tap pair
   __shared__ __attribute__((aligned(16))) float red[kW][64 * RVP];     // per wave: dz partial of a tile
 
@@ -188,38 +189,44 @@ k_bwd_lr(Params P) {
   }
 
   // ---- global -> register prefetch of one tile ----
-  // Each thread's load slots are fixed for the block: precompute their row
-  // offset (relative to t0), global column and LDS offset once.
+  // Each thread's load slots are fixed for the block: precompute their byte
+  // offset at tile 0 and their LDS destination once.  Per tile the offset only
+  // advances; the buffer's range check returns zeros for every slot whose
+  // offset falls outside the tensor: rows before 0 (the offset wraps to a huge
+  // value), rows past BT, and masked slots (offset kOutside + tile advance,
+  // still above the tensor, which is under 2 GiB).
   const int tile_lo = blockIdx.y * P.tpb;
   const int tile_hi = min(P.n_tiles, tile_lo + P.tpb);
-  const int BT = (int)s.BT, D = (int)s.D;  // B*T*D < 2^31 (host-checked)
+  const int D = (int)s.D;  // B*T*D < 2^31 (host-checked)
   // slot q of a thread: chunk e of the virtual list [x chunks, padded][dy
   // chunks, padded]; whether it is x or dy is the same for the whole wave (a
   // scalar choice of buffer resource, not a per-lane one)
   const int wave_base = __builtin_amdgcn_readfirstlane(tid & ~63);
-  int v_row[kVL], v_goff[kVL], v_loff[kVL];
-  bool v_isx[kVL], v_in[kVL], v_ok[kVL];
+  uint32_t v_gbase[kVL];
+  int v_loff[kVL];
+  bool v_isx[kVL];
 #pragma unroll
   for (int q = 0; q < kVL; ++q) {
     const bool isx = q * NT + wave_base < CHXP;
     const int e = tid + q * NT;
     const int e2 = isx ? e : e - CHXP;
     const int r = e2 / CH, c16 = e2 % CH;
+    const bool in = e2 < CHX;                        // the slot has a place in the tile
+    const bool ok = in && cblk + c16 * 8 < s.D;      // ... and its channels exist (else zeros)
     v_isx[q] = isx;
-    v_in[q] = e2 < CHX;                            // the slot has a place in the tile
-    v_ok[q] = v_in[q] && cblk + c16 * 8 < s.D;     // ... and its channels exist (else zeros)
-    v_row[q] = isx ? r - KH : r;
-    v_goff[q] = (int)cblk + c16 * 8;
-    v_loff[q] = r * kRow + c16 * 8;
+    v_gbase[q] = ok ? (uint32_t)((isx ? r - KH : r) * D + (int)cblk + c16 * 8) * 2u : kOutside;
+    v_loff[q] = in ? r * kRow + c16 * 8 : TR * kRow;
   }
-  int z_row[kZL], z_col[kZL];
-  bool z_ok[kZL];
+  uint32_t z_gbase[kZL];
+  int zs_off[kZL], zt_off[kZL];
 #pragma unroll
   for (int q = 0; q < kZL; ++q) {
     const int e = tid + q * NT;
-    z_row[q] = e / ZC;
-    z_col[q] = e % ZC;
-    z_ok[q] = e < TR * ZC && z_col[q] < rank;
+    const int zr = e / ZC, zc = e % ZC;
+    const bool ok = e < TR * ZC && zc < rank;
+    z_gbase[q] = ok ? (uint32_t)(zr * rank + zc) * 4u : kOutside;
+    zs_off[q] = ok ? zr * ZW + zc : TR * ZW;
+    zt_off[q] = ok && zr < 32 ? zc * kGRow + zr : ZC * kGRow;
   }
   // NSET register sets: tile i+NSET is loaded while tile i is computed
   uint4 vpre[NSET][kVL];
@@ -228,32 +235,20 @@ k_bwd_lr(Params P) {
   const auto rx = make_rsrc(P.x, (uint32_t)(s.BT * s.D * 2)), rdy = make_rsrc(P.dy, (uint32_t)(s.BT * s.D * 2));
   const auto rz = make_rsrc(P.z, (uint32_t)(s.BT * rank * 4));
   auto prefetch = [&](int set, int tile) {
-    const int t0 = tile * 32;
+    const uint32_t vstep = (uint32_t)(tile * 32 * D) * 2u, zstep = (uint32_t)(tile * 32 * rank) * 4u;
 #pragma unroll
-    for (int q = 0; q < kVL; ++q) {
-      const int row = t0 + v_row[q];
-      const uint32_t off = (v_ok[q] && row >= 0 && row < BT) ? (uint32_t)(row * D + v_goff[q]) * 2u : kOutside;
-      vpre[set][q] = buf_load16(v_isx[q] ? rx : rdy, off);
-    }
+    for (int q = 0; q < kVL; ++q) vpre[set][q] = buf_load16(v_isx[q] ? rx : rdy, v_gbase[q] + vstep);
 #pragma unroll
-    for (int q = 0; q < kZL; ++q) {
-      const int row = t0 + z_row[q];
-      const uint32_t off = (z_ok[q] && row < BT) ? (uint32_t)(row * rank + z_col[q]) * 4u : kOutside;
-      zpre[set][q] = buf_load_f32(rz, off);
-    }
+    for (int q = 0; q < kZL; ++q) zpre[set][q] = buf_load_f32(rz, z_gbase[q] + zstep);
   };
   auto stage = [&](int set) {
 #pragma unroll
-    for (int q = 0; q < kVL; ++q)
-      if (v_in[q])
-        *reinterpret_cast<uint4 *>((v_isx[q] ? xs : dys) + v_loff[q]) = vpre[set][q];
+    for (int q = 0; q < kVL; ++q) *reinterpret_cast<uint4 *>((v_isx[q] ? xs : dys) + v_loff[q]) = vpre[set][q];
 #pragma unroll
     for (int q = 0; q < kZL; ++q) {
-      if (z_ok[q]) {
-        const bf16 v = (bf16)zpre[set][q];
-        zs[z_row[q] * ZW + z_col[q]] = v;
-        if (z_row[q] < 32) zt[z_col[q] * kGRow + z_row[q]] = v;
-      }
+      const bf16 v = (bf16)zpre[set][q];
+      zs[zs_off[q]] = v;
+      zt[zt_off[q]] = v;
     }
   };
 
@@ -262,6 +257,23 @@ k_bwd_lr(Params P) {
   const auto rdx = make_rsrc(P.dx, (uint32_t)(s.BT * s.D * 2));
   const auto rg = make_rsrc(P.gpart + (int64_t)blockIdx.x * s.BT * rank, (uint32_t)(s.BT * rank * 4));
   const uint32_t ones = 0x3f803f80u;     // bf16 pair (1, 1)
+  // store offsets at tile 0 (the range checks of rdx / rg drop rows past BT
+  // and masked slots): dx of the lane's token n, channels cw+4g .. +3; the dz
+  // partial of thread -> (q, token), token fastest (consecutive threads read
+  // consecutive lanes' rows of the exchange buffer)
+  const uint32_t dx_base = cw + 4 * g + 4 <= s.D ? (uint32_t)(n * D + (int)cw + 4 * g) * 2u : kOutside;
+  constexpr int NIT = (32 * ZC + NT - 1) / NT;
+  uint32_t dz_base[NIT];
+  int dz_src[NIT];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int o = tid + it * NT;
+    const int sr = o % 32, q = o / 32;
+    const bool ok = o < 32 * ZC && q < rank;
+    const int tb = sr >> 4, nn = sr & 15, mq = q >> 4, gg = (q >> 2) & 3, r = q & 3;
+    dz_src[it] = ok ? (16 * gg + nn) * RVP + (tb * NQ + mq) * 4 + r : 0;
+    dz_base[it] = ok ? (uint32_t)(sr * rank + q) * 4u : kOutside;
+  }
   const int wc = wave * kCW + 4 * g;     // the lane's first channel within the tile rows
   unsigned char *gtw = gt[wave];
   // G writes: token row 16tb + n, channel quad g; transposed reads for the
@@ -400,8 +412,7 @@ k_bwd_lr(Params P) {
     // lanes write outside the buffer, which drops them)
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-      const int64_t t = t0 + 16 * tb + n;
-      const uint32_t off = (t < s.BT && cw + 4 * g + 4 <= s.D) ? (uint32_t)(t * s.D + cw + 4 * g) * 2u : kOutside;
+      const uint32_t off = dx_base + (uint32_t)(((int)t0 + 16 * tb) * D) * 2u;
       buf_store8(rdx, off, make_uint2(pack2(dxacc[tb][0], dxacc[tb][1]), pack2(dxacc[tb][2], dxacc[tb][3])));
     }
     // dz partial of the wave: element (tb*NQ + mq)*4 + r = dz[t0 + 16tb + n][16mq + 4g + r]
@@ -415,17 +426,11 @@ k_bwd_lr(Params P) {
     // the waves' sum, one partial per (slice, token): thread -> (q, token),
     // token fastest (consecutive threads read consecutive lanes' rows)
 #pragma unroll
-    for (int it = 0; it < (32 * ZC + NT - 1) / NT; ++it) {
-      const int o = tid + it * NT;
-      const int sr = o % 32, q = o / 32;
-      const int64_t row = t0 + sr;
-      const bool ok = o < 32 * ZC && q < rank && row < s.BT;
-      const int tb = sr >> 4, nn = sr & 15, mq = q >> 4, gg = (q >> 2) & 3, r = q & 3;
-      const int src = ok ? (16 * gg + nn) * RVP + (tb * NQ + mq) * 4 + r : 0;
-      float v = red[0][src];
+    for (int it = 0; it < NIT; ++it) {
+      float v = red[0][dz_src[it]];
 #pragma unroll
-      for (int w = 1; w < kW; ++w) v += red[w][src];
-      buf_store_f32(rg, ok ? (uint32_t)(row * rank + q) * 4u : kOutside, v);
+      for (int w = 1; w < kW; ++w) v += red[w][dz_src[it]];
+      buf_store_f32(rg, dz_base[it] + (uint32_t)((int)t0 * rank) * 4u, v);
     }
   };
   // unrolled by two so that each register set has fixed registers
