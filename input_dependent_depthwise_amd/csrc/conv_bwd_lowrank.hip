@@ -192,9 +192,11 @@ k_bwd_lr(Params P) {
   // Each thread's load slots are fixed for the block: precompute their byte
   // offset at tile 0 and their LDS destination once.  Per tile the offset only
   // advances; the buffer's range check returns zeros for every slot whose
-  // offset falls outside the tensor: rows before 0 (the offset wraps to a huge
-  // value), rows past BT, and masked slots (offset kOutside + tile advance,
-  // still above the tensor, which is under 2 GiB).
+  // offset falls outside the tensor: rows before 0 (the offset wraps to the
+  // top of the 32-bit range; clamped to kTop so that the offset plus the
+  // access size never wraps past 2^32), rows past BT, and masked slots
+  // (offset kOutside + tile advance, still above the tensor, which is under
+  // 2 GiB).
   const int tile_lo = blockIdx.y * P.tpb;
   const int tile_hi = min(P.n_tiles, tile_lo + P.tpb);
   const int D = (int)s.D;  // B*T*D < 2^31 (host-checked)
@@ -236,8 +238,9 @@ k_bwd_lr(Params P) {
   const auto rz = make_rsrc(P.z, (uint32_t)(s.BT * rank * 4));
   auto prefetch = [&](int set, int tile) {
     const uint32_t vstep = (uint32_t)(tile * 32 * D) * 2u, zstep = (uint32_t)(tile * 32 * rank) * 4u;
+    constexpr uint32_t kTop = 0xffffff00u;
 #pragma unroll
-    for (int q = 0; q < kVL; ++q) vpre[set][q] = buf_load16(v_isx[q] ? rx : rdy, v_gbase[q] + vstep);
+    for (int q = 0; q < kVL; ++q) vpre[set][q] = buf_load16(v_isx[q] ? rx : rdy, min(v_gbase[q] + vstep, kTop));
 #pragma unroll
     for (int q = 0; q < kZL; ++q) zpre[set][q] = buf_load_f32(rz, z_gbase[q] + zstep);
   };

@@ -103,27 +103,38 @@ k_fwd_lowrank(Shape s, const float *__restrict__ z, const bf16 *__restrict__ U, 
     }
   }
 
-  // per-thread load slots (fixed for the block)
-  int v_row[kVLoads], v_col[kVLoads], v_loff[kVLoads];
-  bool v_ok[kVLoads];
+  // per-thread load slots (fixed for the block): byte offset at tile 0 and
+  // LDS destination.  Per tile the offset advances by the tile's rows; the
+  // buffer's range check returns zeros for rows past BT and masked slots
+  // (kOutside + advance), and rows before 0 (tile 0's history rows) wrap to
+  // the top of the 32-bit range, clamped below 2^32 - 256 so that offset +
+  // access size never wraps.  Tiles past the block's range (the second of a
+  // pair, the loads two ahead) load whatever their offsets reach: their
+  // results are never stored.
+  uint32_t v_gbase[kVLoads];
+  int v_loff[kVLoads];
 #pragma unroll
   for (int q = 0; q < kVLoads; ++q) {
     const int e = tid + q * 256;
     const int r = e / CH, c16 = e % CH;
-    v_ok[q] = r < 32 + KH && c16 * 8 < nch;
-    v_row[q] = r - KH;
-    v_col[q] = cblk + c16 * 8;
+    const bool ok = r < 32 + KH && c16 * 8 < nch;
+    v_gbase[q] = ok ? (uint32_t)((r - KH) * D + cblk + c16 * 8) * 2u : kOutside;
     v_loff[q] = r * kRowB + c16 * 16;
   }
-  int s_tt[kSLoads], s_q[kSLoads], s_loff[kSLoads];
-  bool s_ok[kSLoads];
+  // y store offset at tile 0 of the lane's token and 8 channels, per group
+  uint32_t y_base[kCPW];
+#pragma unroll
+  for (int g = 0; g < kCPW; ++g)
+    y_base[g] = glive[g] ? (uint32_t)(tl * D + cblk + (wave * kCPW + g) * 16 + hh * 8) * 2u : kOutside;
+  uint32_t s_gbase[kSLoads];
+  int s_loff[kSLoads];
 #pragma unroll
   for (int q = 0; q < kSLoads; ++q) {
     const int e = tid + q * 256;
-    s_tt[q] = e / ZW;
-    s_q[q] = e % ZW;
-    s_ok[q] = s_tt[q] < 32 && s_q[q] < rank;
-    s_loff[q] = s_ok[q] ? s_tt[q] * ZWP + s_q[q] : 32 * ZWP;  // unused slots write the spare element
+    const int tt = e / ZW, sq = e % ZW;
+    const bool ok = tt < 32 && sq < rank;
+    s_gbase[q] = ok ? (uint32_t)(tt * rank + sq) * 4u : kOutside;
+    s_loff[q] = ok ? tt * ZWP + sq : 32 * ZWP;  // unused slots write the spare element
   }
   const auto rx = make_rsrc(x, (uint32_t)(BT * D * 2));
   const auto rz = make_rsrc(z, (uint32_t)(BT * rank * 4));
@@ -131,20 +142,14 @@ k_fwd_lowrank(Shape s, const float *__restrict__ z, const bf16 *__restrict__ U, 
   uint4 vpre[2][kVLoads];
   float spre[2][kSLoads];
   auto prefetch = [&](int set, int tile) {
-    const int t0 = tile * 32;
     const bool tin = tile < tile_hi;
+    const uint32_t vstep = tin ? (uint32_t)(tile * 32 * D) * 2u : kOutside;
+    const uint32_t zstep = tin ? (uint32_t)(tile * 32 * rank) * 4u : kOutside;
+    constexpr uint32_t kTop = 0xffffff00u;
 #pragma unroll
-    for (int q = 0; q < kVLoads; ++q) {
-      const int row = t0 + v_row[q];
-      const uint32_t off = (tin && v_ok[q] && row >= 0 && row < BT) ? (uint32_t)(row * D + v_col[q]) * 2u : kOutside;
-      vpre[set][q] = buf_load16(rx, off);
-    }
+    for (int q = 0; q < kVLoads; ++q) vpre[set][q] = buf_load16(rx, min(v_gbase[q] + vstep, kTop));
 #pragma unroll
-    for (int q = 0; q < kSLoads; ++q) {
-      const int row = t0 + s_tt[q];
-      const uint32_t off = (tin && s_ok[q] && row < BT) ? (uint32_t)(row * rank + s_q[q]) * 4u : kOutside;
-      spre[set][q] = buf_load_f32(rz, off);
-    }
+    for (int q = 0; q < kSLoads; ++q) spre[set][q] = buf_load_f32(rz, min(s_gbase[q] + zstep, kTop));
   };
 
   auto step = [&](const int set, const int tile) {
@@ -157,7 +162,10 @@ k_fwd_lowrank(Shape s, const float *__restrict__ z, const bf16 *__restrict__ U, 
     prefetch(set, tile + 2);
 
     const int t = tile * 32 + tl;
-    const bool tv = tile < tile_hi && t < BT;
+    // y of this tile: rows past BT fall outside ry; tiles past the block's
+    // range store nothing
+    const bool tin = tile < tile_hi;
+    const uint32_t ystep = (uint32_t)(tile * 32 * D) * 2u;
     const int pos = (int)((uint32_t)t % (uint32_t)s.T);
     bf16x8 bz[KQ];
 #pragma unroll
@@ -198,8 +206,7 @@ k_fwd_lowrank(Shape s, const float *__restrict__ z, const bf16 *__restrict__ U, 
       for (int i = 0; i < 4; ++i)
         w[i] = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)out[2 * i]) |
                ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)out[2 * i + 1]) << 16);
-      const uint32_t off = (tv && glive[g]) ? (uint32_t)(t * D + cblk + cl) * 2u : kOutside;
-      buf_store16(ry, off, make_uint4(w[0], w[1], w[2], w[3]));
+      buf_store16(ry, tin ? y_base[g] + ystep : kOutside, make_uint4(w[0], w[1], w[2], w[3]));
     }
   };
 
