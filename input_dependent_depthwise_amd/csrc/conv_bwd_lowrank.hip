@@ -285,14 +285,22 @@ k_bwd_lr(Params P) {
   const int gw_off[2] = {g_off(n, g), g_off(16 + n, g)};
   const int gr_off[2] = {g_off(8 * g + n / 4, n % 4), g_off(8 * g + 4 + n / 4, n % 4)};
 
+  // position in its sequence of the current tile's first token (wave-uniform,
+  // advanced by one tile per step)
+  const int T = s.T;
+  int p0 = (int)((uint32_t)(tile_lo * 32) % (uint32_t)T);
   auto tile_step = [&](const int set, const int tile) {
     const int64_t t0 = (int64_t)tile * 32;
-    int pos[2];
+    // only tiles that hold a token with pos < KH (x before its sequence start)
+    // or pos > T-1-KH (dy past its sequence end) need the per-token masks
+    const bool edge_lo = KH > 0 && (p0 < KH || T - p0 <= 31);
+    const bool edge_hi = KH > 0 && T - KH - p0 <= 31;
+    int pos[2] = {0, 0};
+    if (edge_lo || edge_hi) {
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) pos[tb] = (int)((uint32_t)(t0 + 16 * tb + n) % (uint32_t)s.T);  // B*T < 2^31
-    // only waves that hold a sequence start / end need the masks
-    const bool edge_lo = __any(KH > 0 && (pos[0] < KH || pos[1] < KH));
-    const bool edge_hi = __any(KH > 0 && (pos[0] + KH > s.T - 1 || pos[1] + KH > s.T - 1));
+      for (int tb = 0; tb < 2; ++tb) pos[tb] = (int)((uint32_t)(p0 + 16 * tb + n) % (uint32_t)T);
+    }
+    p0 = T >= 32 ? (p0 + 32 >= T ? p0 + 32 - T : p0 + 32) : (p0 + 32) % T;
 
     __syncthreads();  // the previous tile's LDS reads are done
     stage(set);
@@ -345,7 +353,7 @@ k_bwd_lr(Params P) {
         } else {
           const uint2 d = *reinterpret_cast<const uint2 *>(&dys[(16 * tb + n + j) * kRow + wc]);
           w[0] = d.x, w[1] = d.y;
-          if (__builtin_expect(edge_hi, 0) && pos[tb] + j > s.T - 1) w[0] = 0u, w[1] = 0u;
+          if (__builtin_expect(edge_hi, 0) && pos[tb] + j > T - 1) w[0] = 0u, w[1] = 0u;
         }
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
