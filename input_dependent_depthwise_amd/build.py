@@ -29,11 +29,18 @@ CFLAGS = [
     # keep the compiler from emitting packed fp32 VALU ops (v_pk_fma_f32 and kin)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+# Per-file additions.  The low-rank forward consumes each matrix-core result
+# on the VALU once: with the results in VGPRs (this target's MFMAs write them
+# directly) it needs no v_accvgpr_read copy per element.  Kernels that keep
+# accumulating in the matrix cores are better off with AGPR accumulators.
+FILE_FLAGS = {
+    "conv_fwd_lowrank.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the packed-fp32 feature and says so; that line is harmless
     noise = "'-packed-fp32-ops' is not a recognized feature"
