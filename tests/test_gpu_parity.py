@@ -162,3 +162,52 @@ def test_empty_batch():
     torch.cuda.synchronize()
     for k in ("dA", "dU", "dw0"):
         assert torch.count_nonzero(g[k]).item() == 0, k
+
+
+@pytest.mark.parametrize("kind", ["lowrank", "headwise"])
+def test_near_size_limit_per_sequence(kind):
+    """Tensors just under the 2 GiB limit of the fused kernels' 32-bit byte
+    offsets.  The oracle cannot run at this size; a property that holds at any
+    size stands in: a sequence's y, dx and dh depend only on that sequence
+    (tiles are aligned to sequence starts and every reduction has a fixed
+    order), so the last sequences of the big batch, where the offsets are
+    largest, must equal bitwise a run of those sequences alone.  (The wide
+    projection picks its K split by row count, so the tail is large enough,
+    32768 rows, to take the same one as the full batch.)"""
+    import input_dependent_depthwise_amd as dc
+    T, k = 2048, 4
+    if kind == "lowrank":
+        d, D, rank, n_heads = 768, 2304, 16, 0
+    else:
+        d, D, rank, n_heads = 512, 3072, 0, 24
+    B = ((1 << 31) - 64 - 1) // (T * D * 2)  # largest batch with B*T*D*2 below the limit
+    assert B * T * D * 2 < (1 << 31) - 64
+    _note(f"[limit] {kind} B={B} T={T} d={d} D={D} bytes per tensor={B * T * D * 2}")
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    bf = torch.bfloat16
+    h = torch.randn(B, T, d, device="cuda", generator=gen).to(bf)
+    x = torch.randn(B, T, D, device="cuda", generator=gen).to(bf)
+    dy = torch.randn(B, T, D, device="cuda", generator=gen).to(bf)
+    w0 = (0.1 * torch.randn(D, k, device="cuda", generator=gen)).to(bf)
+    if kind == "lowrank":
+        wk = dict(A=(0.02 * torch.randn(d, rank, device="cuda", generator=gen)).to(bf),
+                  U=(0.02 * torch.randn(rank, D * k, device="cuda", generator=gen)).to(bf))
+    else:
+        wk = dict(W=(0.02 * torch.randn(d, n_heads * k, device="cuda", generator=gen)).to(bf), n_heads=n_heads)
+
+    def run(hh, xx, dd):
+        y, cache = dc.dynconv_fwd(hh, xx, k=k, w0=w0, want_cache=True, **wk)
+        g = dc.dynconv_bwd(hh, xx, dd, k=k, w0=w0, gen_cache=cache, need_dh=True, need_dw0=True, **wk)
+        torch.cuda.synchronize()
+        return y, g["dx"], g["dh"]
+
+    tail = 16
+    big = run(h, x, dy)
+    big = [t[B - tail:].clone() for t in big]
+    torch.cuda.empty_cache()
+    small = run(h[B - tail:].contiguous(), x[B - tail:].contiguous(), dy[B - tail:].contiguous())
+    for name, a, b in zip(("y", "dx", "dh"), big, small):
+        assert torch.isfinite(a.float()).all(), name
+        assert torch.equal(a, b), f"{kind} {name}: the last sequences differ from a run of them alone"
+    del h, x, dy, big, small
+    torch.cuda.empty_cache()
