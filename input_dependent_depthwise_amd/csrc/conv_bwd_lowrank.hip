@@ -57,13 +57,6 @@ constexpr int kGTap = 32 * 32 + 4 * 128;
 __device__ __forceinline__ int g_off(int t, int quad) {
   return 32 * t + 128 * (t >> 3) + 8 * (quad ^ (2 * ((t >> 3) & 1)));
 }
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-// four bf16 of one channel from four token rows (lane l%16 = channel)
-__device__ __forceinline__ uint2 read_tr16(const unsigned char *p) {
-  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p));
-  return __builtin_bit_cast(uint2, v);
-}
 
 struct Params {
   Shape s;

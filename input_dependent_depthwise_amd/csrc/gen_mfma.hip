@@ -242,6 +242,158 @@ k_gen_proj_ksplit(const bf16 *__restrict__ h, const bf16 *__restrict__ Mt, float
     }
 }
 
+// Narrow weights with N a multiple of 8 whose whole (row-padded) copy fits
+// in 64 KB of LDS: as k_gen_proj_ksplit, but each block first stages the
+// weight itself in LDS, rows k as given (Np columns, zeros past N), and every
+// B fragment is two transposed LDS reads (read_tr16: four k of one column
+// per read), so no transposed copy and no prep kernel are needed.  Bank
+// spread: with 16 columns, the 128-byte blocks of four rows are stored at
+// position b ^ ((b >> 1) & 1); with 32, the two 32-byte halves of row k at
+// half h ^ ((k >> 3) & 1).  Either way the two token groups of a 32-lane
+// pass (8 rows apart) read disjoint banks.
+constexpr size_t kNarrowLds = 48 * 1024;  // staged weight (the K-quarter sums take 12 KB more)
+template <int NT>
+__device__ __forceinline__ int wrow_off(int k, int half) {
+  if constexpr (NT == 1) {
+    const int b = k >> 2;
+    return ((b ^ ((b >> 1) & 1)) << 7) + ((k & 3) << 5) + half * 16;
+  } else {
+    return (k << 6) + (((half >> 1) ^ ((k >> 3) & 1)) << 5) + (half & 1) * 16;
+  }
+}
+
+template <int NT>
+__global__ void __launch_bounds__(256)
+k_gen_proj_narrow(const bf16 *__restrict__ h, const bf16 *__restrict__ Mw, float *__restrict__ out,
+                  int64_t M, int K, int Kp, int N) {
+  constexpr int KS = 4, U = 4;
+  constexpr int CPR = NT * 2;  // 16-byte chunks per staged row
+  extern __shared__ __attribute__((aligned(16))) unsigned char wl[];  // Kp rows x 32*NT bytes
+  const int lane = threadIdx.x & 63, ks = threadIdx.x >> 6;
+  const int lr = lane & 15, lk = (lane >> 4) * 8;
+  const int64_t rbase = (int64_t)blockIdx.x * 32;
+
+  const int64_t ra = rbase + lr < M ? rbase + lr : M - 1;  // rows >= M are never stored
+  const int64_t rb = rbase + 16 + lr < M ? rbase + 16 + lr : M - 1;
+  const bf16 *ha = h + ra * K + lk;
+  const bf16 *hb = h + rb * K + lk;
+  const int steps = Kp / 32, full = K / 32;
+  const int per = (steps + KS - 1) / KS;
+  const int s0 = ks * per, s1 = min(steps, s0 + per);
+  const int s1f = min(s1, full);  // steps whose 32 k all lie below K
+  bf16x8 a0[U], a1[U];
+  auto load_a = [&](int st) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k = (st + u) * 32;
+      a0[u] = as_bf16x8(*reinterpret_cast<const uint4 *>(ha + k));
+      a1[u] = as_bf16x8(*reinterpret_cast<const uint4 *>(hb + k));
+    }
+  };
+  // the first h fragments, and those of the tail (the fewer than U steps
+  // after the full groups, the last one possibly partial), are in flight
+  // while the weight is staged
+  int s = s0;
+  if (s + U <= s1f) load_a(s);
+  const int sg = s0 + max(0, s1f - s0) / U * U;  // first tail step
+  bf16x8 t0[U], t1[U];
+#pragma unroll
+  for (int q = 0; q < U; ++q) {
+    const int k = (sg + q) * 32;
+    t0[q] = t1[q] = zero_bf16x8();
+    if (sg + q < s1 && k + lk < K) {  // K is a multiple of 8: a fragment is all-in or all-out
+      t0[q] = as_bf16x8(*reinterpret_cast<const uint4 *>(ha + k));
+      t1[q] = as_bf16x8(*reinterpret_cast<const uint4 *>(hb + k));
+    }
+  }
+
+  // stage the weight: chunk e -> row k = e / CPR, 8 columns 8c .. 8c+7
+  // (rows past K and columns past N read zeros from outside the buffer)
+  {
+    const auto rw = make_rsrc(Mw, (uint32_t)((int64_t)K * N * 2));
+    const int nch = Kp * CPR;
+    for (int e = threadIdx.x; e < nch; e += 256) {
+      const int k = e / CPR, c = e - k * CPR;
+      const uint32_t off = 8 * c < N ? (uint32_t)(k * N + 8 * c) * 2u : kOutside;
+      *reinterpret_cast<uint4 *>(wl + wrow_off<NT>(k, c)) = buf_load16(rw, off);
+    }
+  }
+  __syncthreads();
+
+  // B fragment (K-step at k, column tile n): lane lr of token group g reads
+  // row k + 8g + 4q + lr/4 (q = 0, 1), columns 16n + 4(lr%4) .. +3, i.e.
+  // chunk 2n + (lr%4)/2 of the row, byte 8(lr%2) of it; it receives
+  // B[k + 8g + i][16n + lr], i = 4q .. 4q+3
+  auto bfrag = [&](int k, int n) -> bf16x8 {
+    const int r0 = k + lk + (lr >> 2), c = 2 * n + ((lr & 3) >> 1), b8 = (lr & 1) * 8;
+    const uint2 lo = read_tr16(wl + wrow_off<NT>(r0, c) + b8);
+    const uint2 hi = read_tr16(wl + wrow_off<NT>(r0 + 4, c) + b8);
+    return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+  };
+
+  f32x4 acc[2][NT];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[r][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // groups of U K-steps; the next group's h loads are issued behind the
+  // current group's MFMAs
+  for (; s + U <= s1f; s += U) {
+    bf16x8 b[U][NT];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) b[u][n] = bfrag((s + u) * 32, n);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        acc[0][n] = mfma16(a0[u], b[u][n], acc[0][n]);
+        acc[1][n] = mfma16(a1[u], b[u][n], acc[1][n]);
+      }
+    if (s + 2 * U <= s1f) load_a(s + U);
+  }
+#pragma unroll
+  for (int q = 0; q < U; ++q) {
+    if (sg + q >= s1) break;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const bf16x8 b = bfrag((sg + q) * 32, n);
+      acc[0][n] = mfma16(t0[q], b, acc[0][n]);
+      acc[1][n] = mfma16(t1[q], b, acc[1][n]);
+    }
+  }
+
+  __shared__ f32x4 red[KS - 1][2][NT][64];
+  if (ks > 0) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) red[ks - 1][r][n][lane] = acc[r][n];
+  }
+  __syncthreads();
+  if (ks > 0) return;
+#pragma unroll
+  for (int q = 0; q < KS - 1; ++q)
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[r][n] += red[q][r][n][lane];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const int col = n * 16 + lr;
+      if (col >= N) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t row = rbase + r * 16 + (lane >> 4) * 4 + i;
+        if (row < M) out[row * N + col] = acc[r][n][i];
+      }
+    }
+}
+
 template <int NT>
 void launch_nt(const bf16 *h, const bf16 *Mt, float *out, int64_t M, int K, int Kp, int N,
                hipStream_t st) {
@@ -273,10 +425,22 @@ int gen_proj_mfma(const Shape &s, const void *h, const void *M, float *out, void
   const int N = s.N, K = (int)s.d;
   const int Np = (int)ceil_div(N, 16) * 16;
   const int Kp = (int)ceil_div(K, 32) * 32;
+  const bf16 *hh = (const bf16 *)h;
+  // narrow weights that fit in LDS: staged from the weight itself, no prep kernel
+  if (Np <= 32 && N % 8 == 0 && (size_t)Kp * Np * 2 <= kNarrowLds) {
+    const bool tr = trace_begin(DYNCONV_K_GEN_PROJ, st);
+    const dim3 grid((unsigned)ceil_div(s.BT, 32)), block(256);
+    const size_t lds = (size_t)Kp * Np * 2;
+    if (Np == 16)
+      hipLaunchKernelGGL((k_gen_proj_narrow<1>), grid, block, lds, st, hh, (const bf16 *)M, out, s.BT, K, Kp, N);
+    else
+      hipLaunchKernelGGL((k_gen_proj_narrow<2>), grid, block, lds, st, hh, (const bf16 *)M, out, s.BT, K, Kp, N);
+    trace_end(tr, st);
+    return 0;
+  }
   bf16 *Mt = (bf16 *)ws;
   hipLaunchKernelGGL(k_transpose_pad, dim3((unsigned)ceil_div((int64_t)Np * Kp, 256)), dim3(256), 0, st,
                      (const bf16 *)M, Mt, K, N, Kp, Np);
-  const bf16 *hh = (const bf16 *)h;
   const bool tr = trace_begin(DYNCONV_K_GEN_PROJ, st);
   switch (Np / 16) {
 #define CASE(nt) \

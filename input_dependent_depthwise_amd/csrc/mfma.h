@@ -26,6 +26,18 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8 &a, const bf16x8 &b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// ds_read_b64_tr_b16 (gfx950): in each group of 16 lanes, lane L receives
+// element L%4 of the 8-byte reads of lanes L/4, 4 + L/4, 8 + L/4 and
+// 12 + L/4, in that order.  When lane 4e + c reads row r0 + e at column
+// 4c, lane L gets rows r0 .. r0+3 of column L: four bf16 of one column of a
+// row-major LDS tile.  p is the lane's LDS address.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+__device__ __forceinline__ uint2 read_tr16(const unsigned char *p) {
+  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
 // 16 bytes of bf16 as an MFMA operand.
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4 &r) { return __builtin_bit_cast(bf16x8, r); }
 
