@@ -168,6 +168,60 @@ k_combine(Shape s, const float *__restrict__ gpart, int n_slices, int R, int Dt,
   }
 }
 
+// Low-rank g for rank 16 (Np = R): the same fixed-order sums over more,
+// smaller blocks (rank 32, with 8-token blocks, was slower than k_combine).
+// Block: 64 / (R/4) tokens; lane = token x
+// column quad, so each wave's load of one slice is one contiguous 1 KB run of
+// dz rows; wave w sums its quarter of the slices (ascending), and wave 0
+// adds the four quarters in order.  g and g^T (zeros past BT) are written
+// straight from registers.
+__global__ void __launch_bounds__(256)
+k_combine_lr(const float *__restrict__ gpart, int64_t BT, int R, int n_slices, int64_t BTp,
+             bf16 *__restrict__ g, bf16 *__restrict__ gT) {
+  __shared__ float4 part[3][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int Q = R / 4, tpw = 64 / Q;  // column quads per token, tokens per block
+  const int64_t t = (int64_t)blockIdx.x * tpw + lane / Q;
+  const int n0 = (lane % Q) * 4;
+  const bool live = t < BT;
+  const int d0 = w * n_slices / 4, d1 = (w + 1) * n_slices / 4;
+  const int64_t stride = BT * R;
+  const float *src = gpart + (live ? t : 0) * R + n0;
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (live) {
+    int d = d0;
+    for (; d + 4 <= d1; d += 4) {
+      float4 a[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) a[u] = *reinterpret_cast<const float4 *>(src + (d + u) * stride);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v.x += a[u].x, v.y += a[u].y, v.z += a[u].z, v.w += a[u].w;
+    }
+    for (; d < d1; ++d) {
+      const float4 a = *reinterpret_cast<const float4 *>(src + d * stride);
+      v.x += a.x, v.y += a.y, v.z += a.z, v.w += a.w;
+    }
+  }
+  if (w > 0) part[w - 1][lane] = v;
+  __syncthreads();
+  if (w > 0) return;
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    const float4 a = part[q][lane];
+    v.x += a.x, v.y += a.y, v.z += a.z, v.w += a.w;
+  }
+  const bf16 o[4] = {(bf16)v.x, (bf16)v.y, (bf16)v.z, (bf16)v.w};
+  if (live) {
+    const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, o[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, o[1]) << 16);
+    const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, o[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, o[3]) << 16);
+    *reinterpret_cast<uint2 *>(g + t * R + n0) = make_uint2(lo, hi);
+  }
+  if (t < BTp) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) gT[(int64_t)(n0 + c) * BTp + t] = o[c];
+  }
+}
+
 // Mp[i, n] = M[i, n] zero-padded to Np columns (bf16).
 __global__ void __launch_bounds__(256)
 k_pad_cols(const bf16 *__restrict__ M, bf16 *__restrict__ Mp, int64_t rows, int N, int Np) {
@@ -548,7 +602,10 @@ int gen_bwd(const Shape &s, const float *gpart, int n_slices, int R, int Dt, con
   bf16 *gT = (bf16 *)((char *)g + g_rows_bytes(s, L));
   const int span = s.kind == DYNCONV_HEADWISE ? combine_span(s, Dt) : 0;
   if (span > gbwd::kMaxSpan) return DYNCONV_E_LIMIT;
-  if (L.Np <= 32) {
+  if (s.kind == DYNCONV_LOWRANK && R == 16 && L.Np == R) {
+    hipLaunchKernelGGL(gbwd::k_combine_lr, dim3((unsigned)(L.BTp / (256 / R))), dim3(256), 0, st, gpart, s.BT,
+                       R, n_slices, L.BTp, g, gT);
+  } else if (L.Np <= 32) {
     const int cw = L.Np;  // 16 or 32
     const dim3 grid((unsigned)ceil_div(L.BTp, 2048 / cw));
     if (cw == 16)
