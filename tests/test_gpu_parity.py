@@ -6,7 +6,8 @@ Covers the five workloads at their full sizes (the launch configuration the
 benchmark times), shapes that span several tiles with ragged tails, and the
 degenerate cases (T = 1, T < k, k = 1, heads narrower than a vector, rank 1,
 no bias).  Bitwise invariants: zero filter gives y == x and dx == dy,
-causality, determinism, cache reuse == recompute.
+causality, determinism, cache reuse == recompute, the autograd wrapper ==
+the direct calls.
 """
 from __future__ import annotations
 
@@ -16,6 +17,7 @@ import numpy as np
 import pytest
 import torch
 
+import input_dependent_depthwise_amd as dc
 import workloads
 from tests import gpu_util as gu
 from workloads import HEADWISE, LOWRANK, WORKLOADS, Workload
@@ -162,6 +164,27 @@ def test_empty_batch():
     torch.cuda.synchronize()
     for k in ("dA", "dU", "dw0"):
         assert torch.count_nonzero(g[k]).item() == 0, k
+
+
+@pytest.mark.parametrize("w", [SMALL[0], SMALL[7]], ids=["hw", "lr"])
+def test_autograd_wrapper(w):
+    """DynConvFn gives the direct calls' results bitwise: y, dx, dh, and the
+    weight gradients cast to the weights' dtype."""
+    _note(f"[autograd] {w.name}")
+    dev = gu.to_dev(workloads.generate(w))
+    ref = gu.gpu_run(w, dev)
+    leaves = {k: (None if dev.get(k) is None else dev[k].clone().requires_grad_(True))
+              for k in ("h", "x", "W", "A", "U", "w0")}
+    y = dc.DynConvFn.apply(leaves["h"], leaves["x"], leaves["W"], leaves["A"], leaves["U"], leaves["w0"],
+                           w.k, w.n_heads)
+    y.backward(dev["dy"])
+    torch.cuda.synchronize()
+    assert torch.equal(y.detach(), ref["y"])
+    assert torch.equal(leaves["x"].grad, ref["dx"])
+    assert torch.equal(leaves["h"].grad, ref["dh"])
+    for key, gkey in (("W", "dW"), ("A", "dA"), ("U", "dU"), ("w0", "dw0")):
+        if leaves[key] is not None:
+            assert torch.equal(leaves[key].grad, ref[gkey].to(leaves[key].dtype)), key
 
 
 @pytest.mark.parametrize("kind", ["lowrank", "headwise"])
