@@ -10,13 +10,15 @@
 // Kernels:
 //   k_combine  g = fixed-order sum of the conv kernel's per-slice partials,
 //              written as bf16 (the MFMA operand precision) twice: g [BT, Np]
-//              for dh and g^T [Np, BTp] (token-contiguous) for dM;
+//              for dh and g^T [Np, BTp] (token-contiguous) for dM
+//              (k_combine_lr: the same for rank 16 on finer blocks);
 //   k_dh       dh^T tiles = M . g^T on v_mfma_f32_32x32x16_bf16; a block holds
 //              256 rows of M in registers and walks a token range with the g
 //              tiles staged in LDS, writing dh rows through LDS;
 //   k_dM       per (128-row chunk of d, token range) partials of h^T g on
 //              v_mfma_f32_16x16x32_bf16, h staged in LDS, g^T tiles as loaded;
 //              the row chunks of one token range share an XCD (and its L2);
+//   k_dh_dM    both in one launch for weights up to 128 columns;
 //   k_finalize fixed-order sums of all weight-gradient partials (dU, dw0, dM).
 #include "kernels.h"
 #include "bufio.h"
@@ -248,18 +250,20 @@ constexpr int kOP = 36;  // dh staging tile row (one token): 32 rows of d + pad,
 // [32 tokens][Np] in LDS (double-buffered, one barrier per tile; loaded two
 // tiles ahead in two register sets), and a wave writes its dh tile through a
 // private LDS tile so that every store is a whole 64-byte row segment.
+// LDS of one dh block (bf16 elements): two g tiles, eight per-wave output tiles
 template <int KS>
-__global__ void __launch_bounds__(512)
-k_dh(const bf16 *__restrict__ g, const bf16 *__restrict__ Mp, bf16 *__restrict__ dh, int64_t BT, int d,
-     int Mcols, int n_rb, int n_tr, int tpr, int n_tiles, int slots) {
+constexpr int dh_lds_elems() { return 2 * 32 * (KS * 16 + 8) + 8 * 32 * kOP; }
+
+template <int KS>
+__device__ __forceinline__ void dh_body(const bf16 *__restrict__ g, const bf16 *__restrict__ Mp,
+                                        bf16 *__restrict__ dh, int64_t BT, int d, int Mcols, int n_rb, int n_tr,
+                                        int tpr, int n_tiles, const int q, bf16 *lds) {
   constexpr int NP = KS * 16;
   constexpr int GP = NP + 8;            // LDS row of the g tile (one token), bf16
   constexpr int CH = 4 * NP;            // 16-byte pieces of a g tile
   constexpr int CPT = (CH + 511) / 512;  // per thread
-  constexpr int GR = (CPT * 512 + NP / 8 - 1) / (NP / 8);  // tile rows incl. spare ones for pieces past CH
-  __shared__ __attribute__((aligned(16))) bf16 gs[2][GR * GP];
-  __shared__ __attribute__((aligned(16))) bf16 ot[8][32 * kOP];
-  const int q = xcd_item(slots);
+  bf16 (*gs)[32 * GP] = reinterpret_cast<bf16 (*)[32 * GP]>(lds);
+  bf16 (*ot)[32 * kOP] = reinterpret_cast<bf16 (*)[32 * kOP]>(lds + 2 * 32 * GP);
   if (q >= n_rb * n_tr) return;
   const int tr = q / n_rb, rb = q - tr * n_rb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -298,9 +302,10 @@ k_dh(const bf16 *__restrict__ g, const bf16 *__restrict__ Mp, bf16 *__restrict__
   const uint32_t col_ok = active && i0 + c8 < d;  // d is a multiple of 8
   auto step = [&](int set, int tile) {
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {  // pieces past CH (zeros) land in the spare rows
+    for (int c = 0; c < CPT; ++c) {  // pieces past CH (loaded as zeros) are not stored
       const int e = tid + 512 * c;
-      *reinterpret_cast<uint4 *>(gs[set] + (e / (NP / 8)) * GP + (e % (NP / 8)) * 8) = gr[set][c];
+      if (CH % 512 == 0 || e < CH)
+        *reinterpret_cast<uint4 *>(gs[set] + (e / (NP / 8)) * GP + (e % (NP / 8)) * 8) = gr[set][c];
     }
     __syncthreads();
     load(set, tile + 2);
@@ -352,6 +357,14 @@ k_dh(const bf16 *__restrict__ g, const bf16 *__restrict__ Mp, bf16 *__restrict__
   }
 }
 
+template <int KS>
+__global__ void __launch_bounds__(512)
+k_dh(const bf16 *__restrict__ g, const bf16 *__restrict__ Mp, bf16 *__restrict__ dh, int64_t BT, int d,
+     int Mcols, int n_rb, int n_tr, int tpr, int n_tiles, int slots) {
+  __shared__ __attribute__((aligned(16))) bf16 lds[dh_lds_elems<KS>()];
+  dh_body<KS>(g, Mp, dh, BT, d, Mcols, n_rb, n_tr, tpr, n_tiles, xcd_item(slots), lds);
+}
+
 constexpr int kHP = 132;  // dM h tile row (one token): 128 rows of d + pad, bf16
 constexpr int kGP = 40;   // dM g^T tile row (one column): 32 tokens + pad, bf16
 
@@ -366,20 +379,34 @@ constexpr int kGP = 40;   // dM g^T tile row (one column): 32 tokens + pad, bf16
 // ahead; loads are issued g^T first so that waiting for a tile's g^T leaves
 // the later h tile in flight.  Tiles past the range read as zeros.
 template <int NT>
-__global__ void __launch_bounds__(256, 2)
-k_dM(const bf16 *__restrict__ h, const bf16 *__restrict__ gT, float *__restrict__ dMp, int64_t BT, int64_t BTp,
-     int d, int N, int n_chunks, int n_ranges, int tpb, int n_tiles, int slots) {
+constexpr int dM_lds_elems() { return 2 * 32 * kHP + 2 * NT * 16 * kGP; }
+
+// tiles of item q (q = range * n_chunks + chunk), 0 past the last item
+__device__ __forceinline__ int dM_tiles(int q, int n_chunks, int n_ranges, int tpb, int n_tiles) {
+  if (q >= n_chunks * n_ranges) return 0;
+  const int lo = q / n_chunks * tpb;
+  return min(n_tiles, lo + tpb) - lo;
+}
+
+// One item on 256 threads (tid); the loop takes n_loop tiles (at least the
+// item's own; more when it shares a block's barriers with another item, the
+// extra tiles loading zeros).  An item past the last (q >= n_chunks *
+// n_ranges) loads nothing and stores nothing but meets the barriers.
+template <int NT>
+__device__ __forceinline__ void dM_body(const bf16 *__restrict__ h, const bf16 *__restrict__ gT,
+                                        float *__restrict__ dMp, int64_t BT, int64_t BTp, int d, int N,
+                                        int n_chunks, int n_ranges, int tpb, int n_tiles, const int q, const int tid,
+                                        const int n_loop, bf16 *lds) {
   constexpr int CH = NT * 64;            // 16-byte chunks of a g^T tile
   constexpr int CPT = (CH + 255) / 256;  // per thread
-  constexpr int GR = CPT * 64;           // g^T tile rows incl. spare ones for the pieces past CH
-  __shared__ __attribute__((aligned(16))) bf16 hs[2][32 * kHP];
-  __shared__ __attribute__((aligned(16))) bf16 gs[2][GR * kGP];
-  const int q = xcd_item(slots);
-  if (q >= n_chunks * n_ranges) return;
-  const int range = q / n_chunks, chunk = q - range * n_chunks;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  bf16 (*hs)[32 * kHP] = reinterpret_cast<bf16 (*)[32 * kHP]>(lds);
+  bf16 (*gs)[NT * 16 * kGP] = reinterpret_cast<bf16 (*)[NT * 16 * kGP]>(lds + 2 * 32 * kHP);
+  const bool valid = q < n_chunks * n_ranges;
+  const int qv = valid ? q : 0;
+  const int range = qv / n_chunks, chunk = qv - range * n_chunks;
+  const int lane = tid & 63, wave = tid >> 6;
   const int i0 = chunk * 128;
-  const int tile_lo = range * tpb, ntl = min(n_tiles, tile_lo + tpb) - tile_lo;
+  const int tile_lo = range * tpb, ntl = dM_tiles(q, n_chunks, n_ranges, tpb, n_tiles);
   const int64_t tok_lo = (int64_t)tile_lo * 32;
   const int64_t tok_n = min(BT, tok_lo + (int64_t)ntl * 32) - tok_lo;
   const __amdgpu_buffer_rsrc_t rh = make_rsrc(h + tok_lo * d, (uint32_t)(tok_n * d * 2));
@@ -422,9 +449,9 @@ k_dM(const bf16 *__restrict__ h, const bf16 *__restrict__ gT, float *__restrict_
       dst[1] = make_uint2(hr[set][c].z, hr[set][c].w);
     }
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {  // pieces past CH (zeros) land in the spare rows
+    for (int c = 0; c < CPT; ++c) {  // pieces past CH (loaded as zeros) are not stored
       const int e = tid + 256 * c;
-      *reinterpret_cast<uint4 *>(gs[set] + (e >> 2) * kGP + (e & 3) * 8) = gr[c];
+      if (CH % 256 == 0 || e < CH) *reinterpret_cast<uint4 *>(gs[set] + (e >> 2) * kGP + (e & 3) * 8) = gr[c];
     }
     __syncthreads();
     load_g(tile + 1);
@@ -451,10 +478,11 @@ k_dM(const bf16 *__restrict__ h, const bf16 *__restrict__ gT, float *__restrict_
   load_g(0);
   load_h(0, 0);
   load_h(1, 1);
-  for (int tile = 0; tile < ntl; tile += 2) {
+  for (int tile = 0; tile < n_loop; tile += 2) {
     step(0, tile);
     step(1, tile + 1);
   }
+  if (!valid) return;
   // D fragment: lane holds D[4(lane/16) + r][lane%16] of each 16x16 block
   float *out = dMp + (int64_t)range * d * N;
 #pragma unroll
@@ -467,6 +495,44 @@ k_dM(const bf16 *__restrict__ h, const bf16 *__restrict__ gT, float *__restrict_
         const int col = n * 16 + (lane & 15);
         if (i < d && col < N) out[(int64_t)i * N + col] = acc[r][n][k];
       }
+}
+
+template <int NT>
+__global__ void __launch_bounds__(256, 2)
+k_dM(const bf16 *__restrict__ h, const bf16 *__restrict__ gT, float *__restrict__ dMp, int64_t BT, int64_t BTp,
+     int d, int N, int n_chunks, int n_ranges, int tpb, int n_tiles, int slots) {
+  __shared__ __attribute__((aligned(16))) bf16 lds[dM_lds_elems<NT>()];
+  const int q = xcd_item(slots);
+  if (q >= n_chunks * n_ranges) return;
+  dM_body<NT>(h, gT, dMp, BT, BTp, d, N, n_chunks, n_ranges, tpb, n_tiles, q, threadIdx.x,
+              dM_tiles(q, n_chunks, n_ranges, tpb, n_tiles), lds);
+}
+
+// dh and dM in one launch: dh writes as much as dM reads, and each alone
+// leaves the chip mostly waiting on memory.  Blocks below 8 * dh_slots are
+// dh blocks (512 threads); the others each run two dM items, one per half,
+// which meet the same barriers (both loop over the longer item's tiles).
+// The LDS of the two kinds overlaps.
+template <int KS>
+__global__ void __launch_bounds__(512)
+k_dh_dM(const bf16 *__restrict__ g, const bf16 *__restrict__ Mp, bf16 *__restrict__ dh, const bf16 *__restrict__ h,
+        const bf16 *__restrict__ gT, float *__restrict__ dMp, int64_t BT, int64_t BTp, int d, int Mcols, int N,
+        int n_rb, int n_tr, int tpr, int n_chunks, int n_ranges, int tpb, int n_tiles, int dh_slots, int dm_slots) {
+  constexpr int DH = dh_lds_elems<KS>(), DM = dM_lds_elems<KS>();
+  __shared__ __attribute__((aligned(16))) bf16 lds[DH > 2 * DM ? DH : 2 * DM];
+  const int b = blockIdx.x;
+  if (b < 8 * dh_slots) {
+    dh_body<KS>(g, Mp, dh, BT, d, Mcols, n_rb, n_tr, tpr, n_tiles, (b & 7) * dh_slots + (b >> 3), lds);
+    return;
+  }
+  const int bm = b - 8 * dh_slots;
+  const int pair = (bm & 7) * dm_slots + (bm >> 3);
+  if (2 * pair >= n_chunks * n_ranges) return;  // the whole block
+  const int n_loop = max(dM_tiles(2 * pair, n_chunks, n_ranges, tpb, n_tiles),
+                         dM_tiles(2 * pair + 1, n_chunks, n_ranges, tpb, n_tiles));
+  const int half = threadIdx.x >> 8;
+  dM_body<KS>(h, gT, dMp, BT, BTp, d, N, n_chunks, n_ranges, tpb, n_tiles, 2 * pair + half, threadIdx.x & 255,
+              n_loop, lds + half * DM);
 }
 
 // out[e] = sum_p part[p][e] for e < n, p < np, for up to three independent
@@ -620,6 +686,7 @@ int gen_bwd(const Shape &s, const float *gpart, int n_slices, int R, int Dt, con
                        g, gT);
   }
   const bool tr = trace_begin(DYNCONV_K_GEN_BWD, st);
+  const int dm_items = L.n_chunks * L.n_ranges;
   if (dh) {
     // the weight is read in place when its rows are whole 8-column chunks
     const bool direct = s.N % 8 == 0;
@@ -628,20 +695,38 @@ int gen_bwd(const Shape &s, const float *gpart, int n_slices, int R, int Dt, con
                          (const bf16 *)M, Mp, s.d, s.N, L.Np);
     const bf16 *Ma = direct ? (const bf16 *)M : Mp;
     const int Mcols = direct ? s.N : L.Np;
-    const int slots = (int)ceil_div((int64_t)L.n_rb * L.n_tr, 8);
-    switch (L.Np / 16) {
-#define CASE(ks)                                                                                        \
-  case ks:                                                                                              \
-    hipLaunchKernelGGL(gbwd::k_dh<ks>, dim3((unsigned)(8 * slots)), dim3(512), 0, st, g, Ma, (bf16 *)dh, \
-                       s.BT, (int)s.d, Mcols, L.n_rb, L.n_tr, L.tpr, L.n_tiles, slots);                 \
+    const int dh_slots = (int)ceil_div((int64_t)L.n_rb * L.n_tr, 8);
+    if (L.Np <= 128) {
+      // dh and dM in one launch (for wider weights, where both are long, it
+      // was no faster than two)
+      const int dm_slots = (int)ceil_div(ceil_div(dm_items, 2), 8);
+      const dim3 grid((unsigned)(8 * (dh_slots + dm_slots)));
+      switch (L.Np / 16) {
+#define CASE(ks)                                                                                              \
+  case ks:                                                                                                    \
+    hipLaunchKernelGGL(gbwd::k_dh_dM<ks>, grid, dim3(512), 0, st, g, Ma, (bf16 *)dh, (const bf16 *)h, gT, dMp, \
+                       s.BT, L.BTp, (int)s.d, Mcols, s.N, L.n_rb, L.n_tr, L.tpr, L.n_chunks, L.n_ranges, L.tpb,    \
+                       L.n_tiles, dh_slots, dm_slots);                                                        \
     break;
-      CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)
+        CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)
+#undef CASE
+        default: trace_end(tr, st); return DYNCONV_E_LIMIT;
+      }
+      trace_end(tr, st);
+      return 0;
+    }
+    switch (L.Np / 16) {
+#define CASE(ks)                                                                                          \
+  case ks:                                                                                                \
+    hipLaunchKernelGGL(gbwd::k_dh<ks>, dim3((unsigned)(8 * dh_slots)), dim3(512), 0, st, g, Ma, (bf16 *)dh, \
+                       s.BT, (int)s.d, Mcols, L.n_rb, L.n_tr, L.tpr, L.n_tiles, dh_slots);                \
+    break;
       CASE(9) CASE(10) CASE(11) CASE(12) CASE(13) CASE(14) CASE(15) CASE(16)
 #undef CASE
       default: trace_end(tr, st); return DYNCONV_E_LIMIT;
     }
   }
-  const int slots = (int)ceil_div((int64_t)L.n_chunks * L.n_ranges, 8);
+  const int slots = (int)ceil_div((int64_t)dm_items, 8);
   switch (L.Np / 16) {
 #define CASE(nb)                                                                                      \
   case nb:                                                                                            \
