@@ -109,6 +109,9 @@ def main() -> int:
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--roofline-kernel", default="bwd_conv", choices=["bwd_conv", "fwd_conv"],
                     help="kernel whose roofline is reported (the dominant one by default)")
+    ap.add_argument("--decode", type=int, default=0, metavar="B",
+                    help="instead of the training step, time dynconv_decode (one new token for each "
+                         "of B sequences) on the workload's layer shape")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the layer, run --steps device copies of MIB MiB (a plain copy "
                          "kernel of known size, to scale the FETCH_SIZE / WRITE_SIZE counters)")
@@ -137,6 +140,9 @@ def main() -> int:
 
     import torch
     import input_dependent_depthwise_amd as dc
+
+    if args.decode:
+        return bench_decode(args, torch, dc)
 
     w = workloads.WORKLOADS[args.workload]
     dev = torch.device("cuda", 0)
@@ -233,6 +239,57 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def bench_decode(args, torch, dc) -> int:
+    """Decode steps: B sequences, one token each per step, on the workload's
+    layer shape (d_model, D, k, generator).  Inputs are synthetic (seeded
+    normal h and x, the workload's generator and bias distributions); 16
+    different token rows rotate, and the history is updated in place."""
+    w = workloads.WORKLOADS[args.workload]
+    B = args.decode
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    g = torch.Generator().manual_seed(100 + w.seed)
+    rows = 16
+    h = (torch.randn(rows, B, w.d, generator=g)).to(dt).cuda()
+    x = (torch.randn(rows, B, w.D, generator=g)).to(dt).cuda()
+    wts = {}
+    if w.kind == workloads.HEADWISE:
+        wts["W"] = (torch.randn(w.d, w.n_heads * w.k, generator=g) * w.gen_std).to(dt).cuda()
+    else:
+        wts["A"] = (torch.randn(w.d, w.rank, generator=g) * w.gen_std).to(dt).cuda()
+        wts["U"] = (torch.randn(w.rank, w.D * w.k, generator=g) * w.gen_std).to(dt).cuda()
+    wts["w0"] = (torch.randn(w.D, w.k, generator=g) * w.bias_std).to(dt).cuda() if w.bias_std > 0 else None
+    state = torch.zeros(B, w.k - 1, w.D, dtype=dt, device="cuda") if w.k > 1 else None
+    y = torch.empty(B, w.D, dtype=dt, device="cuda")
+    kw = dict(k=w.k, n_heads=w.n_heads, y=y, **wts)
+
+    def step(i):
+        dc.dynconv_decode(h[i % rows], x[i % rows], state, **kw)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(args.steps):
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / args.steps
+    eb = 2 if dt == torch.bfloat16 else 4
+    wbytes = sum(t.numel() for t in wts.values() if t is not None) * eb
+    per_seq = (w.d + 2 * w.D + 2 * (w.k - 1) * w.D) * eb  # h, x, y, history read and written
+    nbytes = wbytes + B * per_seq
+    line = {"metric": "dynconv decode tokens/s", "value": round(B / (us / 1e6), 1), "unit": "tokens/s",
+            "us_per_step": round(us, 3), "batch": B, "steps": args.steps, "warmup": args.warmup,
+            "dtype": w.dtype, "data": "synthetic (seeded normal h, x; workload's generator and bias scales)",
+            "config": {"workload": w.name, "d_model": w.d, "D": w.D, "k": w.k, "generator": w.describe()["generator"]},
+            "roofline": {"bound": "hbm", "achieved": round(nbytes / (us / 1e6) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(nbytes / (us / 1e6) / 1e9 / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes_per_step": nbytes}}
     print(json.dumps(line), flush=True)
     return 0
 

@@ -157,6 +157,32 @@ DYNCONV_API int dynconv_bwd(const dynconv_problem *p, const dynconv_gen *g, cons
                 const dynconv_gen_grad *gg, void *workspace, size_t workspace_bytes,
                 hipStream_t stream);
 
+/*
+ * Decode step (inference): one new token for each of B sequences.  The taps
+ * of the causal convolution (Mechanism) reach the k-1 previous rows of x, so
+ * a decoder keeps those rows per sequence; the filter of the new token comes
+ * from its hidden state as in the forward (Parameterization).  The pages
+ * leave inference unoptimised (atlas.scime.ai, "Dynamic Convolutions Improve
+ * Transformers", Limitations).  For every sequence b and channel c:
+ *
+ *   y[b,c] = x[b,c] + w[b,c,0] x[b,c] + sum_{j=1}^{k-1} w[b,c,j] state[b,k-1-j,c]
+ *
+ * with w[b,c,j] formed from h[b] exactly as in dynconv_fwd, then the history
+ * shifts by one row: state[b,m] = state[b,m+1] for m < k-2, state[b,k-2] =
+ * x[b].  Starting from a zeroed state, the t-th call on a sequence returns
+ * row t of dynconv_fwd on that sequence (up to summation order).
+ *   p      sizes with T == 1 (one token per sequence); B may be 0 (no-op)
+ *   h, x   inputs [B, d_model] and [B, D], I/O dtype
+ *   state  [B, k-1, D], I/O dtype, read and updated in place (the oldest row
+ *          first); may be NULL when k == 1
+ *   y      output [B, D], I/O dtype
+ * No workspace.  Errors as for dynconv_fwd; DYNCONV_E_SHAPE if T != 1,
+ * DYNCONV_E_LIMIT if B > 65535.  y and state must not overlap each other or
+ * any input.
+ */
+DYNCONV_API int dynconv_decode(const dynconv_problem *p, const dynconv_gen *g, const void *h, const void *x,
+                   void *state, void *y, hipStream_t stream);
+
 /* Workspace bytes a pass needs (pass 0 = forward, 1 = backward); 0 on
  * invalid arguments.  Depends only on the sizes, never on pointers. */
 DYNCONV_API size_t dynconv_workspace_bytes(const dynconv_problem *p, const dynconv_gen *g, int pass);

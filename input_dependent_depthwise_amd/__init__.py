@@ -1,7 +1,7 @@
 """MI355X (gfx950) dynamic short convolution: Python binding of libdynconv.
 
 Thin ctypes binding of the C ABI in ``include/dynconv.h``, with the same
-names (``dynconv_fwd``, ``dynconv_bwd``, ``dynconv_workspace_bytes``,
+names (``dynconv_fwd``, ``dynconv_bwd``, ``dynconv_decode``, ``dynconv_workspace_bytes``,
 ``dynconv_gen_cache_bytes``, ``dynconv_status_str``, ``dynconv_abi_version``).
 It only marshals arguments: torch provides device memory (outputs and
 workspace are ``torch.empty``) and the current HIP stream; every step of the
@@ -51,7 +51,7 @@ class GenGrad(ctypes.Structure):
 
 
 # names the C header declares; the CPU tests check each is exported
-EXPORTS = ("dynconv_fwd", "dynconv_bwd", "dynconv_workspace_bytes", "dynconv_gen_cache_bytes",
+EXPORTS = ("dynconv_fwd", "dynconv_bwd", "dynconv_decode", "dynconv_workspace_bytes", "dynconv_gen_cache_bytes",
            "dynconv_status_str", "dynconv_abi_version", "dynconv_trace_next")
 
 # kernel ids for dynconv_trace_next
@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
         L.dynconv_fwd.restype = ctypes.c_int
         L.dynconv_bwd.argtypes = [PP, PG, P, P, P, P, P, P, PGG, P, ctypes.c_size_t, P]
         L.dynconv_bwd.restype = ctypes.c_int
+        L.dynconv_decode.argtypes = [PP, PG, P, P, P, P, P]
+        L.dynconv_decode.restype = ctypes.c_int
         L.dynconv_workspace_bytes.argtypes = [PP, PG, ctypes.c_int]
         L.dynconv_workspace_bytes.restype = ctypes.c_size_t
         L.dynconv_gen_cache_bytes.argtypes = [PP, PG]
@@ -204,6 +206,20 @@ def dynconv_bwd(h, x, dy, *, k, W=None, A=None, U=None, w0=None, n_heads=0, gen_
                            _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check(rc, "dynconv_bwd")
     return o
+
+
+def dynconv_decode(h, x, state, *, k, W=None, A=None, U=None, w0=None, n_heads=0, y=None, stream=None):
+    """One decoding step: h [B, d_model], x [B, D], state [B, k-1, D] (updated
+    in place; None when k == 1).  Returns y [B, D]."""
+    B, D = x.shape
+    prob = Problem(B, 1, h.shape[-1], D, k, _dtype_code(x.dtype))
+    gen = make_gen(W, A, U, w0, n_heads)
+    if y is None:
+        y = torch.empty_like(x)
+    rc = lib().dynconv_decode(ctypes.byref(prob), ctypes.byref(gen), _ptr(h), _ptr(x), _ptr(state), _ptr(y),
+                              _stream(stream))
+    _check(rc, "dynconv_decode")
+    return y
 
 
 class DynConvFn(torch.autograd.Function):

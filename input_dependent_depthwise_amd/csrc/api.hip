@@ -271,6 +271,34 @@ int dynconv_fwd(const dynconv_problem *p, const dynconv_gen *g, const void *h, c
   return launch_status();
 }
 
+int dynconv_decode(const dynconv_problem *p, const dynconv_gen *g, const void *h, const void *x, void *state,
+                   void *y, hipStream_t stream) {
+  Shape s;
+  int rc = check_problem(p, g, s);
+  if (rc) return rc;
+  if (p->T != 1) return DYNCONV_E_SHAPE;
+  if (s.B == 0) return DYNCONV_OK;
+  if (!h || !x || !y || (s.k > 1 && !state)) return DYNCONV_E_NULL;
+  if ((rc = check_weights(s, g))) return rc;
+  if (s.B > 65535) return DYNCONV_E_LIMIT;  // grid rows of four sequences stay far below the limit
+  const void *ptrs[] = {h, x, y, state};
+  for (const void *q : ptrs)
+    if (q && !aligned16(q)) return DYNCONV_E_ALIGN;
+  const int eb = p->dtype == DYNCONV_BF16 ? 2 : 4;
+  const Sizes z = sizes(s, eb);
+  const size_t st_bytes = s.k > 1 ? (size_t)s.B * (s.k - 1) * s.D * eb : 0;
+  const Range ins[] = {{h, z.h}, {x, z.x}, {g->W, z.W}, {g->A, z.A}, {g->U, z.U}, {g->w0, g->w0 ? z.w0 : 0}};
+  const Range outs[] = {{y, z.x}, {state, st_bytes}};
+  for (const Range &o : outs)
+    for (const Range &i : ins)
+      if (overlap(o, i)) return DYNCONV_E_ALIAS;
+  if (overlap(outs[0], outs[1])) return DYNCONV_E_ALIAS;
+  rc = p->dtype == DYNCONV_BF16 ? decode_step<bf16>(s, h, g->W, g->A, g->U, g->w0, x, state, y, stream)
+                                : decode_step<float>(s, h, g->W, g->A, g->U, g->w0, x, state, y, stream);
+  if (rc) return rc;
+  return launch_status();
+}
+
 int dynconv_bwd(const dynconv_problem *p, const dynconv_gen *g, const void *h, const void *x,
                 const void *dy, const void *gen_cache, void *dx, void *dh,
                 const dynconv_gen_grad *gg, void *workspace, size_t workspace_bytes,

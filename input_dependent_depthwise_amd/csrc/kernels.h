@@ -24,6 +24,11 @@ int simple_bwd(const Shape &s, const float *gen, const void *W, const void *A, c
                const void *w0, const void *h, const void *x, const void *dy, void *dx, void *dh,
                const dynconv_gen_grad &gg, float *g, hipStream_t st);
 
+// --- one decoding step, T = float or bf16 (decode.hip) ---
+template <typename T>
+int decode_step(const Shape &s, const void *h, const void *W, const void *A, const void *U, const void *w0,
+                const void *x, void *state, void *y, hipStream_t st);
+
 // --- bf16 matrix-core generator projection (gen_mfma.hip) ---
 size_t gen_proj_mfma_ws_bytes(const Shape &s);
 int gen_proj_mfma(const Shape &s, const void *h, const void *M, float *out, void *ws, hipStream_t st);

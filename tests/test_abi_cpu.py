@@ -201,3 +201,42 @@ def test_bwd_validation(L, case, expect):
     elif case == "ws_small":
         kw["ws_bytes"] = 100
     assert bwd(L, p, g, **kw) == expect
+
+
+def dec(L, p, g, h=addr(1), x=addr(2), state=addr(3), y=addr(4)):
+    return L.dynconv_decode(ctypes.byref(p) if p is not None else None,
+                            ctypes.byref(g) if g is not None else None, h, x, state, y, None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_problem", E_NULL), ("T2", E_SHAPE), ("k9", E_K), ("null_x", E_NULL), ("null_state", E_NULL),
+    ("null_W", E_NULL), ("align_y", E_ALIGN), ("alias_y_state", E_ALIAS), ("alias_state_x", E_ALIAS),
+    ("B_limit", E_LIMIT), ("empty", OK),
+])
+def test_decode_validation(L, case, expect):
+    """dynconv_decode rejects bad arguments on the host; B == 0 is a no-op."""
+    p, g = prob(T=1), gen_hw()
+    kw = {}
+    if case == "null_problem":
+        p = None
+    elif case == "T2":
+        p = prob(T=2)
+    elif case == "k9":
+        p = prob(T=1, k=9)
+    elif case == "null_x":
+        kw["x"] = None
+    elif case == "null_state":
+        kw["state"] = None
+    elif case == "null_W":
+        g.W = None
+    elif case == "align_y":
+        kw["y"] = addr(4) + 4
+    elif case == "alias_y_state":
+        kw["y"] = addr(3) + 256
+    elif case == "alias_state_x":
+        kw["state"] = addr(2)
+    elif case == "B_limit":
+        p = prob(B=70000, T=1)
+    elif case == "empty":
+        p = prob(B=0, T=1)
+    assert dec(L, p, g, **kw) == expect

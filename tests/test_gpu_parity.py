@@ -18,6 +18,7 @@ import pytest
 import torch
 
 import input_dependent_depthwise_amd as dc
+import oracle
 import workloads
 from tests import gpu_util as gu
 from workloads import HEADWISE, LOWRANK, WORKLOADS, Workload
@@ -185,6 +186,34 @@ def test_autograd_wrapper(w):
     for key, gkey in (("W", "dW"), ("A", "dA"), ("U", "dU"), ("w0", "dw0")):
         if leaves[key] is not None:
             assert torch.equal(leaves[key].grad, ref[gkey].to(leaves[key].dtype)), key
+
+
+DECODE = [SMALL[0], SMALL[7], SMALL[6], SMALL[12], SMALL[9], SMALL[5], SMALL[10], SMALL[4]]
+
+
+@pytest.mark.parametrize("w", DECODE, ids=[w.name for w in DECODE])
+def test_decode_steps_match_forward(w):
+    """dynconv_decode, called once per position from a zeroed history, gives
+    the oracle's forward rows (first 48 positions of every sequence)."""
+    _note(f"[decode] {w.name}")
+    inp = workloads.generate(w)
+    s = gu.oracle_shape(w)
+    ref = oracle.forward(s, inp["h"], inp["x"], W=inp.get("W"), A=inp.get("A"), U=inp.get("U"),
+                         w0=inp.get("w0"))["y"]
+    dev = gu.to_dev(inp)
+    B, T, D = dev["x"].shape
+    steps = min(T, 48)
+    state = torch.zeros(B, w.k - 1, D, dtype=dev["x"].dtype, device="cuda") if w.k > 1 else None
+    kw = dict(k=w.k, W=dev.get("W"), A=dev.get("A"), U=dev.get("U"), w0=dev.get("w0"), n_heads=w.n_heads)
+    ys = [dc.dynconv_decode(dev["h"][:, t].contiguous(), dev["x"][:, t].contiguous(), state, **kw)
+          for t in range(steps)]
+    torch.cuda.synchronize()
+    y = torch.stack(ys, 1).float().cpu().numpy()
+    err = gu.max_rel_err(y, np.asarray(ref).reshape(B, T, D)[:, :steps])
+    assert err <= gu.TOL[w.dtype], (w.name, err)
+    if w.k > 1:  # the history holds the last k-1 rows of x
+        last = dev["x"][:, max(0, steps - (w.k - 1)):steps]
+        assert torch.equal(state[:, state.shape[1] - last.shape[1]:], last)
 
 
 @pytest.mark.parametrize("kind", ["lowrank", "headwise"])
