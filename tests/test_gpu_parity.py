@@ -188,7 +188,11 @@ def test_autograd_wrapper(w):
             assert torch.equal(leaves[key].grad, ref[gkey].to(leaves[key].dtype)), key
 
 
-DECODE = [SMALL[0], SMALL[7], SMALL[6], SMALL[12], SMALL[9], SMALL[5], SMALL[10], SMALL[4]]
+DECODE = [SMALL[0], SMALL[7], SMALL[6], SMALL[12], SMALL[9], SMALL[5], SMALL[10], SMALL[4],
+          # more than 1024 (sequence, 256-channel) blocks: four sequences per block, the
+          # last block with one (161 = 4 * 40 + 1)
+          Workload("dec_grouped_lr", B=161, T=6, d=64, D=2048, k=4, kind=LOWRANK, rank=16, seed=41),
+          Workload("dec_grouped_hw_k3", B=161, T=5, d=64, D=2048, k=3, kind=HEADWISE, n_heads=16, seed=42)]
 
 
 @pytest.mark.parametrize("w", DECODE, ids=[w.name for w in DECODE])
