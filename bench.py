@@ -89,11 +89,18 @@ def cpu_baseline(w: workloads.Workload, inp: dict, budget_s: float) -> dict:
     t1 = run(1)
     nseq = max(1, min(w.B, int(budget_s / max(t1, 1e-6))))
     t = run(nseq) if nseq > 1 else t1
-    tokens = nseq * w.T
+    # a whole workload that takes well under the budget is run again, so that the
+    # rate comes from about budget_s of work
+    reps = 1
+    if nseq == w.B and t < budget_s / 2:
+        extra = min(30, int(budget_s / max(t, 1e-6)) - 1)
+        t += sum(run(nseq) for _ in range(extra))
+        reps += extra
+    tokens = nseq * w.T * reps
     return {"value": round(tokens / t, 1), "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"{nseq} of {w.B} sequences ({tokens} tokens) of {w.name}, fwd+bwd, fp64, "
-                      f"{t:.2f} s"}
+            "sample": f"{nseq} of {w.B} sequences of {w.name}, fwd+bwd, fp64, {reps} run(s), "
+                      f"{tokens} tokens in {t:.2f} s"}
 
 
 def main() -> int:
