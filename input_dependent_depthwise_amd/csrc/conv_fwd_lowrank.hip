@@ -14,7 +14,7 @@
 // tokens of a tile, K is the rank.  Lane l owns token l%32 and the 8
 // channels 8*(l/32)..+7 of a 16-channel group; two MFMAs ("quads" p = 0, 1)
 // give it taps 0..3 of channels 8*(l/32)+4p+b (b = 0..3) in accumulator
-// elements 4b+r.  For k > 4 two more MFMAs give taps 4..7.  The bias w0
+// elements 4b+r (k <= 4; wider filters take the plain VALU kernel).  The bias w0
 // enters the same MFMA chain as one extra K row: the B operand (z) carries a
 // constant 1 at q = r and the A operand carries w0 there, so the filter
 // leaves the matrix core complete.  Each lane gathers its A-operand values

@@ -14,9 +14,10 @@
 // zero-padded copy Mt[Np][Kp] of the weight that a prep kernel writes into
 // the workspace (Kp = K rounded up to 32), staged one K-slice at a time in
 // LDS and shared by the block's waves, so the weight is read from L2 once
-// per block.  Narrow weights (N <= 32) use a K-split variant instead.  h is
-// read once: the kernel is bound by HBM for N <= 64 and near the MFMA/HBM
-// ridge at N = 256.
+// per block.  Narrow weights (N <= 32) use a K-split variant instead, which
+// stages the weight itself in LDS when it fits (no prep kernel).  h is read
+// once: the kernel is bound by HBM for N <= 64 and near the MFMA/HBM ridge at
+// N = 256.
 #include "kernels.h"
 #include "bufio.h"
 #include "mfma.h"
