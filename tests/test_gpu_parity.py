@@ -6,8 +6,8 @@ Covers the five workloads at their full sizes (the launch configuration the
 benchmark times), shapes that span several tiles with ragged tails, and the
 degenerate cases (T = 1, T < k, k = 1, heads narrower than a vector, rank 1,
 no bias).  Bitwise invariants: zero filter gives y == x and dx == dy,
-causality, determinism, cache reuse == recompute, the autograd wrapper ==
-the direct calls.
+causality, batch isolation, determinism, cache reuse == recompute, the
+autograd wrapper == the direct calls.
 """
 from __future__ import annotations
 
@@ -146,6 +146,25 @@ def test_causality(w):
         y1 = gu.gpu_run(w, d2)["y"]
         assert torch.equal(y0[:, : t + 1], y1[:, : t + 1]), t
         assert not torch.equal(y0[:, t + 1:], y1[:, t + 1:]), t
+
+
+@pytest.mark.parametrize("w", [SMALL[0], SMALL[7]], ids=["hw", "lr"])
+def test_batch_isolation(w):
+    """Changing one sequence's h, x and dy leaves the other sequences' y, dx
+    and dh bitwise unchanged (nothing crosses batch rows)."""
+    _note(f"[isolation] {w.name}")
+    assert w.B >= 2
+    dev = gu.to_dev(workloads.generate(w))
+    a = gu.gpu_run(w, dev)
+    d2 = dict(dev)
+    for key, delta in (("x", 1.0), ("h", -0.5), ("dy", 0.25)):
+        t = dev[key].clone()
+        t[0] += delta
+        d2[key] = t
+    b = gu.gpu_run(w, d2)
+    for key in ("y", "dx", "dh"):
+        assert torch.equal(a[key][1:], b[key][1:]), key
+        assert not torch.equal(a[key][0], b[key][0]), key
 
 
 def test_empty_batch():
