@@ -32,7 +32,9 @@ sys.path.insert(0, ROOT)
 import workloads  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix-core peak, published
 MALL_BYTES = 256 * 2**20     # Infinity Cache
+MAX_SETS = 8                 # rotating input sets at most (small workloads fit in the cache anyway)
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -47,6 +49,26 @@ def algorithmic_bytes(w: workloads.Workload) -> dict:
     eb, d, D = w.elem_bytes, w.d, w.D
     return {"fwd": eb * (d + 2 * D), "bwd": eb * (2 * d + 3 * D), "step": eb * (3 * d + 5 * D),
             "bwd_conv": eb * 3 * D, "fwd_conv": eb * 2 * D}
+
+
+def generator_flops(w: workloads.Workload) -> dict:
+    """Matrix-core flops per launch of the generator kernels (dense bf16 GEMMs).
+
+    gen_proj: u = h W or z = h A                        -> 2 * BT * d * N
+    gen_bwd : dh = g M^T and dM = h^T g (M = W or A)     -> 4 * BT * d * N
+    """
+    n = w.gen_cols
+    return {"gen_proj": 2 * w.tokens * w.d * n, "gen_bwd": 4 * w.tokens * w.d * n}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def kernel_source_sha() -> str:
@@ -98,9 +120,9 @@ def cpu_baseline(w: workloads.Workload, inp: dict, budget_s: float) -> dict:
         reps += extra
     tokens = nseq * w.T * reps
     return {"value": round(tokens / t, 1), "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
             "sample": f"{nseq} of {w.B} sequences of {w.name}, fwd+bwd, fp64, {reps} run(s), "
-                      f"{tokens} tokens in {t:.2f} s"}
+                      f"{tokens} tokens in {t:.2f} s on {oracle.num_threads()} OpenMP threads"}
 
 
 def main() -> int:
@@ -109,7 +131,11 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=workloads.BENCH_WORKLOAD, choices=list(workloads.WORKLOADS))
-    ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0: enough to exceed 2x MALL)")
+    ap.add_argument("--sets", type=int, default=0,
+                    help=f"rotating input sets (0: enough to exceed 2x MALL, at most {MAX_SETS})")
+    ap.add_argument("--mfma-steps", type=int, default=8,
+                    help="after the timed steps, this many more steps time the generator kernels "
+                         "with HIP events (matrix-core roofline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--trace-every", type=int, default=4,
                     help="time the dominant kernel with HIP events on every N-th timed step")
@@ -158,7 +184,7 @@ def main() -> int:
 
     # --- device buffers: R rotating sets ---
     per_set = (w.tokens * (2 * w.d + 4 * w.D) * w.elem_bytes)  # h, x, dy, y, dx, dh
-    R = args.sets or max(2, -(-2 * MALL_BYTES // per_set) + 1)
+    R = args.sets or min(MAX_SETS, max(2, -(-2 * MALL_BYTES // per_set) + 1))
     prob = dc.make_problem(inp["x"], inp["h"], w.k)
     sets = []
     for _ in range(R):
@@ -226,6 +252,35 @@ def main() -> int:
     ms = t_start.elapsed_time(t_stop) / args.steps
     kern_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
 
+    # matrix-core roofline of the generator kernels, from extra (untimed) steps
+    # so that their events do not stretch the timed ones
+    mfma = None
+    if args.mfma_steps > 0 and w.dtype == "bf16":
+        fl = generator_flops(w)
+        mev = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.mfma_steps)] for k in ("gen_proj", "gen_bwd")}
+        for evs in mev.values():  # create the underlying HIP events
+            for a, b in evs:
+                a.record()
+                b.record()
+        for i in range(args.mfma_steps):
+            s_ = sets[i % R]
+            g = dict(W=s_.get("W"), A=s_.get("A"), U=s_.get("U"), w0=s_.get("w0"))
+            a, b = mev["gen_proj"][i]
+            dc.dynconv_trace_next(dc.DYNCONV_K_GEN_PROJ, a, b)
+            dc.dynconv_fwd(s_["h"], s_["x"], y=s_["y"], gen_cache=s_["cache"], workspace=s_["ws_f"], **g, **kw)
+            a, b = mev["gen_bwd"][i]
+            dc.dynconv_trace_next(dc.DYNCONV_K_GEN_BWD, a, b)
+            dc.dynconv_bwd(s_["h"], s_["x"], s_["dy"], gen_cache=s_["cache"], out=s_["out"],
+                           workspace=s_["ws_b"], **g, **kw)
+        torch.cuda.synchronize()
+        mfma = {"bound": "mfma", "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s", "dtype": "bf16"}
+        for k, evs in mev.items():
+            kms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+            tf = fl[k] / (kms / 1e3) / 1e12
+            mfma[k] = {"achieved": round(tf, 1), "frac": round(tf / MFMA_BF16_PEAK_TFS, 4),
+                       "flops_per_launch": fl[k], "kernel_ms": round(kms, 5)}
+
     ab = algorithmic_bytes(w)
     value = w.tokens / (ms / 1e3)
     dom_bytes = ab[dom[2]] * w.tokens
@@ -244,6 +299,8 @@ def main() -> int:
                      "algorithmic_bytes_per_launch": dom_bytes, "traced_launches": len(ev)},
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 4),
     }
+    if mfma is not None:
+        line["mfma_roofline"] = mfma
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget)
     print(json.dumps(line), flush=True)

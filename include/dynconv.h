@@ -51,14 +51,22 @@
  * not be used by anything else until the enqueued work has finished.
  * Results are bitwise deterministic for fixed inputs and shapes (no float
  * atomics; every reduction runs in a fixed order).  The library is
- * thread-safe; its only global state is a cached device-property query.
+ * thread-safe; its only global state is the one-shot event pair that
+ * dynconv_trace_next arms, kept per host thread.
  *
  * Errors: every call returns DYNCONV_OK (0) or a negative status.  Argument
  * errors are detected on the host before anything is enqueued, and the
  * outputs are then untouched.  DYNCONV_E_HIP reports a failed launch; a
  * fault during kernel execution surfaces at the caller's next
- * synchronisation.  B*T == 0 is a no-op returning DYNCONV_OK.  No C++
- * exception crosses this interface and nothing is printed.
+ * synchronisation.  With B*T == 0 the forward enqueues nothing and the
+ * backward only writes the (empty-sum) zero weight gradients; both return
+ * DYNCONV_OK.  No C++ exception crosses this interface and nothing is
+ * printed.
+ *
+ * Sizes: any D and d_model are accepted.  The tuned kernels take rows made
+ * of whole 16-byte vectors (D and d_model multiples of 8 for bf16, of 4 for
+ * fp32); other widths run on plain per-element kernels with the same
+ * results up to summation order.
  */
 #ifndef DYNCONV_H
 #define DYNCONV_H
@@ -88,8 +96,7 @@ enum {
   DYNCONV_OK = 0,
   DYNCONV_E_NULL = -1,      /* a required pointer is NULL                        */
   DYNCONV_E_SHAPE = -2,     /* a size <= 0 (B, T may be 0), D % n_heads != 0,    */
-                            /* rank <= 0, or D / d_model not a multiple of the    */
-                            /* 16-byte vector (8 bf16 or 4 fp32 channels)         */
+                            /* or rank <= 0                                       */
   DYNCONV_E_K = -3,         /* k outside [1, 8]                                   */
   DYNCONV_E_DTYPE = -4,     /* dtype or kind not one of the enums                 */
   DYNCONV_E_ALIGN = -5,     /* a tensor pointer not 16-byte aligned               */
@@ -136,7 +143,8 @@ typedef struct {
  *   gen_cache NULL, or an fp32 buffer of dynconv_gen_cache_bytes() that
  *             receives u = h W (head-wise) or z = h A (low-rank) for reuse
  *             by dynconv_bwd with the same inputs and weights
- *   workspace device scratch of at least dynconv_workspace_bytes(p, g, 0)
+ *   workspace device scratch of at least dynconv_workspace_bytes(p, g, 0),
+ *             or (p, g, DYNCONV_WS_CACHED) when gen_cache is given
  */
 DYNCONV_API int dynconv_fwd(const dynconv_problem *p, const dynconv_gen *g, const void *h, const void *x,
                 void *y, void *gen_cache, void *workspace, size_t workspace_bytes,
@@ -150,7 +158,8 @@ DYNCONV_API int dynconv_fwd(const dynconv_problem *p, const dynconv_gen *g, cons
  *   dx        output [B,T,D], I/O dtype
  *   dh        output [B,T,d_model], I/O dtype, or NULL to skip
  *   gg        weight gradients (fp32), overwritten
- *   workspace device scratch of at least dynconv_workspace_bytes(p, g, 1)
+ *   workspace device scratch of at least dynconv_workspace_bytes(p, g, 1),
+ *             or (p, g, 1 | DYNCONV_WS_CACHED) when gen_cache is given
  */
 DYNCONV_API int dynconv_bwd(const dynconv_problem *p, const dynconv_gen *g, const void *h, const void *x,
                 const void *dy, const void *gen_cache, void *dx, void *dh,
@@ -183,8 +192,13 @@ DYNCONV_API int dynconv_bwd(const dynconv_problem *p, const dynconv_gen *g, cons
 DYNCONV_API int dynconv_decode(const dynconv_problem *p, const dynconv_gen *g, const void *h, const void *x,
                    void *state, void *y, hipStream_t stream);
 
-/* Workspace bytes a pass needs (pass 0 = forward, 1 = backward); 0 on
- * invalid arguments.  Depends only on the sizes, never on pointers. */
+/* Workspace bytes a pass needs: pass 0 = forward, 1 = backward, each
+ * optionally or-ed with DYNCONV_WS_CACHED when the caller passes gen_cache
+ * to that call (the library then needs no slot of its own for the
+ * generator cache, B*T * (n_heads*k or rank) * 4 bytes less).  Without the
+ * flag the size covers both cases.  0 on invalid arguments.  Depends only
+ * on the sizes and the flag, never on pointers. */
+#define DYNCONV_WS_CACHED 2
 DYNCONV_API size_t dynconv_workspace_bytes(const dynconv_problem *p, const dynconv_gen *g, int pass);
 
 /* Bytes of the fp32 generator cache (B*T * (n_heads*k or rank) * 4). */

@@ -26,6 +26,7 @@ LIB_PATH = os.path.join(_PKG, "libdynconv.so")
 
 DYNCONV_FP32, DYNCONV_BF16 = 0, 1
 DYNCONV_HEADWISE, DYNCONV_LOWRANK = 0, 1
+DYNCONV_WS_CACHED = 2  # or-ed into dynconv_workspace_bytes' pass when the call gets gen_cache
 
 
 class DynConvError(RuntimeError):
@@ -171,7 +172,7 @@ def dynconv_fwd(h, x, *, k, W=None, A=None, U=None, w0=None, n_heads=0, y=None, 
     if gen_cache is None and want_cache:
         n = gen.n_heads * k if gen.kind == DYNCONV_HEADWISE else gen.rank
         gen_cache = torch.empty(x.shape[0] * x.shape[1], n, dtype=torch.float32, device=x.device)
-    nbytes = dynconv_workspace_bytes(prob, gen, 0)
+    nbytes = dynconv_workspace_bytes(prob, gen, 0 | (DYNCONV_WS_CACHED if gen_cache is not None else 0))
     ws = _workspace(nbytes, x.device, workspace)
     rc = lib().dynconv_fwd(ctypes.byref(prob), ctypes.byref(gen), _ptr(h), _ptr(x), _ptr(y),
                            _ptr(gen_cache), _ptr(ws), ws.numel() * ws.element_size(),
@@ -199,7 +200,7 @@ def dynconv_bwd(h, x, dy, *, k, W=None, A=None, U=None, w0=None, n_heads=0, gen_
         o.setdefault("dA", torch.empty(prob.d_model, gen.rank, **f32))
         o.setdefault("dU", torch.empty(gen.rank, prob.D * k, **f32))
     gg = GenGrad(_ptr(o.get("dW")), _ptr(o.get("dA")), _ptr(o.get("dU")), _ptr(o.get("dw0")))
-    nbytes = dynconv_workspace_bytes(prob, gen, 1)
+    nbytes = dynconv_workspace_bytes(prob, gen, 1 | (DYNCONV_WS_CACHED if gen_cache is not None else 0))
     ws = _workspace(nbytes, dev, workspace)
     rc = lib().dynconv_bwd(ctypes.byref(prob), ctypes.byref(gen), _ptr(h), _ptr(x), _ptr(dy),
                            _ptr(gen_cache), _ptr(o["dx"]), _ptr(o.get("dh")), ctypes.byref(gg),

@@ -36,8 +36,6 @@ int check_problem(const dynconv_problem *p, const dynconv_gen *g, Shape &s) {
   if (g->kind != DYNCONV_HEADWISE && g->kind != DYNCONV_LOWRANK) return DYNCONV_E_DTYPE;
   if (p->k < 1 || p->k > 8) return DYNCONV_E_K;
   if (p->B < 0 || p->T < 0 || p->d_model <= 0 || p->D <= 0) return DYNCONV_E_SHAPE;
-  const int64_t vec = p->dtype == DYNCONV_BF16 ? 8 : 4;
-  if (p->D % vec != 0 || p->d_model % vec != 0) return DYNCONV_E_SHAPE;
   int N;
   if (g->kind == DYNCONV_HEADWISE) {
     if (g->n_heads <= 0 || p->D % g->n_heads != 0) return DYNCONV_E_SHAPE;
@@ -81,14 +79,24 @@ struct Plan {
   size_t total = 0;
 };
 
+// Rows of h and x made of whole 16-byte vectors (8 bf16 or 4 fp32 channels):
+// the layout every tuned kernel assumes.  Other widths take the plain
+// kernels, which address single elements.
+inline bool vec_rows(const Shape &s, int dtype) {
+  const int64_t vec = dtype == DYNCONV_BF16 ? 8 : 4;
+  return s.D % vec == 0 && s.d % vec == 0;
+}
+inline bool mfma_proj(const Shape &s, int dtype) { return dtype == DYNCONV_BF16 && s.d % 8 == 0; }
 inline bool fast_lowrank(const Shape &s, int dtype) {
-  return dtype == DYNCONV_BF16 && s.kind == DYNCONV_LOWRANK && fwd_lowrank_supported(s);
+  return dtype == DYNCONV_BF16 && s.kind == DYNCONV_LOWRANK && vec_rows(s, dtype) && fwd_lowrank_supported(s);
 }
 inline bool fast_bwd(const Shape &s, int dtype) {
-  return dtype == DYNCONV_BF16 && bwd_fused_supported(s) && gen_bwd_supported(s);
+  return dtype == DYNCONV_BF16 && vec_rows(s, dtype) && bwd_fused_supported(s) && gen_bwd_supported(s);
 }
 
-Plan plan(const Shape &s, int dtype, int pass) {
+// pass: 0 forward, 1 backward; `cached`: the caller passes gen_cache, so no
+// cache slot is needed.
+Plan plan(const Shape &s, int dtype, int pass, bool cached) {
   Plan pl;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -96,8 +104,9 @@ Plan plan(const Shape &s, int dtype, int pass) {
     off += round_up(bytes);
     return at;
   };
-  pl.cache = take((size_t)s.BT * s.N * sizeof(float));
-  if (dtype == DYNCONV_BF16) pl.mt = take(gen_proj_mfma_ws_bytes(s));
+  if (!cached) pl.cache = take((size_t)s.BT * s.N * sizeof(float));
+  // the projection runs in the forward, and in the backward only to rebuild a missing cache
+  if (mfma_proj(s, dtype) && (pass == 0 || !cached)) pl.mt = take(gen_proj_mfma_ws_bytes(s));
   if (pass == 1) {
     if (fast_bwd(s, dtype)) {
       const BwdLayout L = bwd_layout(s);
@@ -153,7 +162,8 @@ int check_weights(const Shape &s, const dynconv_gen *g) {
 int gen_proj(const Shape &s, int dtype, const dynconv_gen *g, const void *h, float *cache,
              void *ws, const Plan &pl, hipStream_t st) {
   const void *M = s.kind == DYNCONV_HEADWISE ? g->W : g->A;
-  if (dtype == DYNCONV_BF16) return gen_proj_mfma(s, h, M, cache, (char *)ws + pl.mt, st);
+  if (mfma_proj(s, dtype)) return gen_proj_mfma(s, h, M, cache, (char *)ws + pl.mt, st);
+  if (dtype == DYNCONV_BF16) return simple_gen_proj<bf16>(s, h, M, cache, st);
   return simple_gen_proj<float>(s, h, M, cache, st);
 }
 
@@ -204,7 +214,7 @@ const char *dynconv_status_str(int status) {
   switch (status) {
     case DYNCONV_OK: return "ok";
     case DYNCONV_E_NULL: return "a required pointer is NULL";
-    case DYNCONV_E_SHAPE: return "invalid shape (size <= 0, D % n_heads != 0, rank <= 0, or D/d_model not a multiple of 16 bytes)";
+    case DYNCONV_E_SHAPE: return "invalid shape (a size <= 0, D % n_heads != 0 or rank <= 0)";
     case DYNCONV_E_K: return "filter width k outside [1, 8]";
     case DYNCONV_E_DTYPE: return "unknown dtype or generator kind";
     case DYNCONV_E_ALIGN: return "a tensor pointer is not 16-byte aligned";
@@ -224,8 +234,9 @@ size_t dynconv_gen_cache_bytes(const dynconv_problem *p, const dynconv_gen *g) {
 
 size_t dynconv_workspace_bytes(const dynconv_problem *p, const dynconv_gen *g, int pass) {
   Shape s;
-  if ((pass != 0 && pass != 1) || check_problem(p, g, s) != DYNCONV_OK) return 0;
-  return plan(s, p->dtype, pass).total;
+  const int base = pass & ~DYNCONV_WS_CACHED;
+  if ((base != 0 && base != 1) || check_problem(p, g, s) != DYNCONV_OK) return 0;
+  return plan(s, p->dtype, base, (pass & DYNCONV_WS_CACHED) != 0).total;
 }
 
 int dynconv_fwd(const dynconv_problem *p, const dynconv_gen *g, const void *h, const void *x,
@@ -240,7 +251,7 @@ int dynconv_fwd(const dynconv_problem *p, const dynconv_gen *g, const void *h, c
   const void *ptrs[] = {h, x, y, gen_cache, workspace};
   for (const void *q : ptrs)
     if (q && !aligned16(q)) return DYNCONV_E_ALIGN;
-  const Plan pl = plan(s, p->dtype, 0);
+  const Plan pl = plan(s, p->dtype, 0, gen_cache != nullptr);
   if (workspace_bytes < pl.total || (pl.total > 0 && !workspace)) return DYNCONV_E_WORKSPACE;
   const int eb = p->dtype == DYNCONV_BF16 ? 2 : 4;
   const Sizes z = sizes(s, eb);
@@ -257,7 +268,7 @@ int dynconv_fwd(const dynconv_problem *p, const dynconv_gen *g, const void *h, c
 
   float *cache = gen_cache ? (float *)gen_cache : (float *)((char *)workspace + pl.cache);
   if ((rc = gen_proj(s, p->dtype, g, h, cache, workspace, pl, stream))) return rc;
-  if (s.kind == DYNCONV_HEADWISE) {
+  if (s.kind == DYNCONV_HEADWISE && vec_rows(s, p->dtype)) {
     rc = p->dtype == DYNCONV_BF16 ? fwd_headwise<bf16>(s, cache, g->w0, x, y, stream)
                                   : fwd_headwise<float>(s, cache, g->w0, x, y, stream);
   } else if (fast_lowrank(s, p->dtype)) {
@@ -327,7 +338,7 @@ int dynconv_bwd(const dynconv_problem *p, const dynconv_gen *g, const void *h, c
   const void *ptrs[] = {h, x, dy, gen_cache, dx, dh, workspace, gg->dW, gg->dA, gg->dU, gg->dw0};
   for (const void *q : ptrs)
     if (q && !aligned16(q)) return DYNCONV_E_ALIGN;
-  const Plan pl = plan(s, p->dtype, 1);
+  const Plan pl = plan(s, p->dtype, 1, gen_cache != nullptr);
   if (workspace_bytes < pl.total || (pl.total > 0 && !workspace)) return DYNCONV_E_WORKSPACE;
   const int eb = p->dtype == DYNCONV_BF16 ? 2 : 4;
   const Sizes z = sizes(s, eb);

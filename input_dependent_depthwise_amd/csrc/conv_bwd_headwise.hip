@@ -185,7 +185,7 @@ k_bwd_hw(Params P) {
   const int cc = act ? c0 : Dc - CPL;  // clamped: inactive lanes read valid memory, use dy = 0
   const int e = (int)(cc / s.hd);
   const int e_lo = (int)(span_c0 / s.hd);
-  const int BT = (int)s.BT;  // the host keeps every tensor below 4 GiB (32-bit byte offsets)
+  const int BT = (int)s.BT;  // the host keeps every tensor below 2 GiB (32-bit byte offsets)
   const int T = s.T;
 
   // per-lane bias: CPL*K contiguous bf16 at w0[cc*K], read as dwords with
@@ -471,8 +471,9 @@ BwdLayout bwd_headwise_layout(const Shape &s) {
 
 bool bwd_headwise_supported(const Shape &s) {
   if (s.kind != DYNCONV_HEADWISE || s.k > 4 || hw_cpl(s) == 0) return false;
-  // 32-bit byte offsets into x, dy, dx, u and the du partials
-  const int64_t lim = (int64_t)1 << 32;
+  // 32-bit byte offsets into x, dy, dx, u and the du partials, each tensor
+  // below 2 GiB like those of the other tuned kernels
+  const int64_t lim = ((int64_t)1 << 31) - 64;
   if (s.BT * s.D * 2 >= lim || s.BT * s.N * 4 >= lim) return false;
   const BwdLayout L = bwd_headwise_layout(s);
   return s.BT * L.R * 4 < ((int64_t)1 << 31) - 64;

@@ -1,6 +1,7 @@
 // simple_kernels.hip -- plain VALU kernels of the dynamic short convolution.
 //
-// One thread per output element (or per 16-byte output vector), fp32
+// One thread per output element (or per 16-byte output vector when rows are
+// whole vectors), fp32
 // accumulation in the order of each defining sum, no atomics.  They are the
 // fp32 path of the library (where bf16 MFMA would not meet fp32 accuracy)
 // and the general fallback for shapes the tuned bf16 kernels do not cover.
@@ -99,6 +100,38 @@ k_conv_dx_simple(Shape s, const float *__restrict__ gen, const T *__restrict__ U
       acc[i] = fmaf(filter_tap(s, gen, U, w0, row + j, c0 + i, j), gv[i], acc[i]);
   }
   store_vec(dx + row * s.D + c0, acc);
+}
+
+// The same two convolutions for any D, one thread per element (rows that are
+// not whole 16-byte vectors cannot be read as such).
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_conv_fwd_scalar(Shape s, const float *__restrict__ gen, const T *__restrict__ U,
+                  const T *__restrict__ w0, const T *__restrict__ x, T *__restrict__ y) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= s.BT * s.D) return;
+  const int64_t row = g / s.D;
+  const int64_t c = g - row * s.D;
+  const int64_t t = row % s.T;
+  float acc = to_f32(x[g]);
+  for (int j = 0; j < s.k && j <= t; ++j)
+    acc = fmaf(filter_tap(s, gen, U, w0, row, c, j), to_f32(x[g - j * s.D]), acc);
+  y[g] = from_f32<T>(acc);
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_conv_dx_scalar(Shape s, const float *__restrict__ gen, const T *__restrict__ U,
+                 const T *__restrict__ w0, const T *__restrict__ dy, T *__restrict__ dx) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= s.BT * s.D) return;
+  const int64_t row = g / s.D;
+  const int64_t c = g - row * s.D;
+  const int64_t t = row % s.T;
+  float acc = to_f32(dy[g]);
+  for (int j = 0; j < s.k && t + j <= s.T - 1; ++j)
+    acc = fmaf(filter_tap(s, gen, U, w0, row + j, c, j), to_f32(dy[g + j * s.D]), acc);
+  dx[g] = from_f32<T>(acc);
 }
 
 // G[row, c, j] = [t-j>=0] dy[row, c] x[row-j, c]
@@ -221,9 +254,14 @@ int simple_gen_proj(const Shape &s, const void *h, const void *M, float *out, hi
 template <typename T>
 int simple_fwd_conv(const Shape &s, const float *gen, const void *U, const void *w0, const void *x,
                     void *y, hipStream_t st) {
-  const int64_t n = s.BT * (s.D / Vec<T>::N);
-  hipLaunchKernelGGL(k_conv_fwd_simple<T>, grid1(n), dim3(256), 0, st, s, gen, (const T *)U,
-                     (const T *)w0, (const T *)x, (T *)y);
+  if (s.D % Vec<T>::N == 0) {
+    const int64_t n = s.BT * (s.D / Vec<T>::N);
+    hipLaunchKernelGGL(k_conv_fwd_simple<T>, grid1(n), dim3(256), 0, st, s, gen, (const T *)U,
+                       (const T *)w0, (const T *)x, (T *)y);
+  } else {
+    hipLaunchKernelGGL(k_conv_fwd_scalar<T>, grid1(s.BT * s.D), dim3(256), 0, st, s, gen, (const T *)U,
+                       (const T *)w0, (const T *)x, (T *)y);
+  }
   return 0;
 }
 
@@ -231,9 +269,14 @@ template <typename T>
 int simple_bwd(const Shape &s, const float *gen, const void *W, const void *A, const void *U,
                const void *w0, const void *h, const void *x, const void *dy, void *dx, void *dh,
                const dynconv_gen_grad &gg, float *g, hipStream_t st) {
-  const int64_t nv = s.BT * (s.D / Vec<T>::N);
-  hipLaunchKernelGGL(k_conv_dx_simple<T>, grid1(nv), dim3(256), 0, st, s, gen, (const T *)U,
-                     (const T *)w0, (const T *)dy, (T *)dx);
+  if (s.D % Vec<T>::N == 0) {
+    const int64_t nv = s.BT * (s.D / Vec<T>::N);
+    hipLaunchKernelGGL(k_conv_dx_simple<T>, grid1(nv), dim3(256), 0, st, s, gen, (const T *)U,
+                       (const T *)w0, (const T *)dy, (T *)dx);
+  } else {
+    hipLaunchKernelGGL(k_conv_dx_scalar<T>, grid1(s.BT * s.D), dim3(256), 0, st, s, gen, (const T *)U,
+                       (const T *)w0, (const T *)dy, (T *)dx);
+  }
   if (gg.dw0)
     hipLaunchKernelGGL(k_dw0_simple<T>, grid1(s.D * s.k), dim3(256), 0, st, s, (const T *)x,
                        (const T *)dy, gg.dw0);

@@ -24,13 +24,21 @@ def to_dev(inp: dict, device="cuda") -> dict:
     return {k: (None if v is None else v.to(device).contiguous()) for k, v in inp.items()}
 
 
-def gpu_run(w: Workload, dev_inp: dict, use_cache: bool = True, need_dh: bool = True):
-    """Forward + backward on the GPU; returns dict of device tensors."""
+def gpu_run(w: Workload, dev_inp: dict, use_cache: bool = True, need_dh: bool = True,
+            need_dw0: bool = True, fwd_cache: bool = True):
+    """Forward + backward on the GPU; returns dict of device tensors.
+
+    fwd_cache=False runs the forward without a caller cache (the library keeps
+    the generator values in its workspace); the backward then recomputes it.
+    """
     kw = dict(k=w.k, W=dev_inp.get("W"), A=dev_inp.get("A"), U=dev_inp.get("U"),
               w0=dev_inp.get("w0"), n_heads=w.n_heads)
-    y, cache = dc.dynconv_fwd(dev_inp["h"], dev_inp["x"], want_cache=True, **kw)
+    if fwd_cache:
+        y, cache = dc.dynconv_fwd(dev_inp["h"], dev_inp["x"], want_cache=True, **kw)
+    else:
+        y, cache = dc.dynconv_fwd(dev_inp["h"], dev_inp["x"], **kw), None
     g = dc.dynconv_bwd(dev_inp["h"], dev_inp["x"], dev_inp["dy"], gen_cache=cache if use_cache else None,
-                       need_dh=need_dh, need_dw0=dev_inp.get("w0") is not None, **kw)
+                       need_dh=need_dh, need_dw0=need_dw0 and dev_inp.get("w0") is not None, **kw)
     torch.cuda.synchronize()
     return {"y": y, "cache": cache, **g}
 

@@ -85,13 +85,53 @@ def bwd(L, p, g, h=addr(1), x=addr(2), dy=addr(3), cache=None, dx=addr(4), dh=ad
                          ws, ws_bytes, None)
 
 
+def test_any_width_is_accepted(L):
+    """D and d_model that are not whole 16-byte vectors are valid shapes (the
+    plain per-element kernels take them): sizes are reported for them."""
+    for D, d, n_heads, dt in ((100, 64, 4, dc.DYNCONV_BF16), (66, 60, 6, dc.DYNCONV_FP32),
+                              (128, 60, 4, dc.DYNCONV_BF16), (33, 7, 3, dc.DYNCONV_BF16)):
+        p = prob(D=D, d=d, dtype=dt)
+        for g in (gen_hw(n_heads=n_heads), gen_lr(rank=5)):
+            assert dc.dynconv_gen_cache_bytes(p, g) > 0, (D, d)
+            assert dc.dynconv_workspace_bytes(p, g, 0) > 0, (D, d)
+            assert dc.dynconv_workspace_bytes(p, g, 1) > 0, (D, d)
+
+
+def test_workspace_with_cache_has_no_cache_slot(L):
+    """A call that gets gen_cache needs no slot for it: the size with
+    DYNCONV_WS_CACHED is smaller by at least the cache bytes."""
+    C = dc.DYNCONV_WS_CACHED
+    for p, g in ((prob(B=4, T=512, d=256, D=512), gen_hw(n_heads=8)),
+                 (prob(B=4, T=512, d=256, D=512), gen_lr(rank=16)),
+                 (prob(B=2, T=100, d=32, D=64, dtype=dc.DYNCONV_FP32), gen_lr(rank=8))):
+        cache = dc.dynconv_gen_cache_bytes(p, g)
+        for pass_ in (0, 1):
+            full = dc.dynconv_workspace_bytes(p, g, pass_)
+            cached = dc.dynconv_workspace_bytes(p, g, pass_ | C)
+            assert 0 <= cached <= full - cache, (pass_, full, cached, cache)
+    assert dc.dynconv_workspace_bytes(prob(), gen_hw(), 4) == 0
+
+
+def test_call_checks_the_workspace_it_needs(L):
+    """With a cache the forward accepts the smaller workspace; without one it
+    rejects that size."""
+    p, g = prob(B=4, T=512, d=256, D=512), gen_hw(n_heads=8)
+    small = dc.dynconv_workspace_bytes(p, g, dc.DYNCONV_WS_CACHED)
+    full = dc.dynconv_workspace_bytes(p, g, 0)
+    assert small < full
+    # no cache: the smaller size is refused before anything is enqueued
+    assert fwd(L, p, g, cache=None, ws_bytes=small) == E_WORKSPACE
+    assert bwd(L, p, g, cache=None, ws_bytes=dc.dynconv_workspace_bytes(p, g, 1 | dc.DYNCONV_WS_CACHED)) \
+        == E_WORKSPACE
+
+
 def test_sizes(L):
     p, g = prob(), gen_hw()
     N = 4 * 4
     assert dc.dynconv_gen_cache_bytes(p, g) == 2 * 16 * N * 4
     assert dc.dynconv_workspace_bytes(p, g, 0) >= 0
     assert dc.dynconv_workspace_bytes(p, g, 1) > 0
-    assert dc.dynconv_workspace_bytes(p, g, 2) == 0
+    assert dc.dynconv_workspace_bytes(p, g, 5) == 0
     assert dc.dynconv_workspace_bytes(prob(k=9), g, 0) == 0
     assert dc.dynconv_gen_cache_bytes(prob(), gen_lr(rank=8)) == 2 * 16 * 8 * 4
 
@@ -99,7 +139,8 @@ def test_sizes(L):
 @pytest.mark.parametrize("case,expect", [
     ("null_problem", E_NULL), ("null_gen", E_NULL), ("bad_dtype", E_DTYPE), ("bad_kind", E_DTYPE),
     ("k0", E_K), ("k9", E_K), ("neg_B", E_SHAPE), ("d0", E_SHAPE), ("D_heads", E_SHAPE),
-    ("D_vec", E_SHAPE), ("d_vec", E_SHAPE), ("rank0", E_SHAPE), ("rank_limit", E_LIMIT),
+    ("D_odd_empty", OK), ("d_odd_empty", OK), ("D_odd_ws_small", E_WORKSPACE), ("rank0", E_SHAPE),
+    ("rank_limit", E_LIMIT),
     ("heads_limit", E_LIMIT), ("null_h", E_NULL), ("null_W", E_NULL), ("null_U", E_NULL),
     ("align_x", E_ALIGN), ("align_w0", E_ALIGN), ("alias_y_x", E_ALIAS),
     ("alias_cache_h", E_ALIAS), ("alias_ws_y", E_ALIAS), ("ws_small", E_WORKSPACE),
@@ -126,10 +167,13 @@ def test_fwd_validation(L, case, expect):
         p = prob(d=0)
     elif case == "D_heads":
         g = gen_hw(n_heads=3)
-    elif case == "D_vec":
-        p, g = prob(D=132), gen_hw(n_heads=4)
-    elif case == "d_vec":
-        p = prob(d=60)
+    elif case == "D_odd_empty":  # any D is accepted; no tokens, so nothing is launched
+        p, g = prob(B=0, D=132), gen_hw(n_heads=4)
+    elif case == "d_odd_empty":
+        p = prob(B=0, d=61)
+    elif case == "D_odd_ws_small":  # validated like any other shape
+        p, g = prob(D=100), gen_hw(n_heads=4)
+        kw["ws_bytes"] = 16
     elif case == "rank0":
         g = gen_lr(rank=0)
     elif case == "rank_limit":

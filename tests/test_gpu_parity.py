@@ -62,6 +62,13 @@ SMALL = [
     # across a sequence start are cut at load time), several sequences
     Workload("lr_bf16_r16_T96", B=3, T=96, d=64, D=192, k=4, kind=LOWRANK, rank=16, seed=35),
     Workload("lr_bf16_r32_k3_T64", B=3, T=64, d=64, D=256, k=3, kind=LOWRANK, rank=32, seed=36),
+    # widths that are not whole 16-byte vectors (plain per-element kernels)
+    Workload("hw_bf16_D100", B=2, T=75, d=64, D=100, k=4, kind=HEADWISE, n_heads=4, seed=51),
+    Workload("lr_bf16_D100", B=2, T=75, d=64, D=100, k=3, kind=LOWRANK, rank=16, seed=52),
+    Workload("hw_fp32_D66", B=2, T=60, d=32, D=66, k=4, kind=HEADWISE, n_heads=6, dtype="fp32", seed=53),
+    Workload("lr_fp32_D66_d30", B=1, T=50, d=30, D=66, k=2, kind=LOWRANK, rank=4, dtype="fp32", seed=54),
+    Workload("lr_bf16_d60", B=2, T=80, d=60, D=128, k=4, kind=LOWRANK, rank=16, seed=55),
+    Workload("hw_bf16_d60", B=2, T=80, d=60, D=256, k=4, kind=HEADWISE, n_heads=4, seed=56),
 ]
 
 
@@ -100,6 +107,44 @@ def test_parity_recompute_cache():
         for k in a:
             if a[k] is not None:
                 assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("w", [SMALL[0], SMALL[7], SMALL[12]], ids=["hw_bf16", "lr_bf16", "lr_fp32"])
+def test_forward_without_cache(w):
+    """The forward without a caller cache (generator values in the library's
+    workspace slot) gives the same y bitwise, and the backward that then
+    recomputes the cache the same gradients."""
+    _note(f"[no-cache fwd] {w.name}")
+    dev = gu.to_dev(workloads.generate(w))
+    a = gu.gpu_run(w, dev)
+    b = gu.gpu_run(w, dev, fwd_cache=False, use_cache=False)
+    for k in a:
+        if a[k] is not None and b.get(k) is not None:
+            assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("w", [SMALL[0], SMALL[2], SMALL[7], SMALL[8], SMALL[6], SMALL[12]],
+                         ids=["hw_hd72", "hw_hd68", "lr_r16", "lr_r32", "hw_fp32", "lr_fp32"])
+def test_optional_outputs(w):
+    """dh = NULL (the generator-weight gradient then runs without the dh
+    product, on another launch shape) and dw0 = NULL with a bias present: the
+    outputs still computed are bitwise those of the full backward, except dW
+    / dA, whose token split may differ without dh; those match the oracle."""
+    _note(f"[optional outputs] {w.name}")
+    inp = workloads.generate(w)
+    dev = gu.to_dev(inp)
+    full = gu.gpu_run(w, dev)
+    ref = gu.oracle_run(w, inp)
+    for need_dh, need_dw0 in ((False, True), (True, False), (False, False)):
+        part = gu.gpu_run(w, dev, need_dh=need_dh, need_dw0=need_dw0)
+        assert ("dh" in part) == need_dh and ("dw0" in part) == (need_dw0 and dev.get("w0") is not None)
+        for k in full:
+            if full[k] is None or k not in part:
+                continue
+            if k in ("dW", "dA"):
+                gu.compare(w, part, ref, keys=[k])
+            else:
+                assert torch.equal(full[k], part[k]), (k, need_dh, need_dw0)
 
 
 def test_deterministic():
@@ -208,6 +253,7 @@ def test_autograd_wrapper(w):
 
 
 DECODE = [SMALL[0], SMALL[7], SMALL[6], SMALL[12], SMALL[9], SMALL[5], SMALL[10], SMALL[4],
+          SMALL[22], SMALL[25],  # widths that are not whole 16-byte vectors
           # more than 1024 (sequence, 256-channel) blocks: four sequences per block, the
           # last block with one (161 = 4 * 40 + 1)
           Workload("dec_grouped_lr", B=161, T=6, d=64, D=2048, k=4, kind=LOWRANK, rank=16, seed=41),
@@ -228,7 +274,9 @@ def test_decode_steps_match_forward(w):
     steps = min(T, 48)
     state = torch.zeros(B, w.k - 1, D, dtype=dev["x"].dtype, device="cuda") if w.k > 1 else None
     kw = dict(k=w.k, W=dev.get("W"), A=dev.get("A"), U=dev.get("U"), w0=dev.get("w0"), n_heads=w.n_heads)
-    ys = [dc.dynconv_decode(dev["h"][:, t].contiguous(), dev["x"][:, t].contiguous(), state, **kw)
+    # (clone: a row of a one-sequence batch is already contiguous, and a view of it
+    # would start at an offset that is not 16-byte aligned, which the ABI rejects)
+    ys = [dc.dynconv_decode(dev["h"][:, t].clone(), dev["x"][:, t].clone(), state, **kw)
           for t in range(steps)]
     torch.cuda.synchronize()
     y = torch.stack(ys, 1).float().cpu().numpy()

@@ -93,8 +93,10 @@ WORKLOADS = {
     ]
 }
 
-# The workload the benchmark times: QKV placement at the ~150M-model shape.
-BENCH_WORKLOAD = "qkv_150m_lowrank"
+# The workload the benchmark times by default: the largest one that fits one
+# GPU, the Mamba-2 input convolution (B=2, T=16384, D=4352, 1.83 GB of
+# algorithmic traffic per fwd+bwd step).  The others run with --workload.
+BENCH_WORKLOAD = "mamba2_inconv_headwise"
 
 
 def generate(w: Workload, with_dy: bool = True) -> dict:
