@@ -51,8 +51,10 @@
  * not be used by anything else until the enqueued work has finished.
  * Results are bitwise deterministic for fixed inputs and shapes (no float
  * atomics; every reduction runs in a fixed order).  The library is
- * thread-safe; its only global state is the one-shot event pair that
- * dynconv_trace_next arms, kept per host thread.
+ * thread-safe.  Its global state is the one-shot event pair that
+ * dynconv_trace_next arms, kept per host thread, and the static scratch of
+ * dynconv_fwd_noalloc (one array per GPU, with a mutex-guarded table of its
+ * per-GPU addresses).
  *
  * Errors: every call returns DYNCONV_OK (0) or a negative status.  Argument
  * errors are detected on the host before anything is enqueued, and the
@@ -103,7 +105,9 @@ enum {
   DYNCONV_E_ALIAS = -6,     /* an output overlaps an input or another output      */
   DYNCONV_E_WORKSPACE = -7, /* workspace NULL or smaller than required            */
   DYNCONV_E_HIP = -8,       /* a kernel launch failed                             */
-  DYNCONV_E_LIMIT = -9      /* a size exceeds what the kernels index (see below)  */
+  DYNCONV_E_LIMIT = -9,     /* a size exceeds what the kernels index (see below)  */
+  DYNCONV_E_SCRATCH = -10   /* dynconv_fwd_noalloc: the call needs more workspace */
+                            /* than its static scratch holds                      */
 };
 
 /* Problem sizes.  B*T tokens, hidden width d_model, D convolved channels,
@@ -149,6 +153,27 @@ typedef struct {
 DYNCONV_API int dynconv_fwd(const dynconv_problem *p, const dynconv_gen *g, const void *h, const void *x,
                 void *y, void *gen_cache, void *workspace, size_t workspace_bytes,
                 hipStream_t stream);
+
+/*
+ * Forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation):
+ * dynconv_fwd with the same arguments except the workspace, which is a
+ * static device array of DYNCONV_NOALLOC_SCRATCH_BYTES inside the library.
+ * The call itself allocates nothing (no hipMalloc or hipFree, no allocating
+ * library routine).  Each GPU the library runs on holds one such array from
+ * its first use until the process ends; the call runs on the current device
+ * (`stream` must belong to it).  All calls on one GPU share that GPU's
+ * array, so calls that overlap in time on one GPU race and must be
+ * serialised by the caller (one stream, or events).  Nothing in the array
+ * needs to start at zero: the forward writes every byte it later reads.
+ * Returns DYNCONV_E_SCRATCH, enqueuing nothing, when the forward needs more
+ * workspace than the array holds (dynconv_workspace_bytes with pass 0, or
+ * DYNCONV_WS_CACHED with a caller cache, tells how much it needs); all
+ * other errors as for dynconv_fwd.  The results equal dynconv_fwd's bitwise.
+ */
+#define DYNCONV_NOALLOC_SCRATCH_BYTES (16u << 20)
+DYNCONV_API int dynconv_fwd_noalloc(const dynconv_problem *p, const dynconv_gen *g, const void *h,
+                                    const void *x, void *y, void *gen_cache, hipStream_t stream);
 
 /*
  * Backward of L = sum(dy * y) for the forward above.

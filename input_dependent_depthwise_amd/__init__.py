@@ -52,8 +52,10 @@ class GenGrad(ctypes.Structure):
 
 
 # names the C header declares; the CPU tests check each is exported
-EXPORTS = ("dynconv_fwd", "dynconv_bwd", "dynconv_decode", "dynconv_workspace_bytes", "dynconv_gen_cache_bytes",
-           "dynconv_status_str", "dynconv_abi_version", "dynconv_trace_next")
+EXPORTS = ("dynconv_fwd", "dynconv_fwd_noalloc", "dynconv_bwd", "dynconv_decode", "dynconv_workspace_bytes",
+           "dynconv_gen_cache_bytes", "dynconv_status_str", "dynconv_abi_version", "dynconv_trace_next")
+DYNCONV_E_SCRATCH = -10
+NOALLOC_SCRATCH_BYTES = 16 << 20  # the static scratch of dynconv_fwd_noalloc
 
 # kernel ids for dynconv_trace_next
 DYNCONV_K_GEN_PROJ, DYNCONV_K_FWD_CONV, DYNCONV_K_BWD_CONV, DYNCONV_K_GEN_BWD, DYNCONV_K_FINALIZE = 1, 2, 3, 4, 5
@@ -73,6 +75,8 @@ def lib() -> ctypes.CDLL:
         PP, PG, PGG = ctypes.POINTER(Problem), ctypes.POINTER(Gen), ctypes.POINTER(GenGrad)
         L.dynconv_fwd.argtypes = [PP, PG, P, P, P, P, P, ctypes.c_size_t, P]
         L.dynconv_fwd.restype = ctypes.c_int
+        L.dynconv_fwd_noalloc.argtypes = [PP, PG, P, P, P, P, P]
+        L.dynconv_fwd_noalloc.restype = ctypes.c_int
         L.dynconv_bwd.argtypes = [PP, PG, P, P, P, P, P, P, PGG, P, ctypes.c_size_t, P]
         L.dynconv_bwd.restype = ctypes.c_int
         L.dynconv_decode.argtypes = [PP, PG, P, P, P, P, P]
@@ -179,6 +183,21 @@ def dynconv_fwd(h, x, *, k, W=None, A=None, U=None, w0=None, n_heads=0, y=None, 
                            _stream(stream))
     _check(rc, "dynconv_fwd")
     return (y, gen_cache) if want_cache else y
+
+
+def dynconv_fwd_noalloc(h, x, *, k, W=None, A=None, U=None, w0=None, n_heads=0, y=None, gen_cache=None,
+                        stream=None):
+    """Forward whose workspace is the library's static scratch (no workspace
+    argument).  y and gen_cache, when not given, are allocated here by torch,
+    outside the library call; pass them for a call that allocates nothing."""
+    prob = make_problem(x, h, k)
+    gen = make_gen(W, A, U, w0, n_heads)
+    if y is None:
+        y = torch.empty_like(x)
+    rc = lib().dynconv_fwd_noalloc(ctypes.byref(prob), ctypes.byref(gen), _ptr(h), _ptr(x), _ptr(y),
+                                   _ptr(gen_cache), _stream(stream))
+    _check(rc, "dynconv_fwd_noalloc")
+    return y
 
 
 def dynconv_bwd(h, x, dy, *, k, W=None, A=None, U=None, w0=None, n_heads=0, gen_cache=None,

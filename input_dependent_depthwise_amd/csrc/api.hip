@@ -4,11 +4,17 @@
 // Nothing here allocates, frees, copies or synchronises.  Every entry point
 // validates everything before it enqueues anything, so a rejected call
 // leaves all outputs untouched.
+#include <mutex>
 #include <new>
 
 #include "kernels.h"
 
 namespace dynconv {
+
+// Bytes of the static scratch that dynconv_fwd_noalloc uses as its workspace.
+constexpr size_t kScratchBytes = (size_t)DYNCONV_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
 
 constexpr size_t kAlign = 256;  // sub-buffers of the workspace start on 256-byte boundaries
@@ -167,6 +173,82 @@ int gen_proj(const Shape &s, int dtype, const dynconv_gen *g, const void *h, flo
   return simple_gen_proj<float>(s, h, M, cache, st);
 }
 
+// Validates a forward call and plans its workspace.  check_ws = false: the
+// workspace is the library's static scratch (checked against its size by
+// the caller; it cannot overlap a caller's tensor).
+int fwd_validate(const dynconv_problem *p, const dynconv_gen *g, const void *h, const void *x, void *y,
+                 void *gen_cache, const void *workspace, size_t workspace_bytes, bool check_ws, Shape &s,
+                 Plan &pl) {
+  int rc = check_problem(p, g, s);
+  if (rc) return rc;
+  if (s.BT == 0) return DYNCONV_OK;
+  if (!h || !x || !y) return DYNCONV_E_NULL;
+  if ((rc = check_weights(s, g))) return rc;
+  const void *ptrs[] = {h, x, y, gen_cache, workspace};
+  for (const void *q : ptrs)
+    if (q && !aligned16(q)) return DYNCONV_E_ALIGN;
+  pl = plan(s, p->dtype, 0, gen_cache != nullptr);
+  if (check_ws && (workspace_bytes < pl.total || (pl.total > 0 && !workspace))) return DYNCONV_E_WORKSPACE;
+  const int eb = p->dtype == DYNCONV_BF16 ? 2 : 4;
+  const Sizes z = sizes(s, eb);
+  const Range ins[] = {{h, z.h}, {x, z.x}, {g->W, z.W}, {g->A, z.A}, {g->U, z.U},
+                       {g->w0, g->w0 ? z.w0 : 0}};
+  const Range outs[] = {{y, z.x}, {gen_cache, gen_cache ? z.cache : 0},
+                        {check_ws ? workspace : nullptr, pl.total}};
+  for (const Range &o : outs) {
+    for (const Range &i : ins)
+      if (overlap(o, i)) return DYNCONV_E_ALIAS;
+  }
+  for (int a = 0; a < 3; ++a)
+    for (int b = a + 1; b < 3; ++b)
+      if (overlap(outs[a], outs[b])) return DYNCONV_E_ALIAS;
+  return DYNCONV_OK;
+}
+
+// Enqueues a validated forward: projection into the cache (the caller's, or
+// the workspace slot), then filter formation + conv + residual.
+int fwd_launch(const Shape &s, int dtype, const dynconv_gen *g, const void *h, const void *x, void *y,
+               void *gen_cache, void *workspace, const Plan &pl, hipStream_t stream) {
+  float *cache = gen_cache ? (float *)gen_cache : (float *)((char *)workspace + pl.cache);
+  int rc = gen_proj(s, dtype, g, h, cache, workspace, pl, stream);
+  if (rc) return rc;
+  if (s.kind == DYNCONV_HEADWISE && vec_rows(s, dtype)) {
+    rc = dtype == DYNCONV_BF16 ? fwd_headwise<bf16>(s, cache, g->w0, x, y, stream)
+                               : fwd_headwise<float>(s, cache, g->w0, x, y, stream);
+  } else if (fast_lowrank(s, dtype)) {
+    rc = fwd_lowrank(s, cache, g->U, g->w0, x, y, stream);
+  } else if (dtype == DYNCONV_BF16) {
+    rc = simple_fwd_conv<bf16>(s, cache, g->U, g->w0, x, y, stream);
+  } else {
+    rc = simple_fwd_conv<float>(s, cache, g->U, g->w0, x, y, stream);
+  }
+  if (rc) return rc;
+  return launch_status();
+}
+
+// --- the static scratch of dynconv_fwd_noalloc --------------------------
+// Every GPU the library runs on holds one copy of this array (loaded with
+// the library's device code) until the process ends.  In host code its name
+// is only a host-side stand-in: its device address, which differs per GPU,
+// comes from hipGetSymbolAddress with that GPU current, and only that
+// address is passed to kernels.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];
+
+int scratch_ptr(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DYNCONV_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return DYNCONV_E_HIP;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return DYNCONV_OK;
+}
+
 }  // namespace
 
 // One-shot event pair armed by dynconv_trace_next (per host thread).
@@ -222,6 +304,7 @@ const char *dynconv_status_str(int status) {
     case DYNCONV_E_WORKSPACE: return "workspace missing or too small";
     case DYNCONV_E_HIP: return "kernel launch failed";
     case DYNCONV_E_LIMIT: return "a size exceeds the library's limits";
+    case DYNCONV_E_SCRATCH: return "the call needs more workspace than the static scratch of dynconv_fwd_noalloc holds";
     default: return "unknown status";
   }
 }
@@ -243,43 +326,22 @@ int dynconv_fwd(const dynconv_problem *p, const dynconv_gen *g, const void *h, c
                 void *y, void *gen_cache, void *workspace, size_t workspace_bytes,
                 hipStream_t stream) {
   Shape s;
-  int rc = check_problem(p, g, s);
-  if (rc) return rc;
-  if (s.BT == 0) return DYNCONV_OK;
-  if (!h || !x || !y) return DYNCONV_E_NULL;
-  if ((rc = check_weights(s, g))) return rc;
-  const void *ptrs[] = {h, x, y, gen_cache, workspace};
-  for (const void *q : ptrs)
-    if (q && !aligned16(q)) return DYNCONV_E_ALIGN;
-  const Plan pl = plan(s, p->dtype, 0, gen_cache != nullptr);
-  if (workspace_bytes < pl.total || (pl.total > 0 && !workspace)) return DYNCONV_E_WORKSPACE;
-  const int eb = p->dtype == DYNCONV_BF16 ? 2 : 4;
-  const Sizes z = sizes(s, eb);
-  const Range ins[] = {{h, z.h}, {x, z.x}, {g->W, z.W}, {g->A, z.A}, {g->U, z.U},
-                       {g->w0, g->w0 ? z.w0 : 0}};
-  const Range outs[] = {{y, z.x}, {gen_cache, gen_cache ? z.cache : 0}, {workspace, pl.total}};
-  for (const Range &o : outs) {
-    for (const Range &i : ins)
-      if (overlap(o, i)) return DYNCONV_E_ALIAS;
-  }
-  for (int a = 0; a < 3; ++a)
-    for (int b = a + 1; b < 3; ++b)
-      if (overlap(outs[a], outs[b])) return DYNCONV_E_ALIAS;
+  Plan pl;
+  int rc = fwd_validate(p, g, h, x, y, gen_cache, workspace, workspace_bytes, true, s, pl);
+  if (rc || s.BT == 0) return rc;
+  return fwd_launch(s, p->dtype, g, h, x, y, gen_cache, workspace, pl, stream);
+}
 
-  float *cache = gen_cache ? (float *)gen_cache : (float *)((char *)workspace + pl.cache);
-  if ((rc = gen_proj(s, p->dtype, g, h, cache, workspace, pl, stream))) return rc;
-  if (s.kind == DYNCONV_HEADWISE && vec_rows(s, p->dtype)) {
-    rc = p->dtype == DYNCONV_BF16 ? fwd_headwise<bf16>(s, cache, g->w0, x, y, stream)
-                                  : fwd_headwise<float>(s, cache, g->w0, x, y, stream);
-  } else if (fast_lowrank(s, p->dtype)) {
-    rc = fwd_lowrank(s, cache, g->U, g->w0, x, y, stream);
-  } else if (p->dtype == DYNCONV_BF16) {
-    rc = simple_fwd_conv<bf16>(s, cache, g->U, g->w0, x, y, stream);
-  } else {
-    rc = simple_fwd_conv<float>(s, cache, g->U, g->w0, x, y, stream);
-  }
-  if (rc) return rc;
-  return launch_status();
+int dynconv_fwd_noalloc(const dynconv_problem *p, const dynconv_gen *g, const void *h, const void *x, void *y,
+                        void *gen_cache, hipStream_t stream) {
+  Shape s;
+  Plan pl;
+  int rc = fwd_validate(p, g, h, x, y, gen_cache, nullptr, 0, false, s, pl);
+  if (rc || s.BT == 0) return rc;
+  if (pl.total > kScratchBytes) return DYNCONV_E_SCRATCH;
+  void *ws = nullptr;
+  if ((rc = scratch_ptr(&ws))) return rc;
+  return fwd_launch(s, p->dtype, g, h, x, y, gen_cache, ws, pl, stream);
 }
 
 int dynconv_decode(const dynconv_problem *p, const dynconv_gen *g, const void *h, const void *x, void *state,

@@ -16,8 +16,8 @@ from input_dependent_depthwise_amd import Gen, GenGrad, Problem
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "dynconv.h")
 
-OK, E_NULL, E_SHAPE, E_K, E_DTYPE, E_ALIGN, E_ALIAS, E_WORKSPACE, E_HIP, E_LIMIT = (
-    0, -1, -2, -3, -4, -5, -6, -7, -8, -9)
+OK, E_NULL, E_SHAPE, E_K, E_DTYPE, E_ALIGN, E_ALIAS, E_WORKSPACE, E_HIP, E_LIMIT, E_SCRATCH = (
+    0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10)
 
 
 @pytest.fixture(scope="module")
@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(L):
 
 def test_version_and_status_strings(L):
     assert dc.dynconv_abi_version() == 1
-    for code in (OK, E_NULL, E_SHAPE, E_K, E_DTYPE, E_ALIGN, E_ALIAS, E_WORKSPACE, E_HIP, E_LIMIT):
+    for code in (OK, E_NULL, E_SHAPE, E_K, E_DTYPE, E_ALIGN, E_ALIAS, E_WORKSPACE, E_HIP, E_LIMIT, E_SCRATCH):
         s = dc.dynconv_status_str(code)
         assert s and s != "unknown status"
     assert dc.dynconv_status_str(-1234) == "unknown status"
@@ -284,3 +284,36 @@ def test_decode_validation(L, case, expect):
     elif case == "empty":
         p = prob(B=0, T=1)
     assert dec(L, p, g, **kw) == expect
+
+
+def fwd_na(L, p, g, h=addr(1), x=addr(2), y=addr(3), cache=None):
+    return L.dynconv_fwd_noalloc(ctypes.byref(p), ctypes.byref(g), h, x, y, cache, None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_x", E_NULL), ("align_y", E_ALIGN), ("alias_y_h", E_ALIAS), ("k9", E_K), ("empty", OK),
+    ("too_big_no_cache", E_SCRATCH),
+])
+def test_fwd_noalloc_validation(L, case, expect):
+    """dynconv_fwd_noalloc validates like dynconv_fwd on the host, and refuses
+    (before enqueuing anything) a call whose workspace would not fit its
+    static scratch."""
+    p, g = prob(), gen_hw()
+    kw = {}
+    if case == "null_x":
+        kw["x"] = None
+    elif case == "align_y":
+        kw["y"] = addr(3) + 8
+    elif case == "alias_y_h":
+        kw["y"] = addr(1) + 512
+    elif case == "k9":
+        p = prob(k=9)
+    elif case == "empty":
+        p = prob(B=0)
+    elif case == "too_big_no_cache":
+        # 32768 tokens x 256 generator values x 4 bytes of cache slot: 32 MiB
+        p, g = prob(B=2, T=16384, d=2048, D=4352), gen_hw(n_heads=64)
+        assert dc.dynconv_workspace_bytes(p, g, 0) > dc.NOALLOC_SCRATCH_BYTES
+        assert dc.dynconv_workspace_bytes(p, g, dc.DYNCONV_WS_CACHED) <= dc.NOALLOC_SCRATCH_BYTES
+        kw = dict(h=BASE, x=BASE + (1 << 30), y=BASE + (2 << 30))  # tensors this large must not overlap
+    assert fwd_na(L, p, g, **kw) == expect
