@@ -417,6 +417,7 @@ void launch_nt(const bf16 *h, const bf16 *Mt, float *out, int64_t M, int K, int 
 }  // namespace
 
 size_t gen_proj_mfma_ws_bytes(const Shape &s) {
+  if (gen_proj_wide_ok(s)) return 0;
   const int Np = (int)ceil_div(s.N, 16) * 16;
   const int Kp = (int)ceil_div(s.d, 32) * 32;
   return (size_t)Np * Kp * sizeof(bf16);
@@ -439,6 +440,7 @@ int gen_proj_mfma(const Shape &s, const void *h, const void *M, float *out, void
     trace_end(tr, st);
     return 0;
   }
+  if (gen_proj_wide_ok(s)) return gen_proj_wide(s, h, M, out, st);
   bf16 *Mt = (bf16 *)ws;
   hipLaunchKernelGGL(k_transpose_pad, dim3((unsigned)ceil_div((int64_t)Np * Kp, 256)), dim3(256), 0, st,
                      (const bf16 *)M, Mt, K, N, Kp, Np);

@@ -32,6 +32,9 @@ int decode_step(const Shape &s, const void *h, const void *W, const void *A, con
 // --- bf16 matrix-core generator projection (gen_mfma.hip) ---
 size_t gen_proj_mfma_ws_bytes(const Shape &s);
 int gen_proj_mfma(const Shape &s, const void *h, const void *M, float *out, void *ws, hipStream_t st);
+// wide weights (N a multiple of 8, 64..256 columns), read in place (gen_proj_wide.hip)
+bool gen_proj_wide_ok(const Shape &s);
+int gen_proj_wide(const Shape &s, const void *h, const void *M, float *out, hipStream_t st);
 
 // --- head-wise forward conv, coalesced per-vector walk (conv_fwd_headwise.hip) ---
 template <typename T>

@@ -69,6 +69,13 @@ SMALL = [
     Workload("lr_fp32_D66_d30", B=1, T=50, d=30, D=66, k=2, kind=LOWRANK, rank=4, dtype="fp32", seed=54),
     Workload("lr_bf16_d60", B=2, T=80, d=60, D=128, k=4, kind=LOWRANK, rank=16, seed=55),
     Workload("hw_bf16_d60", B=2, T=80, d=60, D=256, k=4, kind=HEADWISE, n_heads=4, seed=56),
+    # wide generator weights read in place (n_heads*k a multiple of 8, 64..256 columns): a
+    # K tail (d_model 200, 136), ragged row blocks, columns padded to the 32-column tile (72)
+    Workload("hw_bf16_N256_ragged", B=1, T=333, d=200, D=512, k=4, kind=HEADWISE, n_heads=64, seed=57),
+    Workload("hw_bf16_N72", B=2, T=150, d=136, D=1152, k=4, kind=HEADWISE, n_heads=18, seed=58),
+    # more wide weights: 96 and 160 columns with d_model tails (200, 136)
+    Workload("hw_bf16_N96_d200", B=2, T=333, d=200, D=768, k=4, kind=HEADWISE, n_heads=24, seed=59),
+    Workload("hw_bf16_N160_d136", B=1, T=200, d=136, D=1280, k=4, kind=HEADWISE, n_heads=40, seed=60),
 ]
 
 
