@@ -49,7 +49,8 @@ def build(force: bool = True) -> str:
 class _Shape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("d", ctypes.c_int64),
                 ("D", ctypes.c_int64), ("k", ctypes.c_int32), ("kind", ctypes.c_int32),
-                ("n_heads", ctypes.c_int32), ("rank", ctypes.c_int32)]
+                ("n_heads", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("doc", ctypes.POINTER(ctypes.c_int64))]
 
 
 class OracleLib:
@@ -158,9 +159,29 @@ class Shape:
     kind: int          # HEADWISE or LOWRANK
     n_heads: int = 0
     rank: int = 0
+    # packed documents: offsets 0 = c_0 <= c_1 <= ... <= c_n = B*T of the
+    # documents in the flattened tokens (None: one document per batch row)
+    cu_seqlens: tuple | None = None
+
+    def doc_index(self):
+        """Document index of every token ([B*T] int64), or None."""
+        if self.cu_seqlens is None:
+            return None
+        cu = [int(c) for c in self.cu_seqlens]
+        if cu[0] != 0 or cu[-1] != self.B * self.T or any(b < a for a, b in zip(cu, cu[1:])):
+            raise ValueError(f"cu_seqlens must rise from 0 to B*T = {self.B * self.T}: {cu}")
+        doc = np.empty(self.B * self.T, dtype=np.int64)
+        for i in range(len(cu) - 1):
+            doc[cu[i]:cu[i + 1]] = i
+        return doc
 
     def _c(self) -> _Shape:
-        return _Shape(self.B, self.T, self.d, self.D, self.k, self.kind, self.n_heads, self.rank)
+        c = _Shape(self.B, self.T, self.d, self.D, self.k, self.kind, self.n_heads, self.rank, None)
+        doc = self.doc_index()
+        if doc is not None:
+            c._doc = doc  # keeps the array alive as long as the struct
+            c.doc = doc.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+        return c
 
     @property
     def gen_cols(self) -> int:

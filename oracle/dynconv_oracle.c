@@ -41,6 +41,17 @@
  * bias w0 is per channel [D,k] and applies to both parameterisations; there
  * is no nonlinearity anywhere in the layer.
  *
+ * Packed documents: a batch row may hold several documents back to back
+ * (shape field doc: the document index of every token, or NULL for one
+ * document per row).  The causal window then stops at the start of each
+ * document exactly as it stops at the start of a row: a term that would
+ * reach a token of another document counts as zero.  So in every test
+ * above, "t-j >= 0" reads "t-j >= 0 and token t-j is in t's document", and
+ * "s+j <= T-1" reads "s+j <= T-1 and token s+j is in s's document".  (The
+ * pages are silent on packing; one of their off-subject abstracts names
+ * document packing as the practical obstacle for convolutions, and the
+ * Mechanism item fixes only that the window looks back.)
+ *
  * Everything is fp64, row-major and contiguous:
  *   h[B,T,d]  x,y,dy,dx[B,T,D]  W[d, n_heads*k]  A[d,r]  U[r, D*k]  w0[D,k]
  *   w[B,T,D,k] (materialised here on purpose: this is the plain path)
@@ -59,7 +70,14 @@ enum { ORC_HEADWISE = 0, ORC_LOWRANK = 1 };
 typedef struct {
   int64_t B, T, d, D;
   int32_t k, kind, n_heads, rank;
+  const int64_t *doc; /* [B*T] document index of each token, or NULL: one document per row */
 } orc_shape;
+
+/* Whether token rows r1 and r2 (flat indices into [B*T]) lie in one document;
+ * the callers only ask about two rows of the same batch row. */
+static int same_doc(const orc_shape *s, int64_t r1, int64_t r2) {
+  return s->doc == NULL || s->doc[r1] == s->doc[r2];
+}
 
 enum { ORC_OK = 0, ORC_E_SHAPE = -1, ORC_E_NULL = -2 };
 
@@ -157,7 +175,7 @@ int orc_conv(const orc_shape *s, const double *w, const double *x, double *y) {
       for (int64_t c = 0; c < D; ++c) {
         double acc = x[row * D + c];
         for (int64_t j = 0; j < k; ++j) {
-          if (t - j < 0) break;
+          if (t - j < 0 || !same_doc(s, row, row - j)) break;
           acc += wt[c * k + j] * x[(row - j) * D + c];
         }
         y[row * D + c] = acc;
@@ -193,7 +211,7 @@ int orc_backward(const orc_shape *s, const double *h, const double *W,
         for (int64_t c = 0; c < D; ++c) {
           double acc = dy[row * D + c];
           for (int64_t j = 0; j < k; ++j) {
-            if (t + j > T - 1) break;
+            if (t + j > T - 1 || !same_doc(s, row, row + j)) break;
             acc += w[(row + j) * D * k + c * k + j] * dy[(row + j) * D + c];
           }
           dx[row * D + c] = acc;
@@ -201,11 +219,11 @@ int orc_backward(const orc_shape *s, const double *h, const double *W,
       }
   }
 
-  /* G_t[c,j] = [t-j>=0] dy_t[c] x_{t-j}[c], written out as a function. */
+  /* G_t[c,j] = [t-j>=0, same document] dy_t[c] x_{t-j}[c], written out as a function. */
 #define G_AT(b_, t_, c_, j_)                                                   \
-  (((t_) - (j_) < 0) ? 0.0                                                     \
-                     : dy[((b_) * T + (t_)) * D + (c_)] *                      \
-                           x[((b_) * T + (t_) - (j_)) * D + (c_)])
+  (((t_) - (j_) < 0 || !same_doc(s, (b_) * T + (t_), (b_) * T + (t_) - (j_)))  \
+       ? 0.0                                                                   \
+       : dy[((b_) * T + (t_)) * D + (c_)] * x[((b_) * T + (t_) - (j_)) * D + (c_)])
 
   if (dw0) {
 #pragma omp parallel for schedule(static)

@@ -24,8 +24,17 @@ MUTANTS = [
     ("fwd_drops_residual", "double acc = x[row * D + c];", "double acc = 0.0;"),
     ("fwd_flips_taps", "acc += wt[c * k + j] * x[(row - j) * D + c];",
      "acc += wt[c * k + (k - 1 - j)] * x[(row - j) * D + c];"),
-    ("fwd_drops_lag0_history", "if (t - j < 0) break;\n          acc += wt",
-     "if (t - j < 1 && j > 0) break;\n          acc += wt"),
+    ("fwd_drops_lag0_history", "if (t - j < 0 || !same_doc(s, row, row - j)) break;\n          acc += wt",
+     "if ((t - j < 1 && j > 0) || !same_doc(s, row, row - j)) break;\n          acc += wt"),
+    # packed documents: the window crosses a document start
+    ("packed_fwd_ignores_documents", "if (t - j < 0 || !same_doc(s, row, row - j)) break;",
+     "if (t - j < 0) break;"),
+    ("packed_dx_ignores_documents", "if (t + j > T - 1 || !same_doc(s, row, row + j)) break;",
+     "if (t + j > T - 1) break;"),
+    ("packed_G_ignores_documents", "(((t_) - (j_) < 0 || !same_doc(s, (b_) * T + (t_), (b_) * T + (t_) - (j_)))",
+     "(((t_) - (j_) < 0)"),
+    ("packed_doc_off_by_one", "return s->doc == NULL || s->doc[r1] == s->doc[r2];",
+     "return s->doc == NULL || s->doc[r1] == s->doc[r2 > 0 ? r2 - 1 : r2];"),
     ("head_index_interleaved", "const int64_t e = c / hd;", "const int64_t e = c % s->n_heads;"),
     ("lowrank_U_transposed", "for (int64_t m = 0; m < D * k; ++m) wt[m] += zq * Uq[m];",
      "for (int64_t m = 0; m < D * k; ++m) wt[m] += zq * U[m * N + q];"),
@@ -68,6 +77,8 @@ def _battery(orc):
         run(f"autograd:{s}", P.test_grads_match_torch_autograd, s)
         run(f"causal:{s}", P.test_causality, s)
     run("hw==lr", P.test_headwise_equals_lowrank)
+    for base, lens in P.PACKED:
+        run(f"packed:{lens}", P.test_packed_equals_documents_run_alone, base, lens)
     return failed
 
 

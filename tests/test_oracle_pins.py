@@ -288,3 +288,91 @@ def test_adjoint_identity(orc, s):
         lhs = pins.loss(orc, s, q) - L0
         rhs = float((bw[gname].reshape(delta.shape) * delta).sum())
         assert abs(lhs - rhs) <= 1e-9 * max(1.0, abs(rhs)), (leaf, lhs, rhs)
+
+
+# ---------------------------------------------------------------------------
+# packed documents: a row holding several documents back to back is the
+# documents run alone (the window never reaches across a document start)
+# ---------------------------------------------------------------------------
+PACKED = [
+    # (shape with T unset, document lengths): lengths below k, of one token,
+    # and an empty document
+    (Shape(B=1, T=0, d=5, D=8, k=4, kind=HEADWISE, n_heads=4), (1, 6, 2, 3, 9)),
+    (Shape(B=1, T=0, d=4, D=6, k=3, kind=LOWRANK, rank=3), (5, 1, 1, 7, 4)),
+    (Shape(B=1, T=0, d=3, D=4, k=8, kind=HEADWISE, n_heads=2), (10, 3, 0, 8)),
+]
+
+
+def _packed_shape(base: Shape, lens) -> Shape:
+    from dataclasses import replace
+    cu = tuple(int(c) for c in np.cumsum((0,) + tuple(lens)))
+    return replace(base, T=cu[-1], cu_seqlens=cu)
+
+
+GRADS = ("dW", "dA", "dU", "dw0")
+
+
+@pytest.mark.parametrize("base,lens", PACKED, ids=[f"{'hw' if b.kind == HEADWISE else 'lr'}-{l}" for b, l in PACKED])
+def test_packed_equals_documents_run_alone(orc, base, lens):
+    """Per-token outputs (y, the generator values, dx, dh) of the packed row
+    equal bitwise those of each document run as its own sequence; the weight
+    gradients are the sums of the documents' (up to summation order)."""
+    from dataclasses import replace
+    s = _packed_shape(base, lens)
+    rng = np.random.default_rng(21)
+    p = pins.random_problem(rng, s)
+    fw = orc.forward(s, p["h"], p["x"], **pins.gen_args(p))
+    bw = orc.backward(s, p["h"], p["x"], p["dy"], **pins.gen_args(p))
+    total = {g: None for g in GRADS}
+    t0 = 0
+    for L in lens:
+        if L == 0:
+            continue
+        sd = replace(base, T=L)
+        q = {k: (None if v is None else (v[t0:t0 + L] if k in ("h", "x", "dy") else v)) for k, v in p.items()}
+        fd = orc.forward(sd, q["h"], q["x"], **pins.gen_args(q))
+        bd = orc.backward(sd, q["h"], q["x"], q["dy"], **pins.gen_args(q))
+        assert np.array_equal(np.asarray(fw["y"])[t0:t0 + L], np.asarray(fd["y"]))
+        assert np.array_equal(np.asarray(fw["gen"])[t0:t0 + L], np.asarray(fd["gen"]))
+        for key in ("dx", "dh"):
+            assert np.array_equal(np.asarray(bw[key])[t0:t0 + L], np.asarray(bd[key])), key
+        for g in GRADS:
+            if bd.get(g) is not None:
+                total[g] = bd[g] if total[g] is None else total[g] + bd[g]
+        t0 += L
+    for g in GRADS:
+        if total[g] is not None:
+            np.testing.assert_allclose(bw[g], total[g], rtol=1e-12, atol=1e-12, err_msg=g)
+
+
+@pytest.mark.parametrize("s", SHAPES[1:2] + SHAPES[3:4], ids=_ids(SHAPES[1:2] + SHAPES[3:4]))
+def test_one_document_is_the_plain_row(orc, s):
+    """A single document covering the row changes nothing, bitwise."""
+    from dataclasses import replace
+    rng = np.random.default_rng(22)
+    p = pins.random_problem(rng, s)
+    sp = replace(s, cu_seqlens=(0, s.B * s.T))
+    for a, b in ((orc.forward(s, p["h"], p["x"], **pins.gen_args(p)),
+                  orc.forward(sp, p["h"], p["x"], **pins.gen_args(p))),
+                 (orc.backward(s, p["h"], p["x"], p["dy"], **pins.gen_args(p)),
+                  orc.backward(sp, p["h"], p["x"], p["dy"], **pins.gen_args(p)))):
+        for key in a:
+            if a[key] is not None:
+                assert np.array_equal(np.asarray(a[key]), np.asarray(b[key])), key
+
+
+@pytest.mark.parametrize("s", [sh for sh in SHAPES if sh.B > 1], ids=_ids([sh for sh in SHAPES if sh.B > 1]))
+def test_equal_documents_are_the_batch(orc, s):
+    """B documents of length T packed into one row equal the [B, T] batch
+    bitwise, weight gradients included (same token order in every sum)."""
+    from dataclasses import replace
+    rng = np.random.default_rng(23)
+    p = pins.random_problem(rng, s)
+    sp = replace(s, B=1, T=s.B * s.T, cu_seqlens=tuple(range(0, s.B * s.T + 1, s.T)))
+    a = {**orc.forward(s, p["h"], p["x"], **pins.gen_args(p)),
+         **orc.backward(s, p["h"], p["x"], p["dy"], **pins.gen_args(p))}
+    b = {**orc.forward(sp, p["h"], p["x"], **pins.gen_args(p)),
+         **orc.backward(sp, p["h"], p["x"], p["dy"], **pins.gen_args(p))}
+    for key in a:
+        if a[key] is not None:
+            assert np.array_equal(np.asarray(a[key]).reshape(-1), np.asarray(b[key]).reshape(-1)), key
