@@ -22,7 +22,8 @@
  *   u[b,t,e,j] = sum_i h[b,t,i] W[i, e*k+j]
  *
  * Tokens before the start of each sequence count as zero and nothing
- * crosses batch rows.  The filter w is never written to memory (the
+ * crosses batch rows, nor, in a packed row, document boundaries (see
+ * dynconv_problem).  The filter w is never written to memory (the
  * Efficient Training Implementation section's Fused Low-Rank Kernel item
  * describes the same: the product zU is formed on chip).
  *
@@ -82,7 +83,7 @@
 extern "C" {
 #endif
 
-#define DYNCONV_ABI_VERSION 1
+#define DYNCONV_ABI_VERSION 2
 
 #ifndef DYNCONV_API
 #define DYNCONV_API __attribute__((visibility("default")))
@@ -98,10 +99,12 @@ enum {
   DYNCONV_OK = 0,
   DYNCONV_E_NULL = -1,      /* a required pointer is NULL                        */
   DYNCONV_E_SHAPE = -2,     /* a size <= 0 (B, T may be 0), D % n_heads != 0,    */
-                            /* or rank <= 0                                       */
+                            /* rank <= 0, or packed documents with B != 1 or     */
+                            /* n_seqs < 1 (or given to the decode step)           */
   DYNCONV_E_K = -3,         /* k outside [1, 8]                                   */
   DYNCONV_E_DTYPE = -4,     /* dtype or kind not one of the enums                 */
-  DYNCONV_E_ALIGN = -5,     /* a tensor pointer not 16-byte aligned               */
+  DYNCONV_E_ALIGN = -5,     /* a tensor pointer not 16-byte aligned (cu_seqlens:  */
+                            /* not 4-byte aligned)                                */
   DYNCONV_E_ALIAS = -6,     /* an output overlaps an input or another output      */
   DYNCONV_E_WORKSPACE = -7, /* workspace NULL or smaller than required            */
   DYNCONV_E_HIP = -8,       /* a kernel launch failed                             */
@@ -112,11 +115,28 @@ enum {
 
 /* Problem sizes.  B*T tokens, hidden width d_model, D convolved channels,
  * filter width k (1..8).  Limits: B*T*max(D, d_model) < 2^31 elements per
- * tensor; n_heads*k and rank <= 256 (rank <= 64 on the bf16 path). */
+ * tensor; n_heads*k and rank <= 256 (rank <= 64 on the bf16 path).
+ *
+ * Packed documents (cu_seqlens != NULL): the single row (B must be 1) holds
+ * n_seqs documents back to back, document i being tokens cu_seqlens[i] ..
+ * cu_seqlens[i+1]-1.  The causal window stops at every document start as it
+ * stops at a row start: a tap that would reach a token of the previous
+ * document contributes nothing, in the forward and in every gradient.  So
+ * the packed row gives each document's results exactly as if it were run as
+ * its own sequence (the pages are silent on packing; this is the plain
+ * reading of the Mechanism item, whose window only looks back within a
+ * sequence).  cu_seqlens is a device array of n_seqs + 1 int32, 4-byte
+ * aligned, with 0 = cu_seqlens[0] <= cu_seqlens[1] <= ... <= cu_seqlens[n_seqs]
+ * = T (empty documents allowed).  It is read on the device only, so the host
+ * cannot check those values: offsets that break the rule give unspecified
+ * results (never an access outside the tensors).  The decode step takes no
+ * packing (cu_seqlens must be NULL there). */
 typedef struct {
   int64_t B, T, d_model, D;
   int32_t k;
   int32_t dtype; /* dynconv_dtype */
+  const int32_t *cu_seqlens; /* NULL, or document offsets (device, n_seqs + 1 entries) */
+  int64_t n_seqs;            /* documents in the packed row (used with cu_seqlens only) */
 } dynconv_problem;
 
 /* Generator weights (device pointers, I/O dtype). */

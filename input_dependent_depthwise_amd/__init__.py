@@ -37,7 +37,8 @@ class DynConvError(RuntimeError):
 
 class Problem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("d_model", ctypes.c_int64),
-                ("D", ctypes.c_int64), ("k", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("D", ctypes.c_int64), ("k", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("cu_seqlens", ctypes.c_void_p), ("n_seqs", ctypes.c_int64)]
 
 
 class Gen(ctypes.Structure):
@@ -106,12 +107,20 @@ def _dtype_code(dt) -> int:
     raise TypeError(f"unsupported I/O dtype {dt}")
 
 
-def make_problem(x: torch.Tensor, h: torch.Tensor, k: int) -> Problem:
-    """Problem struct from x[B,T,D], h[B,T,d_model] and the filter width k."""
+def make_problem(x: torch.Tensor, h: torch.Tensor, k: int, cu_seqlens=None) -> Problem:
+    """Problem struct from x[B,T,D], h[B,T,d_model] and the filter width k.
+
+    cu_seqlens: None, or packed documents (B must be 1): an int32 device
+    tensor of n_seqs + 1 offsets rising from 0 to T."""
     if x.dim() != 3 or h.dim() != 3 or h.shape[:2] != x.shape[:2]:
         raise ValueError(f"expected h[B,T,d] and x[B,T,D], got {tuple(h.shape)} and {tuple(x.shape)}")
     B, T, D = x.shape
-    return Problem(B, T, h.shape[2], D, int(k), _dtype_code(x.dtype))
+    if cu_seqlens is None:
+        return Problem(B, T, h.shape[2], D, int(k), _dtype_code(x.dtype), None, 0)
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
+        raise TypeError("cu_seqlens must be a contiguous 1-d int32 tensor")
+    return Problem(B, T, h.shape[2], D, int(k), _dtype_code(x.dtype), cu_seqlens.data_ptr(),
+                   cu_seqlens.numel() - 1)
 
 
 def make_gen(W=None, A=None, U=None, w0=None, n_heads: int = 0) -> Gen:
@@ -167,9 +176,10 @@ def _workspace(nbytes: int, device, workspace):
 
 
 def dynconv_fwd(h, x, *, k, W=None, A=None, U=None, w0=None, n_heads=0, y=None, gen_cache=None,
-                want_cache=False, workspace=None, stream=None):
-    """Forward: returns y (and the fp32 generator cache when want_cache)."""
-    prob = make_problem(x, h, k)
+                want_cache=False, workspace=None, stream=None, cu_seqlens=None):
+    """Forward: returns y (and the fp32 generator cache when want_cache).
+    cu_seqlens: packed documents in a single row (see make_problem)."""
+    prob = make_problem(x, h, k, cu_seqlens)
     gen = make_gen(W, A, U, w0, n_heads)
     if y is None:
         y = torch.empty_like(x)
@@ -186,11 +196,11 @@ def dynconv_fwd(h, x, *, k, W=None, A=None, U=None, w0=None, n_heads=0, y=None, 
 
 
 def dynconv_fwd_noalloc(h, x, *, k, W=None, A=None, U=None, w0=None, n_heads=0, y=None, gen_cache=None,
-                        stream=None):
+                        stream=None, cu_seqlens=None):
     """Forward whose workspace is the library's static scratch (no workspace
     argument).  y and gen_cache, when not given, are allocated here by torch,
     outside the library call; pass them for a call that allocates nothing."""
-    prob = make_problem(x, h, k)
+    prob = make_problem(x, h, k, cu_seqlens)
     gen = make_gen(W, A, U, w0, n_heads)
     if y is None:
         y = torch.empty_like(x)
@@ -201,9 +211,10 @@ def dynconv_fwd_noalloc(h, x, *, k, W=None, A=None, U=None, w0=None, n_heads=0, 
 
 
 def dynconv_bwd(h, x, dy, *, k, W=None, A=None, U=None, w0=None, n_heads=0, gen_cache=None,
-                need_dh=True, need_dw0=True, out=None, workspace=None, stream=None):
-    """Backward of sum(dy * y).  Returns dict(dx, dh, dw0, dW | dA, dU)."""
-    prob = make_problem(x, h, k)
+                need_dh=True, need_dw0=True, out=None, workspace=None, stream=None, cu_seqlens=None):
+    """Backward of sum(dy * y).  Returns dict(dx, dh, dw0, dW | dA, dU).
+    cu_seqlens: packed documents, as given to the forward."""
+    prob = make_problem(x, h, k, cu_seqlens)
     gen = make_gen(W, A, U, w0, n_heads)
     dev = x.device
     f32 = dict(dtype=torch.float32, device=dev)
@@ -232,7 +243,7 @@ def dynconv_decode(h, x, state, *, k, W=None, A=None, U=None, w0=None, n_heads=0
     """One decoding step: h [B, d_model], x [B, D], state [B, k-1, D] (updated
     in place; None when k == 1).  Returns y [B, D]."""
     B, D = x.shape
-    prob = Problem(B, 1, h.shape[-1], D, k, _dtype_code(x.dtype))
+    prob = Problem(B, 1, h.shape[-1], D, k, _dtype_code(x.dtype), None, 0)
     gen = make_gen(W, A, U, w0, n_heads)
     if y is None:
         y = torch.empty_like(x)
@@ -243,25 +254,27 @@ def dynconv_decode(h, x, state, *, k, W=None, A=None, U=None, w0=None, n_heads=0
 
 
 class DynConvFn(torch.autograd.Function):
-    """autograd wrapper: y = DynConvFn.apply(h, x, W, A, U, w0, k, n_heads).
+    """autograd wrapper: y = DynConvFn.apply(h, x, W, A, U, w0, k, n_heads[, cu_seqlens]).
 
     Pass W (head-wise, with n_heads) or A and U (low-rank); unused weights
-    are None.  The forward keeps the fp32 generator cache for the backward.
+    are None; cu_seqlens packs documents into one row.  The forward keeps the
+    fp32 generator cache for the backward.
     """
 
     @staticmethod
-    def forward(ctx, h, x, W, A, U, w0, k, n_heads):
-        y, cache = dynconv_fwd(h, x, k=k, W=W, A=A, U=U, w0=w0, n_heads=n_heads, want_cache=True)
-        ctx.save_for_backward(h, x, W, A, U, w0, cache)
+    def forward(ctx, h, x, W, A, U, w0, k, n_heads, cu_seqlens=None):
+        y, cache = dynconv_fwd(h, x, k=k, W=W, A=A, U=U, w0=w0, n_heads=n_heads, want_cache=True,
+                               cu_seqlens=cu_seqlens)
+        ctx.save_for_backward(h, x, W, A, U, w0, cache, cu_seqlens)
         ctx.k, ctx.n_heads = k, n_heads
         return y
 
     @staticmethod
     def backward(ctx, dy):
-        h, x, W, A, U, w0, cache = ctx.saved_tensors
+        h, x, W, A, U, w0, cache, cu_seqlens = ctx.saved_tensors
         g = dynconv_bwd(h, x, dy.contiguous(), k=ctx.k, W=W, A=A, U=U, w0=w0, n_heads=ctx.n_heads,
                         gen_cache=cache, need_dh=ctx.needs_input_grad[0],
-                        need_dw0=w0 is not None)
+                        need_dw0=w0 is not None, cu_seqlens=cu_seqlens)
         cast = lambda t, ref: None if t is None or ref is None else t.to(ref.dtype)
         return (g.get("dh"), g["dx"], cast(g.get("dW"), W), cast(g.get("dA"), A),
-                cast(g.get("dU"), U), cast(g.get("dw0"), w0), None, None)
+                cast(g.get("dU"), U), cast(g.get("dw0"), w0), None, None, None)

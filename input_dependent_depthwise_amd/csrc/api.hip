@@ -58,6 +58,13 @@ int check_problem(const dynconv_problem *p, const dynconv_gen *g, Shape &s) {
   const int64_t BT = p->B * p->T;
   if (BT > 0 && (BT > lim / p->D || BT > lim / p->d_model || BT > lim / N)) return DYNCONV_E_LIMIT;
   if (p->D * p->k > lim / 256 || p->d_model * N > lim) return DYNCONV_E_LIMIT;
+  if (p->cu_seqlens) {  // packed documents: one row, at least one document
+    if (p->B != 1 || p->n_seqs < 1) return DYNCONV_E_SHAPE;
+    if (((uintptr_t)p->cu_seqlens & 3u) != 0) return DYNCONV_E_ALIGN;
+    if (p->n_seqs >= lim) return DYNCONV_E_LIMIT;
+  }
+  s.seqpos = nullptr;
+  s.packed = p->cu_seqlens != nullptr;
   s.B = p->B;
   s.T = p->T;
   s.BT = BT;
@@ -82,6 +89,7 @@ struct Plan {
   size_t dw0p = 0;   // per-range dw0 partials, fp32
   size_t mp = 0;     // generator weight padded to Np columns (bf16)
   size_t dmp = 0;    // per-range dW / dA partials, fp32
+  size_t seqpos = 0; // packed documents: per-token position table, uint16 [BT]
   size_t total = 0;
 };
 
@@ -110,6 +118,9 @@ Plan plan(const Shape &s, int dtype, int pass, bool cached) {
     off += round_up(bytes);
     return at;
   };
+  // (64 bytes of padding: kernels read the table four tokens at a time, a
+  // few groups past the last token)
+  if (s.packed) pl.seqpos = take((size_t)s.BT * sizeof(uint16_t) + 64);
   if (!cached) pl.cache = take((size_t)s.BT * s.N * sizeof(float));
   // the projection runs in the forward, and in the backward only to rebuild a missing cache
   if (mfma_proj(s, dtype) && (pass == 0 || !cached)) pl.mt = take(gen_proj_mfma_ws_bytes(s));
@@ -136,11 +147,12 @@ inline int launch_status() {
 
 // Byte sizes of the problem's tensors.
 struct Sizes {
-  size_t h, x, W, A, U, w0, cache, dW, dA, dU, dw0;
+  size_t h, x, W, A, U, w0, cache, dW, dA, dU, dw0, cu;
 };
 
-Sizes sizes(const Shape &s, int eb) {
+Sizes sizes(const Shape &s, int eb, const dynconv_problem *p) {
   Sizes z;
+  z.cu = s.packed ? (size_t)(p->n_seqs + 1) * sizeof(int32_t) : 0;
   z.h = (size_t)s.BT * s.d * eb;
   z.x = (size_t)s.BT * s.D * eb;
   z.W = s.kind == DYNCONV_HEADWISE ? (size_t)s.d * s.N * eb : 0;
@@ -190,9 +202,9 @@ int fwd_validate(const dynconv_problem *p, const dynconv_gen *g, const void *h, 
   pl = plan(s, p->dtype, 0, gen_cache != nullptr);
   if (check_ws && (workspace_bytes < pl.total || (pl.total > 0 && !workspace))) return DYNCONV_E_WORKSPACE;
   const int eb = p->dtype == DYNCONV_BF16 ? 2 : 4;
-  const Sizes z = sizes(s, eb);
+  const Sizes z = sizes(s, eb, p);
   const Range ins[] = {{h, z.h}, {x, z.x}, {g->W, z.W}, {g->A, z.A}, {g->U, z.U},
-                       {g->w0, g->w0 ? z.w0 : 0}};
+                       {g->w0, g->w0 ? z.w0 : 0}, {p->cu_seqlens, z.cu}};
   const Range outs[] = {{y, z.x}, {gen_cache, gen_cache ? z.cache : 0},
                         {check_ws ? workspace : nullptr, pl.total}};
   for (const Range &o : outs) {
@@ -207,9 +219,14 @@ int fwd_validate(const dynconv_problem *p, const dynconv_gen *g, const void *h, 
 
 // Enqueues a validated forward: projection into the cache (the caller's, or
 // the workspace slot), then filter formation + conv + residual.
-int fwd_launch(const Shape &s, int dtype, const dynconv_gen *g, const void *h, const void *x, void *y,
-               void *gen_cache, void *workspace, const Plan &pl, hipStream_t stream) {
+int fwd_launch(const dynconv_problem *p, Shape s, int dtype, const dynconv_gen *g, const void *h, const void *x,
+               void *y, void *gen_cache, void *workspace, const Plan &pl, hipStream_t stream) {
   float *cache = gen_cache ? (float *)gen_cache : (float *)((char *)workspace + pl.cache);
+  if (s.packed) {
+    uint16_t *sp = (uint16_t *)((char *)workspace + pl.seqpos);
+    seqpos_fill(p->cu_seqlens, p->n_seqs, s.BT, sp, stream);
+    s.seqpos = sp;
+  }
   int rc = gen_proj(s, dtype, g, h, cache, workspace, pl, stream);
   if (rc) return rc;
   if (s.kind == DYNCONV_HEADWISE && vec_rows(s, dtype)) {
@@ -329,7 +346,7 @@ int dynconv_fwd(const dynconv_problem *p, const dynconv_gen *g, const void *h, c
   Plan pl;
   int rc = fwd_validate(p, g, h, x, y, gen_cache, workspace, workspace_bytes, true, s, pl);
   if (rc || s.BT == 0) return rc;
-  return fwd_launch(s, p->dtype, g, h, x, y, gen_cache, workspace, pl, stream);
+  return fwd_launch(p, s, p->dtype, g, h, x, y, gen_cache, workspace, pl, stream);
 }
 
 int dynconv_fwd_noalloc(const dynconv_problem *p, const dynconv_gen *g, const void *h, const void *x, void *y,
@@ -341,7 +358,7 @@ int dynconv_fwd_noalloc(const dynconv_problem *p, const dynconv_gen *g, const vo
   if (pl.total > kScratchBytes) return DYNCONV_E_SCRATCH;
   void *ws = nullptr;
   if ((rc = scratch_ptr(&ws))) return rc;
-  return fwd_launch(s, p->dtype, g, h, x, y, gen_cache, ws, pl, stream);
+  return fwd_launch(p, s, p->dtype, g, h, x, y, gen_cache, ws, pl, stream);
 }
 
 int dynconv_decode(const dynconv_problem *p, const dynconv_gen *g, const void *h, const void *x, void *state,
@@ -349,7 +366,7 @@ int dynconv_decode(const dynconv_problem *p, const dynconv_gen *g, const void *h
   Shape s;
   int rc = check_problem(p, g, s);
   if (rc) return rc;
-  if (p->T != 1) return DYNCONV_E_SHAPE;
+  if (p->T != 1 || s.packed) return DYNCONV_E_SHAPE;
   if (s.B == 0) return DYNCONV_OK;
   if (!h || !x || !y || (s.k > 1 && !state)) return DYNCONV_E_NULL;
   if ((rc = check_weights(s, g))) return rc;
@@ -358,7 +375,7 @@ int dynconv_decode(const dynconv_problem *p, const dynconv_gen *g, const void *h
   for (const void *q : ptrs)
     if (q && !aligned16(q)) return DYNCONV_E_ALIGN;
   const int eb = p->dtype == DYNCONV_BF16 ? 2 : 4;
-  const Sizes z = sizes(s, eb);
+  const Sizes z = sizes(s, eb, p);
   const size_t st_bytes = s.k > 1 ? (size_t)s.B * (s.k - 1) * s.D * eb : 0;
   const Range ins[] = {{h, z.h}, {x, z.x}, {g->W, z.W}, {g->A, z.A}, {g->U, z.U}, {g->w0, g->w0 ? z.w0 : 0}};
   const Range outs[] = {{y, z.x}, {state, st_bytes}};
@@ -386,7 +403,7 @@ int dynconv_bwd(const dynconv_problem *p, const dynconv_gen *g, const void *h, c
   if (s.BT == 0) {
     // No tokens: the weight gradients are empty sums.  Written by a fill
     // kernel, not a memset, so that the call can sit inside a captured graph.
-    const Sizes z0 = sizes(s, p->dtype == DYNCONV_BF16 ? 2 : 4);
+    const Sizes z0 = sizes(s, p->dtype == DYNCONV_BF16 ? 2 : 4, p);
     const void *gp[] = {gg->dW, gg->dA, gg->dU, gg->dw0};
     for (const void *q : gp)
       if (q && !aligned16(q)) return DYNCONV_E_ALIGN;
@@ -403,9 +420,10 @@ int dynconv_bwd(const dynconv_problem *p, const dynconv_gen *g, const void *h, c
   const Plan pl = plan(s, p->dtype, 1, gen_cache != nullptr);
   if (workspace_bytes < pl.total || (pl.total > 0 && !workspace)) return DYNCONV_E_WORKSPACE;
   const int eb = p->dtype == DYNCONV_BF16 ? 2 : 4;
-  const Sizes z = sizes(s, eb);
+  const Sizes z = sizes(s, eb, p);
   const Range ins[] = {{h, z.h},       {x, z.x},   {dy, z.x},  {gen_cache, gen_cache ? z.cache : 0},
-                       {g->W, z.W},    {g->A, z.A}, {g->U, z.U}, {g->w0, g->w0 ? z.w0 : 0}};
+                       {g->W, z.W},    {g->A, z.A}, {g->U, z.U}, {g->w0, g->w0 ? z.w0 : 0},
+                       {p->cu_seqlens, z.cu}};
   const Range outs[] = {{dx, z.x},          {dh, dh ? z.h : 0},     {gg->dW, gg->dW ? z.dW : 0},
                         {gg->dA, gg->dA ? z.dA : 0}, {gg->dU, gg->dU ? z.dU : 0},
                         {gg->dw0, gg->dw0 ? z.dw0 : 0}, {workspace, pl.total}};
@@ -416,6 +434,11 @@ int dynconv_bwd(const dynconv_problem *p, const dynconv_gen *g, const void *h, c
   for (int a = 0; a < n_out; ++a)
     for (int b = a + 1; b < n_out; ++b)
       if (overlap(outs[a], outs[b])) return DYNCONV_E_ALIAS;
+  if (s.packed) {
+    uint16_t *sp = (uint16_t *)((char *)workspace + pl.seqpos);
+    seqpos_fill(p->cu_seqlens, p->n_seqs, s.BT, sp, stream);
+    s.seqpos = sp;
+  }
   const float *cache = (const float *)gen_cache;
   if (!cache) {
     float *c = (float *)((char *)workspace + pl.cache);

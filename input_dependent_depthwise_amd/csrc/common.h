@@ -69,7 +69,21 @@ struct Shape {
   int k, kind, n_heads, rank;
   int N;   // generator outputs per token: n_heads*k or rank
   int hd;  // channels per head (head-wise)
+  // packed documents: per token, its position in its document (low byte)
+  // and the tokens after it in that document (high byte), both clamped to
+  // 255 (more than any tap reaches); NULL when every row is one sequence
+  const uint16_t *seqpos;
+  bool packed;  // the problem has packed documents (seqpos is set before any conv kernel)
 };
+
+// Position of token row r in its sequence, and the tokens after it there
+// (clamped to 255), for kernels that look them up per token.
+__device__ __forceinline__ int seq_pos(const Shape &s, int64_t r) {
+  return s.seqpos ? (int)(s.seqpos[r] & 255u) : (int)(r % s.T);
+}
+__device__ __forceinline__ int seq_rem(const Shape &s, int64_t r) {
+  return s.seqpos ? (int)(s.seqpos[r] >> 8) : (int)(s.T - 1 - r % s.T);
+}
 
 // Launch helpers (defined in api.hip, used by the kernel files).
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -163,8 +163,9 @@ __device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
 }
 
 // S: lanes per head when heads are 1..16 lanes wide and aligned to spans; 0:
-// any head width (LDS reduction).
-template <int K, int CPL, int S>
+// any head width (LDS reduction).  VAR: packed documents (positions from the
+// per-token table).
+template <int K, int CPL, int S, bool VAR>
 __global__ void __launch_bounds__(256, 2)
 k_bwd_hw(Params P) {
   constexpr int NP = CPL / 2;        // bf16 pairs per lane
@@ -250,7 +251,13 @@ k_bwd_hw(Params P) {
 #pragma unroll
       for (int i = 0; i < CPL; ++i) acc[a][i] = 0.f;
 
-    int pos = (int)(t_a % T);  // position in its sequence of the next token to process
+    int pos = VAR ? 0 : (int)(t_a % T);  // position in its sequence of the next token to process
+    // VAR (packed documents): positions from the per-token table, the eight of
+    // a block in two scalar loads issued a block ahead (t_a and the run length
+    // are multiples of 4; the table is padded past its last token)
+    const uint64_t *sp4 = reinterpret_cast<const uint64_t *>(s.seqpos);
+    uint64_t pn[2] = {0, 0};
+    if constexpr (VAR) pn[0] = sp4[t_a >> 2], pn[1] = sp4[(t_a >> 2) + 1];
     // Loads are unconditional: row offsets are clamped to the batch, and what
     // they bring past the run is never consumed (tokens past t_end are not
     // processed, x past t_b feeds no product, and every token past the batch
@@ -289,10 +296,14 @@ k_bwd_hw(Params P) {
     // (scalar branches); keeping them in every block rather than compiling a
     // second, test-free copy keeps the register allocation of the rings simple.
     auto block = [&](int tg) {
+      const uint64_t pc[2] = {pn[0], pn[1]};
+      if constexpr (VAR) pn[0] = sp4[(tg >> 2) + 2], pn[1] = sp4[(tg >> 2) + 3];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int t = tg + i;
         float vals[4] = {0.f, 0.f, 0.f, 0.f};
+        // a token past the batch end starts a new "sequence" (its loads were clamped)
+        if constexpr (VAR) pos = t < BT ? (int)((pc[i >> 2] >> (16 * (i & 3))) & 255u) : 0;
         if (t < t_end) {
           const bool main = t < t_b;
           // (lanes past D in a partial last span compute on the clamped
@@ -355,7 +366,9 @@ k_bwd_hw(Params P) {
 #pragma unroll
             for (int p = 0; p < NP; ++p) held[p] = o[p];
           }
-          if (++pos == T) pos = 0;
+          if constexpr (!VAR) {
+            if (++pos == T) pos = 0;
+          }
         }
         // refill: token t+PD into the slot just released
         load_tok(t + PD, (i + PD) & 7);
@@ -502,7 +515,13 @@ int bwd_headwise(const Shape &s, const BwdLayout &L, const float *u, const void 
   const dim3 grid((unsigned)L.n_slices, (unsigned)L.n_ranges), block(256);
   const bool tr = trace_begin(DYNCONV_K_BWD_CONV, st);
   int rc = 0;
-#define HW(K_, C_, S_) hipLaunchKernelGGL((bwdhw::k_bwd_hw<K_, C_, S_>), grid, block, 0, st, P)
+#define HW(K_, C_, S_)                                                                \
+  do {                                                                                \
+    if (s.seqpos)                                                                     \
+      hipLaunchKernelGGL((bwdhw::k_bwd_hw<K_, C_, S_, true>), grid, block, 0, st, P);  \
+    else                                                                              \
+      hipLaunchKernelGGL((bwdhw::k_bwd_hw<K_, C_, S_, false>), grid, block, 0, st, P); \
+  } while (0)
 #define HW_S8(K_)                      \
   switch (S) {                         \
     case 1: HW(K_, 8, 1); break;       \

@@ -87,7 +87,10 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 }
 
 // K: taps; KQ: 32-row K-steps over rank + bias; NQ: 16-row blocks of rank.
-template <int K, int KQ, int NQ, int kW>
+// VAR: packed documents (each token's position and the tokens after it in
+// its document come from the per-token table, loaded with the tile's other
+// operands; every tile takes the masked path).
+template <int K, int KQ, int NQ, int kW, bool VAR>
 __global__ void __launch_bounds__(kW * 64, 2)
 k_bwd_lr(Params P) {
   constexpr int kDt = kW * kCW;    // channels per block
@@ -229,6 +232,8 @@ k_bwd_lr(Params P) {
   // loads are issued unconditionally (masked slots read zeros from outside the buffer)
   const auto rx = make_rsrc(P.x, (uint32_t)(s.BT * s.D * 2)), rdy = make_rsrc(P.dy, (uint32_t)(s.BT * s.D * 2));
   const auto rz = make_rsrc(P.z, (uint32_t)(s.BT * rank * 4));
+  uint32_t ppre[NSET][2] = {};  // VAR: table entries of the lane's tokens n, 16 + n (zero past BT)
+  const auto rp = make_rsrc(s.seqpos, VAR ? (uint32_t)(s.BT * 2) : 0u);
   auto prefetch = [&](int set, int tile) {
     const uint32_t vstep = (uint32_t)(tile * 32 * D) * 2u, zstep = (uint32_t)(tile * 32 * rank) * 4u;
     constexpr uint32_t kTop = 0xffffff00u;
@@ -236,6 +241,11 @@ k_bwd_lr(Params P) {
     for (int q = 0; q < kVL; ++q) vpre[set][q] = buf_load16(v_isx[q] ? rx : rdy, min(v_gbase[q] + vstep, kTop));
 #pragma unroll
     for (int q = 0; q < kZL; ++q) zpre[set][q] = buf_load_f32(rz, z_gbase[q] + zstep);
+    if constexpr (VAR) {
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+        ppre[set][tb] = __builtin_amdgcn_raw_buffer_load_b16(rp, (uint32_t)(tile * 32 + 16 * tb + n) * 2u, 0, 0);
+    }
   };
   auto stage = [&](int set) {
 #pragma unroll
@@ -285,15 +295,26 @@ k_bwd_lr(Params P) {
   auto tile_step = [&](const int set, const int tile) {
     const int64_t t0 = (int64_t)tile * 32;
     // only tiles that hold a token with pos < KH (x before its sequence start)
-    // or pos > T-1-KH (dy past its sequence end) need the per-token masks
-    const bool edge_lo = KH > 0 && (p0 < KH || T - p0 <= 31);
-    const bool edge_hi = KH > 0 && T - KH - p0 <= 31;
-    int pos[2] = {0, 0};
-    if (edge_lo || edge_hi) {
+    // or rem < KH (dy past its sequence end: rem tokens follow it there) need
+    // the per-token masks
+    bool edge_lo, edge_hi;
+    int pos[2] = {0, 0}, rem[2] = {0, 0};
+    if constexpr (VAR) {
+      edge_lo = edge_hi = KH > 0;
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) pos[tb] = (int)((uint32_t)(p0 + 16 * tb + n) % (uint32_t)T);
+      for (int tb = 0; tb < 2; ++tb) pos[tb] = (int)(ppre[set][tb] & 255u), rem[tb] = (int)(ppre[set][tb] >> 8);
+    } else {
+      edge_lo = KH > 0 && (p0 < KH || T - p0 <= 31);
+      edge_hi = KH > 0 && T - KH - p0 <= 31;
+      if (edge_lo || edge_hi) {
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          pos[tb] = (int)((uint32_t)(p0 + 16 * tb + n) % (uint32_t)T);
+          rem[tb] = T - 1 - pos[tb];
+        }
+      }
+      p0 = T >= 32 ? (p0 + 32 >= T ? p0 + 32 - T : p0 + 32) : (p0 + 32) % T;
     }
-    p0 = T >= 32 ? (p0 + 32 >= T ? p0 + 32 - T : p0 + 32) : (p0 + 32) % T;
 
     __syncthreads();  // the previous tile's LDS reads are done
     stage(set);
@@ -346,7 +367,7 @@ k_bwd_lr(Params P) {
         } else {
           const uint2 d = *reinterpret_cast<const uint2 *>(&dys[(16 * tb + n + j) * kRow + wc]);
           w[0] = d.x, w[1] = d.y;
-          if (__builtin_expect(edge_hi, 0) && pos[tb] + j > T - 1) w[0] = 0u, w[1] = 0u;
+          if (__builtin_expect(edge_hi, 0) && j > rem[tb]) w[0] = 0u, w[1] = 0u;
         }
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
@@ -521,7 +542,13 @@ int bwd_lowrank(const Shape &s, const BwdLayout &L, const float *z, const void *
   const bool tr = trace_begin(DYNCONV_K_BWD_CONV, st);
   int rc = 0;
   // one 16-row block of rank (NQ = 1) <=> rank <= 16 <=> 4 waves per block
-#define LR(K_, KQ_, NQ_, W_) hipLaunchKernelGGL((bwdlr::k_bwd_lr<K_, KQ_, NQ_, W_>), grid, block, 0, st, P)
+#define LR(K_, KQ_, NQ_, W_)                                                                  \
+  do {                                                                                        \
+    if (s.seqpos)                                                                             \
+      hipLaunchKernelGGL((bwdlr::k_bwd_lr<K_, KQ_, NQ_, W_, true>), grid, block, 0, st, P);  \
+    else                                                                                      \
+      hipLaunchKernelGGL((bwdlr::k_bwd_lr<K_, KQ_, NQ_, W_, false>), grid, block, 0, st, P); \
+  } while (0)
 #define LR_K(K_)                                            \
   if (KQ == 1 && NQ == 1 && kw == 4) LR(K_, 1, 1, 4);       \
   else if (KQ == 1 && NQ == 2 && kw == 8) LR(K_, 1, 2, 8);  \

@@ -29,8 +29,11 @@ namespace {
 // on every path (masked ones fall outside the buffer), so the compiler's wait
 // counts keep the ring in flight; a sequence start clears the history in a
 // uniform branch that holds no memory access.  S2: a vector may straddle two
-// heads (head width not a multiple of 8, at least 8).
-template <int K, bool S2>
+// heads (head width not a multiple of 8, at least 8).  VAR: packed documents,
+// the positions come from the per-token table, four tokens per scalar load
+// issued a step ahead (the table is padded, so reads just past the last
+// token stay inside it; their values are never used).
+template <int K, bool S2, bool VAR>
 __global__ void __launch_bounds__(256)
 k_fwd_hw_ring(Shape s, const float *__restrict__ u, const bf16 *__restrict__ w0, const bf16 *__restrict__ x,
               bf16 *__restrict__ y, int n_vg, int n_runs, int tpw) {
@@ -112,7 +115,15 @@ k_fwd_hw_ring(Shape s, const float *__restrict__ u, const bf16 *__restrict__ w0,
   // history: xf[(i - j) & 3] holds x[t - j] (fp32) at step i; rows of the
   // previous sequence read as zero
   float xf[4][8];
-  int pos = t_lo % T;
+  int pos = 0;
+  uint64_t pq = 0;  // VAR: table entries of the next four tokens (t_lo and tpw are multiples of 4)
+  const uint64_t *sp4 = reinterpret_cast<const uint64_t *>(s.seqpos);
+  if constexpr (VAR) {
+    pq = sp4[t_lo >> 2];
+    pos = (int)(pq & 255u);
+  } else {
+    pos = t_lo % T;
+  }
 #pragma unroll
   for (int j = 1; j < 4; ++j) {
     const uint4 r = buf_load16(rx, (j < K && pos - j >= 0) ? xoff(t_lo - j) : kOutside);
@@ -131,10 +142,13 @@ k_fwd_hw_ring(Shape s, const float *__restrict__ u, const bf16 *__restrict__ w0,
 
   const int n_iter = (t_hi - t_lo + 3) & ~3;
   for (int it = 0; it < n_iter; it += 4) {
+    const uint64_t pc = pq;
+    if constexpr (VAR) pq = sp4[(t_lo + it + 4) >> 2];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = t_lo + it + i;
       cvt(xr[i], xf[i]);
+      if constexpr (VAR) pos = (int)((pc >> (16 * i)) & 255u);
       if (pos == 0) {  // a new sequence starts: no history
 #pragma unroll
         for (int j = 1; j < 4; ++j)
@@ -159,7 +173,7 @@ k_fwd_hw_ring(Shape s, const float *__restrict__ u, const bf16 *__restrict__ w0,
                ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)out[2 * q + 1]) << 16);
       buf_store16(ry, xoff(t), make_uint4(w[0], w[1], w[2], w[3]));
       load_tok(i, t + PD);
-      pos = pos + 1 == T ? 0 : pos + 1;
+      if constexpr (!VAR) pos = pos + 1 == T ? 0 : pos + 1;
     }
   }
 }
@@ -198,7 +212,7 @@ k_fwd_headwise(Shape s, const float *__restrict__ u, const T *__restrict__ w0,
 
   // window: xw[j] = x[row - j]; rows before the sequence start are zero
   float xw[KP][V];
-  int64_t pos = row0 % s.T;
+  int64_t pos = seq_pos(s, row0);
 #pragma unroll
   for (int j = 1; j < KP; ++j) {
     if (j < k && pos - j >= 0) {
@@ -210,7 +224,8 @@ k_fwd_headwise(Shape s, const float *__restrict__ u, const T *__restrict__ w0,
   }
 
   for (int64_t row = row0; row < row1; ++row, ++pos) {
-    if (pos == s.T) {  // a new sequence starts: clear the history
+    if (s.seqpos) pos = seq_pos(s, row);  // packed documents: from the table
+    if (s.seqpos ? (pos == 0 && row > row0) : pos == s.T) {  // a new sequence starts: clear the history
       pos = 0;
 #pragma unroll
       for (int j = 1; j < KP; ++j)
@@ -275,8 +290,13 @@ static void launch_ring(const Shape &s, const float *u, const void *w0, const vo
   tpw = std::max(16, (tpw + 3) & ~3);
   const int n_runs = (int)ceil_div(s.BT, tpw);
   const int waves = n_vg * n_runs;
-  hipLaunchKernelGGL((k_fwd_hw_ring<K, S2>), dim3((unsigned)ceil_div(waves, 4)), dim3(256), 0, st, s, u,
-                     (const bf16 *)w0, (const bf16 *)x, (bf16 *)y, n_vg, n_runs, tpw);
+  const dim3 grid((unsigned)ceil_div(waves, 4)), block(256);
+  if (s.seqpos)
+    hipLaunchKernelGGL((k_fwd_hw_ring<K, S2, true>), grid, block, 0, st, s, u, (const bf16 *)w0, (const bf16 *)x,
+                       (bf16 *)y, n_vg, n_runs, tpw);
+  else
+    hipLaunchKernelGGL((k_fwd_hw_ring<K, S2, false>), grid, block, 0, st, s, u, (const bf16 *)w0, (const bf16 *)x,
+                       (bf16 *)y, n_vg, n_runs, tpw);
 }
 
 template <typename T>

@@ -40,7 +40,9 @@ constexpr int kRowB = kDt * 2 + 16;   // LDS row stride of the x tile (bytes, pa
 // slot gets an offset outside the buffer: zeros in, nothing out), so the
 // compiler's wait counts stay exact: tile i+2 is in flight while tile i is
 // computed (two register sets, tiles taken in pairs).
-template <int K, int KQ>
+// VAR: packed documents; each lane's token position comes from the per-token
+// table, loaded with the tile's other operands two tiles ahead.
+template <int K, int KQ, bool VAR>
 __global__ void __launch_bounds__(256)
 k_fwd_lowrank(Shape s, const float *__restrict__ z, const bf16 *__restrict__ U, const bf16 *__restrict__ w0,
               const bf16 *__restrict__ x, bf16 *__restrict__ y, int tpb, int n_tiles) {
@@ -141,6 +143,8 @@ k_fwd_lowrank(Shape s, const float *__restrict__ z, const bf16 *__restrict__ U, 
   const auto ry = make_rsrc(y, (uint32_t)(BT * D * 2));
   uint4 vpre[2][kVLoads];
   float spre[2][kSLoads];
+  uint32_t ppre[2] = {0u, 0u};  // VAR: table entry of the lane's token (zero past BT)
+  const auto rp = make_rsrc(s.seqpos, VAR ? (uint32_t)(BT * 2) : 0u);
   auto prefetch = [&](int set, int tile) {
     const bool tin = tile < tile_hi;
     const uint32_t vstep = tin ? (uint32_t)(tile * 32 * D) * 2u : kOutside;
@@ -150,6 +154,8 @@ k_fwd_lowrank(Shape s, const float *__restrict__ z, const bf16 *__restrict__ U, 
     for (int q = 0; q < kVLoads; ++q) vpre[set][q] = buf_load16(rx, min(v_gbase[q] + vstep, kTop));
 #pragma unroll
     for (int q = 0; q < kSLoads; ++q) spre[set][q] = buf_load_f32(rz, min(s_gbase[q] + zstep, kTop));
+    if constexpr (VAR)
+      ppre[set] = __builtin_amdgcn_raw_buffer_load_b16(rp, tin ? (uint32_t)(tile * 32 + tl) * 2u : kOutside, 0, 0);
   };
 
   auto step = [&](const int set, const int tile) {
@@ -158,15 +164,16 @@ k_fwd_lowrank(Shape s, const float *__restrict__ z, const bf16 *__restrict__ U, 
     for (int q = 0; q < kVLoads; ++q) *reinterpret_cast<uint4 *>(xs[set] + v_loff[q]) = vpre[set][q];
 #pragma unroll
     for (int q = 0; q < kSLoads; ++q) zs[set][s_loff[q]] = (bf16)spre[set][q];
+    const int t = tile * 32 + tl;
+    // (read before the prefetch below refills the set)
+    const int pos = VAR ? (int)(ppre[set] & 255u) : (int)((uint32_t)t % (uint32_t)s.T);
     __syncthreads();
     prefetch(set, tile + 2);
 
-    const int t = tile * 32 + tl;
     // y of this tile: rows past BT fall outside ry; tiles past the block's
     // range store nothing
     const bool tin = tile < tile_hi;
     const uint32_t ystep = (uint32_t)(tile * 32 * D) * 2u;
-    const int pos = (int)((uint32_t)t % (uint32_t)s.T);
     bf16x8 bz[KQ];
 #pragma unroll
     for (int kq = 0; kq < KQ; ++kq)
@@ -239,9 +246,15 @@ int fwd_lowrank(const Shape &s, const float *z, const void *U, const void *w0, c
   dim3 grid((unsigned)n_slices, (unsigned)ceil_div(n_tiles, tpb));
   const bool tr = trace_begin(DYNCONV_K_FWD_CONV, st);
   int rc = 0;
-#define LAUNCH(K_, KQ_)                                                                             \
-  hipLaunchKernelGGL((k_fwd_lowrank<K_, KQ_>), grid, dim3(256), 0, st, s, z, (const bf16 *)U,     \
-                     (const bf16 *)w0, (const bf16 *)x, (bf16 *)y, tpb, n_tiles)
+#define LAUNCH(K_, KQ_)                                                                                \
+  do {                                                                                                 \
+    if (s.seqpos)                                                                                      \
+      hipLaunchKernelGGL((k_fwd_lowrank<K_, KQ_, true>), grid, dim3(256), 0, st, s, z, (const bf16 *)U,  \
+                         (const bf16 *)w0, (const bf16 *)x, (bf16 *)y, tpb, n_tiles);                 \
+    else                                                                                               \
+      hipLaunchKernelGGL((k_fwd_lowrank<K_, KQ_, false>), grid, dim3(256), 0, st, s, z, (const bf16 *)U, \
+                         (const bf16 *)w0, (const bf16 *)x, (bf16 *)y, tpb, n_tiles);                 \
+  } while (0)
 #define LAUNCH_K(K_)                          \
   switch (KQ) {                               \
     case 1: LAUNCH(K_, 1); break;             \

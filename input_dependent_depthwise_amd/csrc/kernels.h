@@ -13,6 +13,10 @@ void trace_end(bool armed, hipStream_t st);
 // Writes n zeros at p (no-op when p is NULL or n is 0).
 void zero_fill(float *p, int64_t n, hipStream_t st);
 
+// Packed documents: the per-token position table of Shape::seqpos from the
+// document offsets cu[0 .. n_seqs] (simple_kernels.hip).
+void seqpos_fill(const int32_t *cu, int64_t n_seqs, int64_t BT, uint16_t *out, hipStream_t st);
+
 // --- plain VALU kernels (simple_kernels.hip); T = float or bf16 ---
 template <typename T>
 int simple_gen_proj(const Shape &s, const void *h, const void *M, float *out, hipStream_t st);

@@ -64,10 +64,10 @@ k_conv_fwd_simple(Shape s, const float *__restrict__ gen, const T *__restrict__ 
   if (g >= s.BT * nvec) return;
   const int64_t row = g / nvec;
   const int64_t c0 = (g - row * nvec) * V;
-  const int64_t t = row % s.T;
+  const int pos = seq_pos(s, row);
   float acc[V];
   load_vec(x + row * s.D + c0, acc);
-  for (int j = 0; j < s.k && j <= t; ++j) {
+  for (int j = 0; j < s.k && j <= pos; ++j) {
     float xv[V];
     load_vec(x + (row - j) * s.D + c0, xv);
 #pragma unroll
@@ -89,10 +89,10 @@ k_conv_dx_simple(Shape s, const float *__restrict__ gen, const T *__restrict__ U
   if (g >= s.BT * nvec) return;
   const int64_t row = g / nvec;
   const int64_t c0 = (g - row * nvec) * V;
-  const int64_t t = row % s.T;
+  const int rem = seq_rem(s, row);
   float acc[V];
   load_vec(dy + row * s.D + c0, acc);
-  for (int j = 0; j < s.k && t + j <= s.T - 1; ++j) {
+  for (int j = 0; j < s.k && j <= rem; ++j) {
     float gv[V];
     load_vec(dy + (row + j) * s.D + c0, gv);
 #pragma unroll
@@ -112,9 +112,9 @@ k_conv_fwd_scalar(Shape s, const float *__restrict__ gen, const T *__restrict__ 
   if (g >= s.BT * s.D) return;
   const int64_t row = g / s.D;
   const int64_t c = g - row * s.D;
-  const int64_t t = row % s.T;
+  const int pos = seq_pos(s, row);
   float acc = to_f32(x[g]);
-  for (int j = 0; j < s.k && j <= t; ++j)
+  for (int j = 0; j < s.k && j <= pos; ++j)
     acc = fmaf(filter_tap(s, gen, U, w0, row, c, j), to_f32(x[g - j * s.D]), acc);
   y[g] = from_f32<T>(acc);
 }
@@ -127,19 +127,18 @@ k_conv_dx_scalar(Shape s, const float *__restrict__ gen, const T *__restrict__ U
   if (g >= s.BT * s.D) return;
   const int64_t row = g / s.D;
   const int64_t c = g - row * s.D;
-  const int64_t t = row % s.T;
+  const int rem = seq_rem(s, row);
   float acc = to_f32(dy[g]);
-  for (int j = 0; j < s.k && t + j <= s.T - 1; ++j)
+  for (int j = 0; j < s.k && j <= rem; ++j)
     acc = fmaf(filter_tap(s, gen, U, w0, row + j, c, j), to_f32(dy[g + j * s.D]), acc);
   dx[g] = from_f32<T>(acc);
 }
 
-// G[row, c, j] = [t-j>=0] dy[row, c] x[row-j, c]
+// G[row, c, j] = [row-j in row's sequence] dy[row, c] x[row-j, c]
 template <typename T>
 __device__ __forceinline__ float gtap(const Shape &s, const T *__restrict__ x,
                                       const T *__restrict__ dy, int64_t row, int64_t c, int j) {
-  const int64_t t = row % s.T;
-  if (t - j < 0) return 0.f;
+  if (j > seq_pos(s, row)) return 0.f;
   return to_f32(dy[row * s.D + c]) * to_f32(x[(row - j) * s.D + c]);
 }
 
@@ -227,6 +226,31 @@ k_dh_simple(Shape s, const float *__restrict__ g, const T *__restrict__ M, T *__
   float acc = 0.f;
   for (int n = 0; n < s.N; ++n) acc = fmaf(g[row * s.N + n], to_f32(M[i * s.N + n]), acc);
   dh[idx] = from_f32<T>(acc);
+}
+
+// Packed documents: per token t, its position in its document and the tokens
+// after it there, each clamped to [0, 255], from the document offsets cu
+// (n + 1 entries, 0 = cu[0] <= ... <= cu[n] = BT).  The document of t is the
+// last i < n with cu[i] <= t (a binary search); offsets that break the rule
+// still give values in range.
+__global__ void __launch_bounds__(256)
+k_seqpos(const int32_t *__restrict__ cu, int64_t n, int64_t BT, uint16_t *__restrict__ out) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= BT) return;
+  int64_t lo = 0, hi = n - 1;  // invariant: the document is in [lo, hi]
+  while (lo < hi) {
+    const int64_t mid = (lo + hi + 1) >> 1;
+    if ((int64_t)cu[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  int64_t start = cu[lo], end = cu[lo + 1];
+  start = start < 0 ? 0 : (start > t ? t : start);
+  end = end > BT ? BT : (end <= t ? t + 1 : end);
+  const int64_t pos = t - start, rem = end - 1 - t;
+  out[t] = (uint16_t)((pos < 255 ? pos : 255) | ((rem < 255 ? rem : 255) << 8));
+}
+
+void seqpos_fill(const int32_t *cu, int64_t n_seqs, int64_t BT, uint16_t *out, hipStream_t st) {
+  if (BT > 0) hipLaunchKernelGGL(k_seqpos, dim3((unsigned)ceil_div(BT, 256)), dim3(256), 0, st, cu, n_seqs, BT, out);
 }
 
 __global__ void __launch_bounds__(256) k_zero(float *__restrict__ p, int64_t n) {

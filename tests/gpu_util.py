@@ -14,10 +14,11 @@ from workloads import HEADWISE, Workload
 TOL = {"fp32": 1e-5, "bf16": 2e-2}
 
 
-def oracle_shape(w: Workload) -> oracle.Shape:
+def oracle_shape(w: Workload, cu_seqlens=None) -> oracle.Shape:
     return oracle.Shape(B=w.B, T=w.T, d=w.d, D=w.D, k=w.k,
                         kind=oracle.HEADWISE if w.kind == HEADWISE else oracle.LOWRANK,
-                        n_heads=w.n_heads, rank=w.rank)
+                        n_heads=w.n_heads, rank=w.rank,
+                        cu_seqlens=None if cu_seqlens is None else tuple(int(c) for c in cu_seqlens))
 
 
 def to_dev(inp: dict, device="cuda") -> dict:
@@ -25,14 +26,18 @@ def to_dev(inp: dict, device="cuda") -> dict:
 
 
 def gpu_run(w: Workload, dev_inp: dict, use_cache: bool = True, need_dh: bool = True,
-            need_dw0: bool = True, fwd_cache: bool = True):
+            need_dw0: bool = True, fwd_cache: bool = True, cu_seqlens=None):
     """Forward + backward on the GPU; returns dict of device tensors.
 
     fwd_cache=False runs the forward without a caller cache (the library keeps
     the generator values in its workspace); the backward then recomputes it.
+    cu_seqlens (a list of document offsets): the single row holds packed
+    documents.
     """
     kw = dict(k=w.k, W=dev_inp.get("W"), A=dev_inp.get("A"), U=dev_inp.get("U"),
               w0=dev_inp.get("w0"), n_heads=w.n_heads)
+    if cu_seqlens is not None:
+        kw["cu_seqlens"] = torch.tensor(list(cu_seqlens), dtype=torch.int32, device=dev_inp["x"].device)
     if fwd_cache:
         y, cache = dc.dynconv_fwd(dev_inp["h"], dev_inp["x"], want_cache=True, **kw)
     else:
@@ -43,8 +48,8 @@ def gpu_run(w: Workload, dev_inp: dict, use_cache: bool = True, need_dh: bool = 
     return {"y": y, "cache": cache, **g}
 
 
-def oracle_run(w: Workload, inp: dict) -> dict:
-    s = oracle_shape(w)
+def oracle_run(w: Workload, inp: dict, cu_seqlens=None) -> dict:
+    s = oracle_shape(w, cu_seqlens)
     args = dict(W=inp.get("W"), A=inp.get("A"), U=inp.get("U"), w0=inp.get("w0"))
     fw = oracle.forward(s, inp["h"], inp["x"], **args)
     bw = oracle.backward(s, inp["h"], inp["x"], inp["dy"], w=fw["w"], **args)

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert dc.dynconv_abi_version() == 1
+    assert dc.dynconv_abi_version() == 2
     for code in (OK, E_NULL, E_SHAPE, E_K, E_DTYPE, E_ALIGN, E_ALIAS, E_WORKSPACE, E_HIP, E_LIMIT, E_SCRATCH):
         s = dc.dynconv_status_str(code)
         assert s and s != "unknown status"
@@ -317,3 +317,51 @@ def test_fwd_noalloc_validation(L, case, expect):
         assert dc.dynconv_workspace_bytes(p, g, dc.DYNCONV_WS_CACHED) <= dc.NOALLOC_SCRATCH_BYTES
         kw = dict(h=BASE, x=BASE + (1 << 30), y=BASE + (2 << 30))  # tensors this large must not overlap
     assert fwd_na(L, p, g, **kw) == expect
+
+
+def packed(B=1, T=64, n_seqs=3, cu=addr(30), **kw):
+    p = prob(B=B, T=T, **kw)
+    p.cu_seqlens = cu
+    p.n_seqs = n_seqs
+    return p
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("B2", E_SHAPE), ("n0", E_SHAPE), ("align", E_ALIGN), ("alias_y_cu", E_ALIAS), ("empty", OK),
+    ("ws_small", E_WORKSPACE),
+])
+def test_packed_validation(L, case, expect):
+    """Packed documents: one row, at least one document, a 4-byte aligned
+    offset array that no output overlaps."""
+    p, g = packed(), gen_hw()
+    kw = {}
+    if case == "B2":
+        p = packed(B=2)
+    elif case == "n0":
+        p = packed(n_seqs=0)
+    elif case == "align":
+        p = packed(cu=addr(30) + 2)
+    elif case == "alias_y_cu":
+        p = packed(cu=addr(3) + 64)
+    elif case == "empty":
+        p = packed(T=0)
+    elif case == "ws_small":
+        kw["ws_bytes"] = dc.dynconv_workspace_bytes(prob(B=1, T=64), g, 0)  # the size without the position table
+    assert fwd(L, p, g, **kw) == expect
+    if case in ("B2", "n0", "align"):
+        assert bwd(L, p, g) == expect
+    if case == "alias_y_cu":  # the backward's dx over the offsets
+        assert bwd(L, packed(cu=addr(4) + 64), g) == E_ALIAS
+
+
+def test_packed_workspace_holds_the_position_table(L):
+    """Packing adds a per-token position table (2 bytes a token) to both passes."""
+    g = gen_lr()
+    for pass_ in (0, 1, 2, 3):
+        plain = dc.dynconv_workspace_bytes(prob(B=1, T=1000), g, pass_)
+        pk = dc.dynconv_workspace_bytes(packed(T=1000), g, pass_)
+        assert pk >= plain + 2 * 1000, pass_
+
+
+def test_decode_refuses_packing(L):
+    assert dec(L, packed(T=1), gen_hw()) == E_SHAPE

@@ -341,3 +341,81 @@ def test_near_size_limit_per_sequence(kind):
         assert torch.equal(a, b), f"{kind} {name}: the last sequences differ from a run of them alone"
     del h, x, dy, big, small
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# packed documents: one row holding documents back to back
+# ---------------------------------------------------------------------------
+def _cu(lens):
+    return list(np.cumsum([0] + list(lens)))
+
+
+# (workload with B = 1 and T = the total, document lengths): documents of 1,
+# 2 and 3 tokens (below k), an empty one, and documents spanning several tiles
+PACKED_LENS = (1, 2, 3, 70, 0, 5, 130, 33, 64)
+PACKED = [
+    Workload("pk_hw_bf16_hd68", B=1, T=308, d=96, D=544, k=4, kind=HEADWISE, n_heads=8, seed=71),
+    Workload("pk_hw_bf16_hd128_k3", B=1, T=308, d=64, D=1024, k=3, kind=HEADWISE, n_heads=8, seed=72),
+    Workload("pk_hw_bf16_hd16_k2", B=1, T=308, d=32, D=256, k=2, kind=HEADWISE, n_heads=16, seed=73),
+    Workload("pk_hw_bf16_hd4", B=1, T=308, d=16, D=64, k=4, kind=HEADWISE, n_heads=16, seed=74),
+    Workload("pk_hw_bf16_N256", B=1, T=308, d=64, D=512, k=4, kind=HEADWISE, n_heads=64, seed=75),
+    Workload("pk_lr_bf16_r16", B=1, T=308, d=128, D=360, k=4, kind=LOWRANK, rank=16, seed=76),
+    Workload("pk_lr_bf16_r16_D384", B=1, T=308, d=128, D=384, k=4, kind=LOWRANK, rank=16, seed=83),
+    Workload("pk_lr_bf16_r32_k3", B=1, T=308, d=64, D=1024, k=3, kind=LOWRANK, rank=32, seed=77),
+    Workload("pk_lr_bf16_r1_k1", B=1, T=308, d=32, D=64, k=1, kind=LOWRANK, rank=1, seed=78),
+    Workload("pk_lr_bf16_r64_k8", B=1, T=308, d=64, D=256, k=8, kind=LOWRANK, rank=64, seed=79),
+    Workload("pk_hw_fp32_k5", B=1, T=308, d=32, D=48, k=5, kind=HEADWISE, n_heads=3, dtype="fp32", seed=80),
+    Workload("pk_lr_fp32", B=1, T=308, d=32, D=64, k=4, kind=LOWRANK, rank=8, dtype="fp32", seed=81),
+    Workload("pk_lr_bf16_D100", B=1, T=308, d=64, D=100, k=3, kind=LOWRANK, rank=16, seed=82),
+]
+
+
+@pytest.mark.parametrize("w", PACKED, ids=[w.name for w in PACKED])
+def test_packed_parity(w):
+    """Packed documents against the oracle's packed reading (the window stops
+    at every document start), element by element."""
+    cu = _cu(PACKED_LENS)
+    assert cu[-1] == w.T
+    _note(f"[packed] {w.name} D={w.D} k={w.k} {w.kind} {w.dtype} docs={PACKED_LENS}")
+    inp = workloads.generate(w)
+    got = gu.gpu_run(w, gu.to_dev(inp), cu_seqlens=cu)
+    ref = gu.oracle_run(w, inp, cu_seqlens=cu)
+    errs = gu.compare(w, got, ref)
+    _note(f"[packed] {w.name} errors {errs}")
+
+
+@pytest.mark.parametrize("name", ["mamba2_inconv_headwise", "qkv_150m_lowrank"])
+def test_packed_equal_documents_are_the_batch(name):
+    """At full size: the B sequences of a workload packed into one row as B
+    documents give the batched run's outputs bitwise (the launch layouts
+    depend on the token count only, and the document table reproduces the
+    batch's sequence starts)."""
+    w = WORKLOADS[name]
+    _note(f"[packed full] {name}")
+    dev = gu.to_dev(workloads.generate(w))
+    a = gu.gpu_run(w, dev)
+    wp = w.with_(B=1, T=w.B * w.T)
+    devp = {k: (None if v is None else (v.reshape(1, w.B * w.T, -1) if k in ("h", "x", "dy") else v))
+            for k, v in dev.items()}
+    b = gu.gpu_run(wp, devp, cu_seqlens=[i * w.T for i in range(w.B + 1)])
+    for k in a:
+        if a[k] is not None:
+            assert torch.equal(a[k].reshape(-1), b[k].reshape(-1)), k
+    del dev, devp, a, b
+    torch.cuda.empty_cache()
+
+
+def test_packed_autograd_wrapper():
+    """DynConvFn with cu_seqlens equals the direct packed calls bitwise."""
+    w = PACKED[0]
+    cu = torch.tensor(_cu(PACKED_LENS), dtype=torch.int32, device="cuda")
+    dev = gu.to_dev(workloads.generate(w))
+    ref = gu.gpu_run(w, dev, cu_seqlens=_cu(PACKED_LENS))
+    leaves = {k: (None if dev.get(k) is None else dev[k].clone().requires_grad_(True))
+              for k in ("h", "x", "W", "w0")}
+    y = dc.DynConvFn.apply(leaves["h"], leaves["x"], leaves["W"], None, None, leaves["w0"], w.k, w.n_heads, cu)
+    y.backward(dev["dy"])
+    torch.cuda.synchronize()
+    assert torch.equal(y.detach(), ref["y"])
+    assert torch.equal(leaves["x"].grad, ref["dx"])
+    assert torch.equal(leaves["h"].grad, ref["dh"])
