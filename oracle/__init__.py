@@ -67,7 +67,8 @@ class OracleLib:
         lib.orc_filters.argtypes = [ctypes.POINTER(_Shape)] + [P] * 7
         lib.orc_conv.argtypes = [ctypes.POINTER(_Shape), P, P, P]
         lib.orc_backward.argtypes = [ctypes.POINTER(_Shape)] + [P] * 13
-        for f in (lib.orc_filters, lib.orc_conv, lib.orc_backward):
+        lib.orc_proj.argtypes = [ctypes.POINTER(_Shape), P, P, P]
+        for f in (lib.orc_filters, lib.orc_conv, lib.orc_backward, lib.orc_proj):
             f.restype = ctypes.c_int
         lib.orc_num_threads.restype = ctypes.c_int
         self.lib = lib
@@ -76,6 +77,15 @@ class OracleLib:
     def num_threads(self) -> int:
         """OpenMP threads the oracle runs on."""
         return int(self.lib.orc_num_threads())
+
+    def proj(self, s: "Shape", h, Wp):
+        """The producing projection x = h Wp ([B*T, D], float64)."""
+        cs = s._c()
+        h = _f64(h, (s.B * s.T, s.d))
+        Wp = _f64(Wp, (s.d, s.D))
+        x = np.empty((s.B * s.T, s.D), dtype=np.float64)
+        _check(self.lib.orc_proj(ctypes.byref(cs), _p(h), _p(Wp), _p(x)), "proj")
+        return x
 
     def filters(self, s: "Shape", h, W=None, A=None, U=None, w0=None):
         """Steps 1-2: returns (w[B*T, D, k], gen) with gen = u or z ([B*T, N])."""
@@ -211,6 +221,10 @@ def _check(rc: int, what: str):
 
 def num_threads() -> int:
     return default().num_threads()
+
+
+def proj(s: Shape, h, Wp):
+    return default().proj(s, h, Wp)
 
 
 def filters(s: Shape, h, W=None, A=None, U=None, w0=None):

@@ -334,3 +334,26 @@ int orc_backward(const orc_shape *s, const double *h, const double *W,
   free(g);
   return ORC_OK;
 }
+
+/*
+ * The producing projection the layer sits after (gist.science, Methodology ->
+ * Dynamic Short Convolutions, Placement: the convolution is applied to the
+ * query, key and value projections, or after any linear layer):
+ *   x_t[c] = sum_i h_t[i] * Wp[i, c]        Wp[d, D]
+ * The layer's input x is this projection of the same hidden state h that
+ * generates the filter, so a fused implementation reads h once for both.
+ */
+int orc_proj(const orc_shape *s, const double *h, const double *Wp, double *x) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (!h || !Wp || !x) return ORC_E_NULL;
+  const int64_t BT = s->B * s->T, d = s->d, D = s->D;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < BT; ++t)
+    for (int64_t c = 0; c < D; ++c) {
+      double acc = 0.0;
+      for (int64_t i = 0; i < d; ++i) acc += h[t * d + i] * Wp[i * D + c];
+      x[t * D + c] = acc;
+    }
+  return ORC_OK;
+}

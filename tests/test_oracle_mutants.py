@@ -35,6 +35,10 @@ MUTANTS = [
      "(((t_) - (j_) < 0)"),
     ("packed_doc_off_by_one", "return s->doc == NULL || s->doc[r1] == s->doc[r2];",
      "return s->doc == NULL || s->doc[r1] == s->doc[r2 > 0 ? r2 - 1 : r2];"),
+    # the producing projection: a transposed weight, a dropped row
+    ("proj_transposed", "acc += h[t * d + i] * Wp[i * D + c];", "acc += h[t * d + i] * Wp[(c % d) * D + (i % D)];"),
+    ("proj_drops_last_row", "for (int64_t i = 0; i < d; ++i) acc += h[t * d + i] * Wp",
+     "for (int64_t i = 0; i < d - 1; ++i) acc += h[t * d + i] * Wp"),
     ("head_index_interleaved", "const int64_t e = c / hd;", "const int64_t e = c % s->n_heads;"),
     ("lowrank_U_transposed", "for (int64_t m = 0; m < D * k; ++m) wt[m] += zq * Uq[m];",
      "for (int64_t m = 0; m < D * k; ++m) wt[m] += zq * U[m * N + q];"),
@@ -79,6 +83,8 @@ def _battery(orc):
     run("hw==lr", P.test_headwise_equals_lowrank)
     for base, lens in P.PACKED:
         run(f"packed:{lens}", P.test_packed_equals_documents_run_alone, base, lens)
+    for s in P.SHAPES:
+        run(f"proj:{s}", P.test_proj_is_matmul, s)
     return failed
 
 

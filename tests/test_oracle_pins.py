@@ -376,3 +376,19 @@ def test_equal_documents_are_the_batch(orc, s):
     for key in a:
         if a[key] is not None:
             assert np.array_equal(np.asarray(a[key]).reshape(-1), np.asarray(b[key]).reshape(-1)), key
+
+
+# ---------------------------------------------------------------------------
+# the producing projection x = h Wp (the layer's input, from the same h)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("s", SHAPES + EDGE_SHAPES[:2], ids=_ids(SHAPES + EDGE_SHAPES[:2]))
+def test_proj_is_matmul(orc, s):
+    """x = h Wp equals a numpy matmul, and a unit column of Wp copies a column of h."""
+    rng = np.random.default_rng(24)
+    h = rng.standard_normal((s.B * s.T, s.d))
+    Wp = rng.standard_normal((s.d, s.D))
+    np.testing.assert_allclose(orc.proj(s, h, Wp), h @ Wp, rtol=1e-13, atol=1e-13)
+    E = np.zeros((s.d, s.D))
+    for c in range(s.D):
+        E[c % s.d, c] = 1.0
+    assert np.array_equal(orc.proj(s, h, E), h[:, [c % s.d for c in range(s.D)]])
