@@ -145,6 +145,9 @@ def main() -> int:
     ap.add_argument("--decode", type=int, default=0, metavar="B",
                     help="instead of the training step, time dynconv_decode (one new token for each "
                          "of B sequences) on the workload's layer shape")
+    ap.add_argument("--proj", action="store_true",
+                    help="instead of the training step, time the forward with the producing "
+                         "projection fused in (dynconv_fwd_proj) beside torch.matmul + dynconv_fwd")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the layer, run --steps device copies of MIB MiB (a plain copy "
                          "kernel of known size, to scale the FETCH_SIZE / WRITE_SIZE counters)")
@@ -176,6 +179,8 @@ def main() -> int:
 
     if args.decode:
         return bench_decode(args, torch, dc)
+    if args.proj:
+        return bench_proj(args, torch, dc)
 
     w = workloads.WORKLOADS[args.workload]
     dev = torch.device("cuda", 0)
@@ -354,6 +359,86 @@ def bench_decode(args, torch, dc) -> int:
             "roofline": {"bound": "hbm", "achieved": round(nbytes / (us / 1e6) / 1e9, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(nbytes / (us / 1e6) / 1e9 / HBM_PEAK_GBS, 4),
                          "algorithmic_bytes_per_step": nbytes}}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def bench_proj(args, torch, dc) -> int:
+    """The forward with its producing projection: x = h Wp, then the layer on
+    x, as one dynconv_fwd_proj call (one matrix-core pass over h writes x and
+    the generator values) against torch.matmul(h, Wp) followed by dynconv_fwd
+    (two passes over h).  Inputs: the workload's seeded h and generator, Wp
+    from workloads.generate_proj_weight; two rotating sets."""
+    w = workloads.WORKLOADS[args.workload]
+    if w.dtype != "bf16":
+        print("bench.py --proj: the fused projection is timed on bf16 workloads", file=sys.stderr)
+        return 2
+    inp = workloads.generate(w, with_dy=False)
+    Wp = workloads.generate_proj_weight(w).cuda()
+    R = 2
+    sets = []
+    for _ in range(R):
+        s = {k: (None if v is None else v.cuda()) for k, v in inp.items() if k != "x"}
+        s["x"] = torch.empty(w.B, w.T, w.D, dtype=torch.bfloat16, device="cuda")
+        s["y"] = torch.empty_like(s["x"])
+        s["cache"] = torch.empty(w.tokens, w.gen_cols, dtype=torch.float32, device="cuda")
+        sets.append(s)
+    prob = dc.make_problem(sets[0]["x"], sets[0]["h"], w.k)
+    gen = dc.make_gen(sets[0].get("W"), sets[0].get("A"), sets[0].get("U"), sets[0].get("w0"), w.n_heads)
+    ws = torch.empty(max(1, dc.dynconv_workspace_bytes(prob, gen, dc.DYNCONV_WS_CACHED)), dtype=torch.uint8,
+                     device="cuda")
+
+    def g(s):
+        return dict(W=s.get("W"), A=s.get("A"), U=s.get("U"), w0=s.get("w0"), k=w.k, n_heads=w.n_heads)
+
+    def fused(i, trace=None):
+        s = sets[i % R]
+        if trace is not None:
+            dc.dynconv_trace_next(dc.DYNCONV_K_GEN_PROJ, trace[0], trace[1])
+        dc.dynconv_fwd_proj(s["h"], Wp, x=s["x"], y=s["y"], gen_cache=s["cache"], workspace=ws, **g(s))
+
+    def separate(i, trace=None):
+        s = sets[i % R]
+        torch.matmul(s["h"], Wp, out=s["x"])
+        dc.dynconv_fwd(s["h"], s["x"], y=s["y"], gen_cache=s["cache"], workspace=ws, **g(s))
+
+    def timed(fn, n_ev=0):
+        for i in range(args.warmup):
+            fn(i)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+        for a, b in ev:
+            a.record()
+            b.record()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for i in range(args.steps):
+            fn(args.warmup + i)
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / args.steps
+        for i, e in enumerate(ev):  # untimed steps: the fused GEMM's own duration
+            fn(i, trace=e)
+        torch.cuda.synchronize()
+        kms = sum(a.elapsed_time(b) for a, b in ev) / len(ev) if ev else None
+        return ms, kms
+
+    ms_f, kms = timed(fused, n_ev=max(1, args.mfma_steps))
+    print(f"[bench] {w.name}: fused {ms_f:.4f} ms/step", file=sys.stderr, flush=True)
+    ms_s, _ = timed(separate)
+    flops = 2 * w.tokens * w.d * (w.D + w.gen_cols)
+    tf = flops / (kms / 1e3) / 1e12
+    line = {"metric": "dynconv fwd with producing projection tokens/s", "value": round(w.tokens / (ms_f / 1e3), 1),
+            "unit": "tokens/s", "ms_per_step": round(ms_f, 4), "steps": args.steps, "warmup": args.warmup,
+            "higher_is_better": True, "dtype": "bf16",
+            "data": "synthetic (seeded N(0,1) h, N(0,1/d_model) Wp, the workload's generator and bias)",
+            "config": {**w.describe(), "tokens_per_step": w.tokens},
+            "separate": {"what": "torch.matmul(h, Wp) then dynconv_fwd", "ms_per_step": round(ms_s, 4),
+                         "tokens_per_s": round(w.tokens / (ms_s / 1e3), 1)},
+            "speedup_vs_separate": round(ms_s / ms_f, 3),
+            "roofline": {"bound": "mfma", "kernel": "proj_fused", "achieved": round(tf, 1),
+                         "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_PEAK_TFS, 4),
+                         "flops_per_launch": flops, "kernel_ms": round(kms, 5)}}
     print(json.dumps(line), flush=True)
     return 0
 

@@ -175,6 +175,27 @@ DYNCONV_API int dynconv_fwd(const dynconv_problem *p, const dynconv_gen *g, cons
                 hipStream_t stream);
 
 /*
+ * Forward with the producing projection fused in.  The layer sits after a
+ * linear projection of the same hidden state that generates its filters
+ * (gist.science Technical Summary, Methodology -> Dynamic Short
+ * Convolutions, Placement: on the query, key and value projections, or after
+ * any linear layer), so its input is x = h Wp.  This call computes that x and
+ * the generator values (u = h W or z = h A) in one pass over h (on the bf16
+ * path, one matrix-core GEMM against [Wp | W] or [Wp | A] with the weights
+ * read in place), then the layer on x as dynconv_fwd does:
+ *   x[t, c] = sum_i h[t, i] Wp[i, c]      (written to x, I/O dtype, rounded to nearest even)
+ *   y = x + dynconv(x)
+ *   Wp        [d_model, D], I/O dtype, row-major (the projection's weight)
+ *   x         output [B,T,D], I/O dtype
+ * Everything else as for dynconv_fwd (same workspace size).  x must not
+ * overlap any input or other output.  The projection's own backward (dh +=
+ * dx Wp^T, dWp = h^T dx) is the caller's: dynconv_bwd returns dx.
+ */
+DYNCONV_API int dynconv_fwd_proj(const dynconv_problem *p, const dynconv_gen *g, const void *h, const void *Wp,
+                                 void *x, void *y, void *gen_cache, void *workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
+/*
  * Forward for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid allocation):
  * dynconv_fwd with the same arguments except the workspace, which is a

@@ -53,7 +53,7 @@ class GenGrad(ctypes.Structure):
 
 
 # names the C header declares; the CPU tests check each is exported
-EXPORTS = ("dynconv_fwd", "dynconv_fwd_noalloc", "dynconv_bwd", "dynconv_decode", "dynconv_workspace_bytes",
+EXPORTS = ("dynconv_fwd", "dynconv_fwd_proj", "dynconv_fwd_noalloc", "dynconv_bwd", "dynconv_decode", "dynconv_workspace_bytes",
            "dynconv_gen_cache_bytes", "dynconv_status_str", "dynconv_abi_version", "dynconv_trace_next")
 DYNCONV_E_SCRATCH = -10
 NOALLOC_SCRATCH_BYTES = 16 << 20  # the static scratch of dynconv_fwd_noalloc
@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
         PP, PG, PGG = ctypes.POINTER(Problem), ctypes.POINTER(Gen), ctypes.POINTER(GenGrad)
         L.dynconv_fwd.argtypes = [PP, PG, P, P, P, P, P, ctypes.c_size_t, P]
         L.dynconv_fwd.restype = ctypes.c_int
+        L.dynconv_fwd_proj.argtypes = [PP, PG, P, P, P, P, P, P, ctypes.c_size_t, P]
+        L.dynconv_fwd_proj.restype = ctypes.c_int
         L.dynconv_fwd_noalloc.argtypes = [PP, PG, P, P, P, P, P]
         L.dynconv_fwd_noalloc.restype = ctypes.c_int
         L.dynconv_bwd.argtypes = [PP, PG, P, P, P, P, P, P, PGG, P, ctypes.c_size_t, P]
@@ -193,6 +195,29 @@ def dynconv_fwd(h, x, *, k, W=None, A=None, U=None, w0=None, n_heads=0, y=None, 
                            _stream(stream))
     _check(rc, "dynconv_fwd")
     return (y, gen_cache) if want_cache else y
+
+
+def dynconv_fwd_proj(h, Wp, *, k, W=None, A=None, U=None, w0=None, n_heads=0, x=None, y=None, gen_cache=None,
+                     want_cache=False, workspace=None, stream=None, cu_seqlens=None):
+    """Forward with the producing projection fused in: x = h Wp, then
+    y = x + dynconv(x).  Returns (x, y) (and the generator cache when
+    want_cache)."""
+    B, T = h.shape[0], h.shape[1]
+    if x is None:
+        x = torch.empty(B, T, Wp.shape[1], dtype=h.dtype, device=h.device)
+    prob = make_problem(x, h, k, cu_seqlens)
+    gen = make_gen(W, A, U, w0, n_heads)
+    if y is None:
+        y = torch.empty_like(x)
+    if gen_cache is None and want_cache:
+        n = gen.n_heads * k if gen.kind == DYNCONV_HEADWISE else gen.rank
+        gen_cache = torch.empty(B * T, n, dtype=torch.float32, device=h.device)
+    nbytes = dynconv_workspace_bytes(prob, gen, 0 | (DYNCONV_WS_CACHED if gen_cache is not None else 0))
+    ws = _workspace(nbytes, h.device, workspace)
+    rc = lib().dynconv_fwd_proj(ctypes.byref(prob), ctypes.byref(gen), _ptr(h), _ptr(Wp), _ptr(x), _ptr(y),
+                                _ptr(gen_cache), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check(rc, "dynconv_fwd_proj")
+    return (x, y, gen_cache) if want_cache else (x, y)
 
 
 def dynconv_fwd_noalloc(h, x, *, k, W=None, A=None, U=None, w0=None, n_heads=0, y=None, gen_cache=None,

@@ -218,16 +218,30 @@ int fwd_validate(const dynconv_problem *p, const dynconv_gen *g, const void *h, 
 }
 
 // Enqueues a validated forward: projection into the cache (the caller's, or
-// the workspace slot), then filter formation + conv + residual.
+// the workspace slot), then filter formation + conv + residual.  Wp != NULL:
+// the producing projection x = h Wp is computed first, fused with the
+// generator projection into one pass over h where the kernels take the
+// shape (x is then an output).
 int fwd_launch(const dynconv_problem *p, Shape s, int dtype, const dynconv_gen *g, const void *h, const void *x,
-               void *y, void *gen_cache, void *workspace, const Plan &pl, hipStream_t stream) {
+               void *y, void *gen_cache, void *workspace, const Plan &pl, hipStream_t stream,
+               const void *Wp = nullptr) {
   float *cache = gen_cache ? (float *)gen_cache : (float *)((char *)workspace + pl.cache);
   if (s.packed) {
     uint16_t *sp = (uint16_t *)((char *)workspace + pl.seqpos);
     seqpos_fill(p->cu_seqlens, p->n_seqs, s.BT, sp, stream);
     s.seqpos = sp;
   }
-  int rc = gen_proj(s, dtype, g, h, cache, workspace, pl, stream);
+  int rc;
+  if (Wp && dtype == DYNCONV_BF16 && proj_fused_ok(s)) {
+    rc = proj_fused(s, h, Wp, s.kind == DYNCONV_HEADWISE ? g->W : g->A, const_cast<void *>(x), cache, stream);
+  } else {
+    if (Wp) {
+      rc = dtype == DYNCONV_BF16 ? simple_proj<bf16>(s, h, Wp, const_cast<void *>(x), stream)
+                                 : simple_proj<float>(s, h, Wp, const_cast<void *>(x), stream);
+      if (rc) return rc;
+    }
+    rc = gen_proj(s, dtype, g, h, cache, workspace, pl, stream);
+  }
   if (rc) return rc;
   if (s.kind == DYNCONV_HEADWISE && vec_rows(s, dtype)) {
     rc = dtype == DYNCONV_BF16 ? fwd_headwise<bf16>(s, cache, g->w0, x, y, stream)
@@ -347,6 +361,29 @@ int dynconv_fwd(const dynconv_problem *p, const dynconv_gen *g, const void *h, c
   int rc = fwd_validate(p, g, h, x, y, gen_cache, workspace, workspace_bytes, true, s, pl);
   if (rc || s.BT == 0) return rc;
   return fwd_launch(p, s, p->dtype, g, h, x, y, gen_cache, workspace, pl, stream);
+}
+
+int dynconv_fwd_proj(const dynconv_problem *p, const dynconv_gen *g, const void *h, const void *Wp, void *x, void *y,
+                     void *gen_cache, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  Shape s;
+  Plan pl;
+  int rc = fwd_validate(p, g, h, x, y, gen_cache, workspace, workspace_bytes, true, s, pl);
+  if (rc || s.BT == 0) return rc;
+  if (!Wp) return DYNCONV_E_NULL;
+  if (!aligned16(Wp)) return DYNCONV_E_ALIGN;
+  // x is written here: it may overlap no input and no other output (the
+  // checks above covered y, the cache and the workspace against x)
+  const int eb = p->dtype == DYNCONV_BF16 ? 2 : 4;
+  const Sizes z = sizes(s, eb, p);
+  const Range wp{Wp, (size_t)s.d * s.D * eb}, xr{x, z.x};
+  const Range ins[] = {{h, z.h}, {g->W, z.W}, {g->A, z.A}, {g->U, z.U}, {g->w0, g->w0 ? z.w0 : 0},
+                       {p->cu_seqlens, z.cu}, wp};
+  for (const Range &i : ins)
+    if (overlap(xr, i)) return DYNCONV_E_ALIAS;
+  const Range outs[] = {{y, z.x}, {gen_cache, gen_cache ? z.cache : 0}, {workspace, pl.total}};
+  for (const Range &o : outs)
+    if (overlap(o, wp)) return DYNCONV_E_ALIAS;
+  return fwd_launch(p, s, p->dtype, g, h, x, y, gen_cache, workspace, pl, stream, Wp);
 }
 
 int dynconv_fwd_noalloc(const dynconv_problem *p, const dynconv_gen *g, const void *h, const void *x, void *y,

@@ -1,33 +1,39 @@
-// gen_proj_wide.hip -- the generator projection for wide generator weights on
-// bf16 matrix cores, the weight read in place.
+// gen_proj_wide.hip -- bf16 matrix-core projections of the hidden state with
+// the weights read in place:
 //
-//   out[t, n] = sum_i h[t, i] * M[i, n]     (u = h W head-wise, z = h A low-rank)
+//   the generator projection for wide generator weights
+//     out[t, n] = sum_i h[t, i] * M[i, n]     (u = h W head-wise, z = h A low-rank)
+//   and the producing projection fused with it
+//     [x | gen][t, :] = h[t, :] . [Wp | M]    x bf16 [BT, D], gen fp32 [BT, N]
 //
 // The filter is a learned linear map of the current hidden state
 // (gist.science Technical Summary of "Dynamic Short Convolutions Improve
 // Transformers", Methodology -> Dynamic Short Convolutions, Parameterization);
-// this is its first, dense factor: rows = tokens, K = d_model, N = n_heads*k
-// or rank, here a multiple of 8 from 64 to 256 (the head-wise weights of the
-// 2B-QKV and Mamba-2 shapes: 96 and 256 columns).
+// the generator projection is its first, dense factor (rows = tokens, K =
+// d_model, N = n_heads*k or rank: 64 to 256 columns here, e.g. 96 and 256 for
+// the 2B-QKV and Mamba-2 shapes).  The layer itself sits after a projection
+// of that same hidden state (Placement: on the query, key and value
+// projections, or after any linear layer), so the fused form reads h once
+// for both the layer's input x and the filter generator.
 //
-// Block: 4 waves (one per SIMD) = RG row groups of 32 rows x KS parts of K;
-// each wave takes all columns of its rows.  Per step of 64 k:
-//   * the wave multiplies its 32 rows by every 32-column tile of the staged
+// Block: 4 waves (one per SIMD) = RG row groups of 32 rows x KS parts of K,
+// over one slab of 32 NT columns (the grid walks row blocks x slabs, slabs
+// fastest, so the slabs of a row block share its rows of h in L2).  Per step
+// of 64 k:
+//   * each wave multiplies its 32 rows by every 32-column tile of the staged
 //     weight slice on v_mfma_f32_32x32x16_bf16, accumulators resident.  A
 //     fragments are four 16-byte loads per lane straight from h (the 128-byte
 //     run of each row), issued three steps ahead into a ring of three
-//     register sets, so every row is read by one wave only and the loads of
-//     the next two steps stay in flight across the barriers;
-//   * the weight slice (64 rows of N columns, contiguous in memory) is staged
-//     row-major in LDS, double-buffered, one barrier per step; its loads are
-//     issued a step ahead, before that step's A loads, so waiting for them
-//     never waits for A.  A B fragment is two ds_read_b64_tr_b16 (four k of
-//     one column each); the reads of the next k-substep are issued before the
-//     current substep's MFMAs.  Rows are padded by 64 bytes so that the four
-//     rows a 32-lane pass reads fall on disjoint quarters of the banks.
-// The K parts meet in LDS at the end in a fixed order.  h is read once from
-// HBM, the weight once per block from L2: the kernel is HBM-bound (bytes per
-// token 2 d + 4 N, against 2 d N flops on the matrix cores).
+//     register sets, so the loads of the next two steps stay in flight across
+//     the barriers;
+//   * the weight slice (64 rows of the slab's columns, contiguous in memory)
+//     is staged row-major in LDS, double-buffered, one barrier per step; its
+//     loads are issued a step ahead, before that step's A loads, so waiting
+//     for them never waits for A.  A B fragment is two ds_read_b64_tr_b16
+//     (four k of one column each); the reads of the next k-substep are issued
+//     before the current substep's MFMAs.  Rows are padded by 64 bytes so that
+//     the four rows a 32-lane pass reads fall on disjoint quarters of the banks.
+// The K parts meet in LDS at the end in a fixed order.
 #include "kernels.h"
 #include "bufio.h"
 #include "mfma.h"
@@ -40,7 +46,7 @@ constexpr int kKT = 64;  // k per step
 template <int NT, int RG, int KS>
 struct WideCfg {
   static constexpr int BM = RG * 32;            // rows per block
-  static constexpr int NP = NT * 32;            // staged columns (zeros past N)
+  static constexpr int NP = NT * 32;            // columns per slab (zeros past the weights)
   static constexpr int LDW = NP + 32;           // LDS row stride (bf16)
   static constexpr int SLICE = kKT * LDW;       // bf16 per staged slice
   static constexpr int STAGE = KS * SLICE;      // bf16 per stage (KS slices)
@@ -53,10 +59,19 @@ struct WideCfg {
   static_assert(KS == 1 || LDS >= (size_t)(KS - 1) * RG * NT * 16 * 64 * 4, "reduction buffer");
 };
 
-template <int NT, int RG, int KS>
+// The weight columns: [0, N0) from W0 (row stride N0), [N0, N0 + N1) from W1
+// (row stride N1); the outputs: columns below N0 to xb (bf16, row stride N0)
+// when it is given, every other column to out (fp32, row stride N - split).
+struct Cols {
+  const bf16 *W0, *W1;
+  int N0, N1;     // N0 and N1 are multiples of 8 (a 16-byte chunk is one source's)
+  bf16 *xb;       // fused: the producing projection's output x; else NULL
+  float *out;     // the generator values
+};
+
+template <int NT, int RG, int KS, bool FUSED>
 __global__ void __launch_bounds__(256, 1)
-k_gen_proj_wide(const bf16 *__restrict__ h, const bf16 *__restrict__ W, float *__restrict__ out, int64_t M,
-                int K, int N) {
+k_gen_proj_wide(const bf16 *__restrict__ h, Cols cols, int64_t M, int K, int n_slabs) {
   using C = WideCfg<NT, RG, KS>;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
   bf16 *bs = reinterpret_cast<bf16 *>(lds_raw);
@@ -64,10 +79,14 @@ k_gen_proj_wide(const bf16 *__restrict__ h, const bf16 *__restrict__ W, float *_
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rg = wave % RG, ks = wave / RG;
-  const int64_t row0 = (int64_t)blockIdx.x * C::BM;
+  const int slab = (int)(blockIdx.x % n_slabs);
+  const int64_t row0 = (int64_t)(blockIdx.x / n_slabs) * C::BM;
+  const int col0 = slab * C::NP;
+  const int N = cols.N0 + cols.N1;
   const int nrows = (int)min<int64_t>(C::BM, M - row0);
   const auto rh = make_rsrc(h + row0 * K, (uint32_t)((int64_t)nrows * K * 2));
-  const auto rw = make_rsrc(W, (uint32_t)((int64_t)K * N * 2));
+  const auto rw0 = make_rsrc(cols.W0, (uint32_t)((int64_t)K * cols.N0 * 2));
+  const auto rw1 = make_rsrc(cols.W1, FUSED ? (uint32_t)((int64_t)K * cols.N1 * 2) : 0u);
   const int S = (K + kKT - 1) / kKT;  // steps over all of K
   const int SH = (S + KS - 1) / KS;   // steps per K part (the last part may run past K: zeros)
 
@@ -77,11 +96,18 @@ k_gen_proj_wide(const bf16 *__restrict__ h, const bf16 *__restrict__ W, float *_
     for (int c = 0; c < C::CPT; ++c) {
       const int e = tid + c * 256;
       const int sl = e / (kKT * C::CPR), e2 = e - sl * (kKT * C::CPR);
-      const int r = e2 / C::CPR, cc = (e2 - r * C::CPR) * 8;
+      const int r = e2 / C::CPR, gc = col0 + (e2 - r * C::CPR) * 8;
       const int k = (sl * SH + st) * kKT + r;
-      // N is a multiple of 8: a chunk lies wholly inside or outside a row
-      const bool in = (C::CH % 256 == 0 || e < C::CH) && k < K && cc < N;
-      breg[c] = buf_load16(rw, in ? (uint32_t)(k * N + cc) * 2u : kOutside);
+      const bool live = (C::CH % 256 == 0 || e < C::CH) && k < K;
+      // a chunk lies wholly in one source, or past both (zeros); the other
+      // source's load falls outside its buffer and reads zeros, so no lane
+      // chooses between resources
+      breg[c] = buf_load16(rw0, live && gc < cols.N0 ? (uint32_t)(k * cols.N0 + gc) * 2u : kOutside);
+      if constexpr (FUSED) {
+        const uint4 b1 = buf_load16(
+            rw1, live && gc >= cols.N0 && gc < N ? (uint32_t)(k * cols.N1 + gc - cols.N0) * 2u : kOutside);
+        breg[c] = make_uint4(breg[c].x | b1.x, breg[c].y | b1.y, breg[c].z | b1.z, breg[c].w | b1.w);
+      }
     }
   };
   auto store_b = [&](int buf) {
@@ -196,35 +222,49 @@ k_gen_proj_wide(const bf16 *__restrict__ h, const bf16 *__restrict__ W, float *_
   }
 
   // D: lane holds D[8 b + 4 (lane / 32) + r][lane % 32] in element 4 b + r
+  const int split = FUSED ? cols.N0 : 0;
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
-    const int col = 32 * n + (lane & 31);
+    const int col = col0 + 32 * n + (lane & 31);
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = rg * 32 + 8 * b + 4 * (lane >> 5) + r;
-        if (col < N && row < nrows) out[(row0 + row) * N + col] = acc[n][4 * b + r];
+        if (col >= N || row >= nrows) continue;
+        const float v = acc[n][4 * b + r];
+        if (FUSED && col < split)
+          cols.xb[(row0 + row) * cols.N0 + col] = (bf16)v;  // round to nearest even
+        else
+          cols.out[(row0 + row) * (N - split) + col - split] = v;
       }
   }
 }
 
-template <int NT, int RG, int KS>
-void launch(const bf16 *h, const bf16 *W, float *out, int64_t M, int K, int N, hipStream_t st) {
+template <int NT, int RG, int KS, bool FUSED>
+void launch(const bf16 *h, const Cols &cols, int64_t M, int K, hipStream_t st) {
   using C = WideCfg<NT, RG, KS>;
   const size_t lds = C::LDS;
-  hipLaunchKernelGGL((k_gen_proj_wide<NT, RG, KS>), dim3((unsigned)ceil_div(M, C::BM)), dim3(256), lds, st, h, W,
-                     out, M, K, N);
+  const int n_slabs = (int)ceil_div(cols.N0 + cols.N1, C::NP);
+  hipLaunchKernelGGL((k_gen_proj_wide<NT, RG, KS, FUSED>), dim3((unsigned)(ceil_div(M, C::BM) * n_slabs)),
+                     dim3(256), lds, st, h, cols, M, K, n_slabs);
 }
 
-// One block of 4 waves per CU: 128-row blocks when the rows give 256 of
-// them, else 64-row blocks with K in two parts.
-template <int NT>
-void launch_nt(const bf16 *h, const bf16 *W, float *out, int64_t M, int K, int N, hipStream_t st) {
-  if (M >= 256 * 128)
-    launch<NT, 4, 1>(h, W, out, M, K, N, st);
-  else
-    launch<NT, 2, 2>(h, W, out, M, K, N, st);
+// One block of 4 waves per CU: 128-row blocks when the blocks number at least
+// 256, else 64-row blocks with K in two parts.  The fused form always takes
+// 128-row blocks: its slabs are many (the producing projection's D columns),
+// and its two-part variant would spill registers.
+template <int NT, bool FUSED>
+void launch_nt(const bf16 *h, const Cols &cols, int64_t M, int K, hipStream_t st) {
+  const int64_t slabs = ceil_div(cols.N0 + cols.N1, NT * 32);
+  if constexpr (FUSED) {
+    launch<NT, 4, 1, true>(h, cols, M, K, st);
+  } else {
+    if (ceil_div(M, 128) * slabs >= 256)
+      launch<NT, 4, 1, false>(h, cols, M, K, st);
+    else
+      launch<NT, 2, 2, false>(h, cols, M, K, st);
+  }
 }
 
 }  // namespace
@@ -236,17 +276,33 @@ bool gen_proj_wide_ok(const Shape &s) {
 
 int gen_proj_wide(const Shape &s, const void *h, const void *M, float *out, hipStream_t st) {
   const bool tr = trace_begin(DYNCONV_K_GEN_PROJ, st);
-  const bf16 *hh = (const bf16 *)h, *W = (const bf16 *)M;
-  const int K = (int)s.d, N = s.N;
-  switch (ceil_div(N, 32)) {
-    case 2: launch_nt<2>(hh, W, out, s.BT, K, N, st); break;
-    case 3: launch_nt<3>(hh, W, out, s.BT, K, N, st); break;
-    case 4: launch_nt<4>(hh, W, out, s.BT, K, N, st); break;
-    case 5: launch_nt<5>(hh, W, out, s.BT, K, N, st); break;
-    case 6: launch_nt<6>(hh, W, out, s.BT, K, N, st); break;
-    case 7: launch_nt<7>(hh, W, out, s.BT, K, N, st); break;
-    default: launch_nt<8>(hh, W, out, s.BT, K, N, st); break;
+  const bf16 *hh = (const bf16 *)h;
+  const Cols cols{(const bf16 *)M, nullptr, s.N, 0, nullptr, out};
+  const int K = (int)s.d;
+  switch (ceil_div(s.N, 32)) {
+    case 2: launch_nt<2, false>(hh, cols, s.BT, K, st); break;
+    case 3: launch_nt<3, false>(hh, cols, s.BT, K, st); break;
+    case 4: launch_nt<4, false>(hh, cols, s.BT, K, st); break;
+    case 5: launch_nt<5, false>(hh, cols, s.BT, K, st); break;
+    case 6: launch_nt<6, false>(hh, cols, s.BT, K, st); break;
+    case 7: launch_nt<7, false>(hh, cols, s.BT, K, st); break;
+    default: launch_nt<8, false>(hh, cols, s.BT, K, st); break;
   }
+  trace_end(tr, st);
+  return 0;
+}
+
+bool proj_fused_ok(const Shape &s) {
+  // chunk-aligned sources; 32-bit byte offsets into h, both weights and x
+  const int64_t lim = ((int64_t)1 << 31) - 64;
+  return s.D % 8 == 0 && s.N % 8 == 0 && s.d % 8 == 0 && s.d * s.D * 2 < lim && s.d * s.N * 2 < lim &&
+         s.BT * s.D * 2 < lim && s.BT * s.d * 2 < lim;
+}
+
+int proj_fused(const Shape &s, const void *h, const void *Wp, const void *M, void *x, float *gen, hipStream_t st) {
+  const bool tr = trace_begin(DYNCONV_K_GEN_PROJ, st);
+  const Cols cols{(const bf16 *)Wp, (const bf16 *)M, (int)s.D, s.N, (bf16 *)x, gen};
+  launch_nt<8, true>((const bf16 *)h, cols, s.BT, (int)s.d, st);
   trace_end(tr, st);
   return 0;
 }

@@ -39,6 +39,13 @@ int gen_proj_mfma(const Shape &s, const void *h, const void *M, float *out, void
 // wide weights (N a multiple of 8, 64..256 columns), read in place (gen_proj_wide.hip)
 bool gen_proj_wide_ok(const Shape &s);
 int gen_proj_wide(const Shape &s, const void *h, const void *M, float *out, hipStream_t st);
+// the producing projection x = h Wp fused with it: one pass over h writes x
+// (bf16 [BT, D]) and the generator values (fp32 [BT, N]) (gen_proj_wide.hip)
+bool proj_fused_ok(const Shape &s);
+int proj_fused(const Shape &s, const void *h, const void *Wp, const void *M, void *x, float *gen, hipStream_t st);
+// the producing projection alone, plain kernel: x[t, c] = sum_i h[t, i] Wp[i, c] in T
+template <typename T>
+int simple_proj(const Shape &s, const void *h, const void *Wp, void *x, hipStream_t st);
 
 // --- head-wise forward conv, coalesced per-vector walk (conv_fwd_headwise.hip) ---
 template <typename T>

@@ -31,6 +31,19 @@ k_gen_proj(const T *__restrict__ a, const T *__restrict__ m, float *__restrict__
   out[g] = acc;
 }
 
+// the producing projection: x[t, c] = sum_i h[t, i] * Wp[i, c], written in T
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_proj_simple(const T *__restrict__ h, const T *__restrict__ Wp, T *__restrict__ x, int64_t rows, int64_t K,
+              int64_t D) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= rows * D) return;
+  const int64_t t = g / D, c = g - t * D;
+  float acc = 0.f;
+  for (int64_t i = 0; i < K; ++i) acc = fmaf(to_f32(h[t * K + i]), to_f32(Wp[i * D + c]), acc);
+  x[g] = from_f32<T>(acc);
+}
+
 // Filter tap j of channel c at token row `row`:
 // head-wise u[row, head(c)*k + j] + w0, low-rank sum_q z[row,q] U[q, c*k+j] + w0.
 template <typename T>
@@ -324,8 +337,17 @@ int simple_bwd(const Shape &s, const float *gen, const void *W, const void *A, c
   return 0;
 }
 
+template <typename T>
+int simple_proj(const Shape &s, const void *h, const void *Wp, void *x, hipStream_t st) {
+  if (s.BT * s.D == 0) return 0;
+  hipLaunchKernelGGL(k_proj_simple<T>, grid1(s.BT * s.D), dim3(256), 0, st, (const T *)h, (const T *)Wp, (T *)x,
+                     s.BT, s.d, s.D);
+  return 0;
+}
+
 #define INST(T)                                                                                  \
   template int simple_gen_proj<T>(const Shape &, const void *, const void *, float *, hipStream_t); \
+  template int simple_proj<T>(const Shape &, const void *, const void *, void *, hipStream_t);       \
   template int simple_fwd_conv<T>(const Shape &, const float *, const void *, const void *,        \
                                   const void *, void *, hipStream_t);                             \
   template int simple_bwd<T>(const Shape &, const float *, const void *, const void *,            \

@@ -319,6 +319,47 @@ def test_fwd_noalloc_validation(L, case, expect):
     assert fwd_na(L, p, g, **kw) == expect
 
 
+def fwd_pj(L, p, g, h=addr(1), Wp=addr(14), x=addr(2), y=addr(3), cache=None, ws=addr(20), ws_bytes=1 << 30):
+    return L.dynconv_fwd_proj(ctypes.byref(p), ctypes.byref(g), h, Wp, x, y, cache, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("ok_empty", OK), ("null_Wp", E_NULL), ("align_Wp", E_ALIGN), ("null_x", E_NULL),
+    ("alias_x_Wp", E_ALIAS), ("alias_x_h", E_ALIAS), ("alias_x_W", E_ALIAS), ("alias_y_Wp", E_ALIAS),
+    ("alias_cache_Wp", E_ALIAS), ("alias_ws_Wp", E_ALIAS), ("ws_small", E_WORKSPACE), ("k9", E_K),
+])
+def test_fwd_proj_validation(L, case, expect):
+    """dynconv_fwd_proj: x is an output here, so it may overlap neither the
+    inputs (h, the generator weights, Wp) nor the other outputs."""
+    p, g = prob(), gen_hw()
+    kw = {}
+    if case == "ok_empty":
+        p = prob(B=0)
+    elif case == "null_Wp":
+        kw["Wp"] = None
+    elif case == "align_Wp":
+        kw["Wp"] = addr(14) + 4
+    elif case == "null_x":
+        kw["x"] = None
+    elif case == "alias_x_Wp":
+        kw["x"] = addr(14) + 256
+    elif case == "alias_x_h":
+        kw["x"] = addr(1) + 256
+    elif case == "alias_x_W":
+        kw["x"] = addr(10)
+    elif case == "alias_y_Wp":
+        kw["y"] = addr(14)
+    elif case == "alias_cache_Wp":
+        kw["cache"] = addr(14) + 512
+    elif case == "alias_ws_Wp":
+        kw["ws"] = addr(14) - 256
+    elif case == "ws_small":
+        kw["ws_bytes"] = 16
+    elif case == "k9":
+        p = prob(k=9)
+    assert fwd_pj(L, p, g, **kw) == expect
+
+
 def packed(B=1, T=64, n_seqs=3, cu=addr(30), **kw):
     p = prob(B=B, T=T, **kw)
     p.cu_seqlens = cu

@@ -129,3 +129,12 @@ def generate(w: Workload, with_dy: bool = True) -> dict:
     if with_dy:
         out["dy"] = randn(w.B, w.T, w.D)
     return out
+
+
+def generate_proj_weight(w: Workload) -> torch.Tensor:
+    """The producing projection's weight Wp[d_model, D] (for the fused form
+    x = h Wp) in the I/O dtype: i.i.d. N(0, 1/d_model), so that x has about
+    unit variance, from its own stream (seed + 1000) so the other inputs of
+    ``w`` keep their values."""
+    g = torch.Generator().manual_seed(w.seed + 1000)
+    return (torch.randn(w.d, w.D, generator=g, dtype=torch.float32) * w.d ** -0.5).to(w.torch_dtype)
