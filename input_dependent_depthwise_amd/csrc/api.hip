@@ -120,7 +120,7 @@ Plan plan(const Shape &s, int dtype, int pass, bool cached) {
   };
   // (64 bytes of padding: kernels read the table four tokens at a time, a
   // few groups past the last token)
-  if (s.packed) pl.seqpos = take((size_t)s.BT * sizeof(uint16_t) + 64);
+  if (s.packed) pl.seqpos = take((size_t)s.BT * sizeof(uint16_t) + 128);
   if (!cached) pl.cache = take((size_t)s.BT * s.N * sizeof(float));
   // the projection runs in the forward, and in the backward only to rebuild a missing cache
   if (mfma_proj(s, dtype) && (pass == 0 || !cached)) pl.mt = take(gen_proj_mfma_ws_bytes(s));

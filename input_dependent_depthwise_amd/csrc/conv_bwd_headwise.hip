@@ -18,8 +18,11 @@
 //     accumulator of token t-j, which is complete (and stored) k-1 steps later;
 //   * du partials per lane are bf16 dot products over the lane's channel pairs
 //     (v_dot2), then summed over the lanes of a head either with DPP
-//     transpose-reductions (heads of 1..16 lanes, aligned) or through LDS
-//     (any other head width), and written as one fp32 partial per span;
+//     transpose-reductions (heads of 1..16 lanes, aligned) or as differences
+//     of a wave-wide prefix sum (any other head width), and written as one
+//     fp32 partial per span.  Head widths of 4 mod 8 (e.g. 68) keep 8
+//     channels per lane: a lane's two quads of 4 channels may then lie in two
+//     heads, each quad with its own u and its own du sum;
 //   * dw0 accumulates in registers over the wave's tokens; the block's 4 waves
 //     (same span, consecutive token runs) add theirs in LDS and write one
 //     fp32 partial per block, summed later in a fixed order.
@@ -163,14 +166,23 @@ __device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
 }
 
 // S: lanes per head when heads are 1..16 lanes wide and aligned to spans; 0:
-// any head width (LDS reduction).  VAR: packed documents (positions from the
-// per-token table).
+// any head width that is a multiple of CPL (prefix sums); -1 (CPL = 8): head
+// widths of 4 mod 8, at least 12 (prefix sums over channel quads).  VAR:
+// packed documents (positions from the per-token table).
 template <int K, int CPL, int S, bool VAR>
 __global__ void __launch_bounds__(256, 2)
 k_bwd_hw(Params P) {
+  constexpr bool QUAD = S < 0;
+  static_assert(!QUAD || CPL == 8, "quad heads: 8 channels per lane");
   constexpr int NP = CPL / 2;        // bf16 pairs per lane
   constexpr int SPAN = 64 * CPL;
-  constexpr int PD = 4;              // tokens loaded ahead
+  // Tokens loaded ahead.  Eight (with rings twice as deep) measured no
+  // faster: the compiler's wait counts across the per-token branches then
+  // stop short of the deeper rings.
+  constexpr int PD = 4;
+  constexpr int XS = 2 * PD;         // x ring slots: the k-tap history plus the loads in flight
+  constexpr int YS = PD;             // dy and u ring slots
+  constexpr int BLK = 2 * PD;        // tokens per unrolled block
   const Shape &s = P.s;
 
   __shared__ __attribute__((aligned(16))) float dwred[4][64 * CPL * K];
@@ -185,6 +197,7 @@ k_bwd_hw(Params P) {
   const bool all_act = span_c0 + SPAN <= Dc;
   const int cc = act ? c0 : Dc - CPL;  // clamped: inactive lanes read valid memory, use dy = 0
   const int e = (int)(cc / s.hd);
+  const int e2 = QUAD ? (int)((cc + 4) / s.hd) : e;  // head of the lane's second quad
   const int e_lo = (int)(span_c0 / s.hd);
   const int BT = (int)s.BT;  // the host keeps every tensor below 2 GiB (32-bit byte offsets)
   const int T = s.T;
@@ -222,7 +235,7 @@ k_bwd_hw(Params P) {
   const uint32_t row_x = (uint32_t)s.D * 2u, row_u = (uint32_t)s.N * 4u;
   const auto rx = rsrc(P.x, (uint32_t)(BT * row_x)), rdy = rsrc(P.dy, (uint32_t)(BT * row_x));
   const auto rdx = rsrc(P.dx, (uint32_t)(BT * row_x)), ru = rsrc(P.u, (uint32_t)(BT * row_u));
-  const uint32_t voff_x = (uint32_t)cc * 2u, voff_u = (uint32_t)e * K * 4u;
+  const uint32_t voff_x = (uint32_t)cc * 2u, voff_u = (uint32_t)e * K * 4u, voff_u2 = (uint32_t)e2 * K * 4u;
   // du partials of this span: [BT][R] fp32
   const uint32_t row_g = (uint32_t)P.R * 4u;
   const auto rg = rsrc(P.gpart + (size_t)span * BT * P.R, (uint32_t)BT * row_g);
@@ -238,13 +251,33 @@ k_bwd_hw(Params P) {
     const int lb = min(nact, ((e + 1) * s.hd - span_c0) / CPL);
     hlast = act && lane == lb - 1;
   }
+  // quad heads: at most one head starts in a lane, at its first quad (qA) or
+  // its second (qB); sb = the wave's prefix sum up to that start.  The lane
+  // holding the start of head h+1 writes head h's sum (its sb minus the sb of
+  // the lane where h starts, or minus 0 when h starts at or before the span);
+  // the last active lane also writes the head of its second quad (its
+  // inclusive prefix minus that head's start).  q_src: the lane whose sb this
+  // lane needs (h's start for the first write, else the last quad's head's).
+  bool qA = false, qB = false, q_prev = false, q_last = false, q_zero = true;
+  int q_src = 0;
+  if constexpr (QUAD) {
+    const int hd = (int)s.hd;
+    const int nact = all_act ? 64 : (Dc - span_c0) / CPL;
+    qA = act && cc % hd == 0;
+    qB = act && (cc + 4) % hd == 0;
+    q_prev = (qA && lane > 0) || qB;
+    q_last = act && lane == nact - 1;
+    const int st = (q_prev ? e2 - 1 : e2) * hd - span_c0;  // that head's first channel, from the span start
+    q_zero = st <= 0;
+    q_src = q_zero ? 0 : st / CPL;
+  }
 
   if (t_a < BT) {
-    // token rings: x in 8 slots (slot = (t - t_a) mod 8) holding tokens
-    // t-3 .. t+PD (the k-tap history plus the loads in flight), dy and u in 4
-    // (slot = (t - t_a) mod 4) holding tokens t .. t+PD
-    uint32_t xr[8][NP], dyr[4][NP];
-    float ur[4][4];
+    // token rings: x in XS slots (slot = (t - t_a) mod XS) holding tokens
+    // t-3 .. t+PD (the k-tap history plus the loads in flight), dy and u in YS
+    // (slot = (t - t_a) mod YS) holding tokens t .. t+PD
+    uint32_t xr[XS][NP], dyr[YS][NP];
+    float ur[YS][4], ur2[YS][4];  // u of the lane's head (quad heads: of each quad's head)
     float acc[4][CPL];  // dx accumulators (slot = (s - t_a) mod 4)
 #pragma unroll
     for (int a = 0; a < 4; ++a)
@@ -256,8 +289,9 @@ k_bwd_hw(Params P) {
     // a block in two scalar loads issued a block ahead (t_a and the run length
     // are multiples of 4; the table is padded past its last token)
     const uint64_t *sp4 = reinterpret_cast<const uint64_t *>(s.seqpos);
-    uint64_t pn[2] = {0, 0};
-    if constexpr (VAR) pn[0] = sp4[t_a >> 2], pn[1] = sp4[(t_a >> 2) + 1];
+    uint64_t pn[BLK / 4];
+#pragma unroll
+    for (int q = 0; q < BLK / 4; ++q) pn[q] = VAR ? sp4[(t_a >> 2) + q] : 0;
     // Loads are unconditional: row offsets are clamped to the batch, and what
     // they bring past the run is never consumed (tokens past t_end are not
     // processed, x past t_b feeds no product, and every token past the batch
@@ -267,15 +301,16 @@ k_bwd_hw(Params P) {
     // skipped by the position tests, not zeroed)
 #pragma unroll
     for (int j = 3; j >= 1; --j) {
-      if (j < K) bload<CPL>(rx, voff_x, row(t_a - j) * row_x, xr[8 - j]);
+      if (j < K) bload<CPL>(rx, voff_x, row(t_a - j) * row_x, xr[XS - j]);
       __builtin_amdgcn_sched_barrier(0);
     }
     // token t into x slot xs, dy and u slot xs mod 4
     auto load_tok = [&](int t, int xs) {
       const uint32_t r = row(t);
       bload<CPL>(rx, voff_x, r * row_x, xr[xs]);
-      bload<CPL>(rdy, voff_x, r * row_x, dyr[xs & 3]);
-      bload_u<K>(ru, voff_u, r * row_u, ur[xs & 3]);
+      bload<CPL>(rdy, voff_x, r * row_x, dyr[xs & (YS - 1)]);
+      bload_u<K>(ru, voff_u, r * row_u, ur[xs & (YS - 1)]);
+      if constexpr (QUAD) bload_u<K>(ru, voff_u2, r * row_u, ur2[xs & (YS - 1)]);
     };
     // (issued in the loop's own order, so that the wait counts the compiler
     // derives at the loop head hold for the first pass too)
@@ -288,20 +323,26 @@ k_bwd_hw(Params P) {
     // Registers of the last stores stay reserved until the next token's loads
     // are issued: on this target a register read by a pending store can only be
     // rewritten after a vmcnt wait, which would also drain the loads in flight.
-    uint32_t held[NP + 4];  // dx of this token, du of the previous one
+    constexpr int NH = NP + (QUAD ? 8 : 4);
+    uint32_t held[NH];  // dx of this token, du of the previous one
 #pragma unroll
-    for (int p = 0; p < NP + 4; ++p) held[p] = 0u;
+    for (int p = 0; p < NH; ++p) held[p] = 0u;
 
-    // one block of 8 tokens from tg.  The tests on t and pos are wave-uniform
+    // one block of BLK tokens from tg.  The tests on t and pos are wave-uniform
     // (scalar branches); keeping them in every block rather than compiling a
     // second, test-free copy keeps the register allocation of the rings simple.
     auto block = [&](int tg) {
-      const uint64_t pc[2] = {pn[0], pn[1]};
-      if constexpr (VAR) pn[0] = sp4[(tg >> 2) + 2], pn[1] = sp4[(tg >> 2) + 3];
+      uint64_t pc[BLK / 4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int q = 0; q < BLK / 4; ++q) {
+        pc[q] = pn[q];
+        if constexpr (VAR) pn[q] = sp4[(tg >> 2) + BLK / 4 + q];
+      }
+#pragma unroll
+      for (int i = 0; i < BLK; ++i) {
         const int t = tg + i;
         float vals[4] = {0.f, 0.f, 0.f, 0.f};
+        float valsb[4] = {0.f, 0.f, 0.f, 0.f};  // quad heads: the second quad's sums
         // a token past the batch end starts a new "sequence" (its loads were clamped)
         if constexpr (VAR) pos = t < BT ? (int)((pc[i >> 2] >> (16 * (i & 3))) & 255u) : 0;
         if (t < t_end) {
@@ -310,7 +351,7 @@ k_bwd_hw(Params P) {
           // channels; nothing of theirs is stored or summed)
           uint32_t dw[NP];
 #pragma unroll
-          for (int p = 0; p < NP; ++p) dw[p] = dyr[i & 3][p];
+          for (int p = 0; p < NP; ++p) dw[p] = dyr[i & (YS - 1)][p];
           // dy as fp32 and as bf16 pairs with one half cleared
           float dyf[CPL];
           uint32_t dlo[NP], dhi[NP];
@@ -325,9 +366,14 @@ k_bwd_hw(Params P) {
 #pragma unroll
           for (int j = 0; j < K; ++j) {
             if (j == 0 || pos >= j) {
-              const int xs = (i - j) & 7;
+              const int xs = (i - j) & (XS - 1);
 #pragma unroll
-              for (int p = 0; p < NP; ++p) vals[j] = dot2(xr[xs][p], dw[p], vals[j]);
+              for (int p = 0; p < NP; ++p) {
+                if (QUAD && p >= 2)
+                  valsb[j] = dot2(xr[xs][p], dw[p], valsb[j]);
+                else
+                  vals[j] = dot2(xr[xs][p], dw[p], vals[j]);
+              }
               if (main) {
 #pragma unroll
                 for (int p = 0; p < NP; ++p) {
@@ -339,14 +385,19 @@ k_bwd_hw(Params P) {
           }
           if (main) {
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) acc[i & 3][c] = fmaf(ur[i & 3][0] + w0r[c][0], dyf[c], dyf[c]);
+            for (int c = 0; c < CPL; ++c) {
+              const float u0 = (QUAD && c >= 4) ? ur2[i & (YS - 1)][0] : ur[i & (YS - 1)][0];
+              acc[i & 3][c] = fmaf(u0 + w0r[c][0], dyf[c], dyf[c]);
+            }
           }
 #pragma unroll
           for (int j = 1; j < K; ++j) {
             if (pos >= j) {
 #pragma unroll
-              for (int c = 0; c < CPL; ++c)
-                acc[(i - j) & 3][c] = fmaf(ur[i & 3][j] + w0r[c][j], dyf[c], acc[(i - j) & 3][c]);
+              for (int c = 0; c < CPL; ++c) {
+                const float uj = (QUAD && c >= 4) ? ur2[i & (YS - 1)][j] : ur[i & (YS - 1)][j];
+                acc[(i - j) & 3][c] = fmaf(uj + w0r[c][j], dyf[c], acc[(i - j) & 3][c]);
+              }
             }
           }
           // token t-k+1 has all its terms
@@ -371,11 +422,11 @@ k_bwd_hw(Params P) {
           }
         }
         // refill: token t+PD into the slot just released
-        load_tok(t + PD, (i + PD) & 7);
+        load_tok(t + PD, (i + PD) & (XS - 1));
         // the previous token's stores have been followed by these loads; their
         // registers may be reused from here on
 #pragma unroll
-        for (int p = 0; p < NP + 4; ++p) asm volatile("" ::"v"(held[p]));
+        for (int p = 0; p < NH; ++p) asm volatile("" ::"v"(held[p]));
         // du of this token: sum over the lanes of each head
         if constexpr (S > 0) {
           if (t < t_b) {
@@ -397,6 +448,41 @@ k_bwd_hw(Params P) {
                 __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(vals[0]), rg, voff_g + (uint32_t)j * 4u, so_g,
                                                       0);
               held[NP] = __float_as_uint(vals[0]);
+            }
+          }
+        } else if constexpr (QUAD) {
+          if (t < t_b) {
+            float hp[4], hl[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float pre = wave_prefix(vals[j] + valsb[j]);
+              const float sb = pre - valsb[j] - (qA ? vals[j] : 0.f);
+              const float got =
+                  __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(4 * q_src, __builtin_bit_cast(int, sb)));
+              const float start = q_zero ? 0.f : got;
+              hp[j] = sb - start;
+              hl[j] = pre - ((qA || qB) ? sb : start);
+            }
+            const uint32_t og = (uint32_t)t * row_g;
+            const uint32_t op = og + (uint32_t)(e2 - 1 - e_lo) * K * 4u, ol = og + (uint32_t)(e2 - e_lo) * K * 4u;
+            if constexpr (K == 4) {
+              buf_store16(rg, q_prev ? op : kOutside,
+                          make_uint4(__float_as_uint(hp[0]), __float_as_uint(hp[1]), __float_as_uint(hp[2]),
+                                     __float_as_uint(hp[3])));
+              buf_store16(rg, q_last ? ol : kOutside,
+                          make_uint4(__float_as_uint(hl[0]), __float_as_uint(hl[1]), __float_as_uint(hl[2]),
+                                     __float_as_uint(hl[3])));
+            } else {
+#pragma unroll
+              for (int j = 0; j < K; ++j) {
+                buf_store_f32(rg, q_prev ? op + (uint32_t)j * 4u : kOutside, hp[j]);
+                buf_store_f32(rg, q_last ? ol + (uint32_t)j * 4u : kOutside, hl[j]);
+              }
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              held[NP + j] = __float_as_uint(hp[j]);
+              held[NP + 4 + j] = __float_as_uint(hl[j]);
             }
           }
         } else {
@@ -430,7 +516,7 @@ k_bwd_hw(Params P) {
       }
     };
 
-    for (int tg = t_a; tg < t_end; tg += 8) block(tg);
+    for (int tg = t_a; tg < t_end; tg += BLK) block(tg);
   }
 
   // dw0: add the block's 4 waves (same channels), one partial per block
@@ -453,7 +539,11 @@ k_bwd_hw(Params P) {
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-static int hw_cpl(const Shape &s) { return (s.hd % 8 == 0) ? 8 : (s.hd % 4 == 0 ? 4 : 0); }
+// channels per lane: 8 when heads are a multiple of 8 wide, or 4 mod 8 and
+// at least 12 (quad heads); 4 for heads of 4 channels
+static bool hw_quad(const Shape &s) { return s.hd % 8 == 4 && s.hd >= 12; }
+static int hw_cpl(const Shape &s) {
+  return (s.hd % 8 == 0 || hw_quad(s)) ? 8 : (s.hd % 4 == 0 ? 4 : 0); }
 
 BwdLayout bwd_headwise_layout(const Shape &s) {
   BwdLayout L = {};
@@ -461,13 +551,18 @@ BwdLayout bwd_headwise_layout(const Shape &s) {
   const int span = 64 * cpl;
   L.Dt = span;
   L.n_slices = (int)ceil_div(s.D, span);
-  // tokens per wave: about one round of resident waves over 256 CUs (the
-  // 8-channel variants with k >= 3 hold 2 waves per SIMD, the others 4)
-  const int waves_per_cu = (cpl == 8 && s.k >= 3) ? 8 : 16;
-  int64_t l = ceil_div(s.BT * L.n_slices, 256 * waves_per_cu);
+  // Blocks (4 waves, one per SIMD) resident per CU, from each variant's
+  // register count (512 per SIMD lane): the grid is sized to one round of
+  // them over the 256 CUs, never more, so no block waits for a second round.
+  static const int kBlocksPerCU[3][4] = {{8, 6, 5, 4},   // 4 channels per lane, k = 1..4
+                                         {6, 3, 3, 2},   // 8 channels per lane
+                                         {5, 3, 2, 2}};  // quad heads
+  const int64_t slots = 256 * kBlocksPerCU[hw_quad(s) ? 2 : (cpl == 8)][s.k - 1];
+  const int64_t ranges = slots / L.n_slices > 1 ? slots / L.n_slices : 1;
+  int64_t l = ceil_div(s.BT, 4 * ranges);  // tokens per wave
   l = (l + 3) / 4 * 4;
   if (l < 4) l = 4;
-  L.tpb = (int)l;  // tokens per wave
+  L.tpb = (int)l;
   L.n_tiles = 0;
   L.n_ranges = (int)ceil_div(s.BT, 4 * l);
   int sl = 0;
@@ -509,7 +604,9 @@ int bwd_headwise(const Shape &s, const BwdLayout &L, const float *u, const void 
   const int cpl = hw_cpl(s);
   const int lanes_per_head = s.hd / cpl;
   int S = 0;
-  if (lanes_per_head == 1 || lanes_per_head == 2 || lanes_per_head == 4 || lanes_per_head == 8 ||
+  if (hw_quad(s))
+    S = -1;
+  else if (lanes_per_head == 1 || lanes_per_head == 2 || lanes_per_head == 4 || lanes_per_head == 8 ||
       lanes_per_head == 16)
     S = lanes_per_head;
   const dim3 grid((unsigned)L.n_slices, (unsigned)L.n_ranges), block(256);
@@ -529,15 +626,14 @@ int bwd_headwise(const Shape &s, const BwdLayout &L, const float *u, const void 
     case 4: HW(K_, 8, 4); break;       \
     case 8: HW(K_, 8, 8); break;       \
     case 16: HW(K_, 8, 16); break;     \
+    case -1: HW(K_, 8, -1); break;     \
     default: HW(K_, 8, 0); break;      \
   }
 #define HW_K(K_)                         \
   if (cpl == 8) {                        \
     HW_S8(K_)                            \
-  } else if (S == 1) {                   \
-    HW(K_, 4, 1);                        \
   } else {                               \
-    HW(K_, 4, 0);                        \
+    HW(K_, 4, 1); /* heads of 4 */       \
   }
   switch (s.k) {
     case 1: HW_K(1) break;
