@@ -18,9 +18,10 @@
 //
 // Block: 4 waves (one per SIMD) = RG row groups of 32 rows x KS parts of K,
 // over one slab of 32 NT columns (the grid walks row blocks x slabs, slabs
-// fastest, so the slabs of a row block share its rows of h in L2).  Per step
+// fastest, so the slabs of a row block share its rows of h in L2); 256-column
+// slabs take two such groups of 4 waves, each on half the columns.  Per step
 // of 64 k:
-//   * each wave multiplies its 32 rows by every 32-column tile of the staged
+//   * each wave multiplies its 32 rows by every 32-column tile (of its group) of the staged
 //     weight slice on v_mfma_f32_32x32x16_bf16, accumulators resident.  A
 //     fragments are four 16-byte loads per lane straight from h (the 128-byte
 //     run of each row), issued three steps ahead into a ring of three
@@ -43,18 +44,21 @@ namespace {
 
 constexpr int kKT = 64;  // k per step
 
-template <int NT, int RG, int KS>
+template <int NT, int RG, int KS, int CG>
 struct WideCfg {
-  static constexpr int BM = RG * 32;            // rows per block
-  static constexpr int NP = NT * 32;            // columns per slab (zeros past the weights)
-  static constexpr int LDW = NP + 32;           // LDS row stride (bf16)
-  static constexpr int SLICE = kKT * LDW;       // bf16 per staged slice
-  static constexpr int STAGE = KS * SLICE;      // bf16 per stage (KS slices)
-  static constexpr int CPR = NP / 8;            // 16-byte chunks per staged row
-  static constexpr int CH = KS * kKT * CPR;     // chunks per stage
-  static constexpr int CPT = (CH + 255) / 256;  // chunks per thread
+  static constexpr int NTH = 64 * RG * KS * CG;  // threads per block
+  static constexpr int NTW = NT / CG;            // column tiles per wave
+  static constexpr int BM = RG * 32;             // rows per block
+  static constexpr int NP = NT * 32;             // columns per slab (zeros past the weights)
+  static constexpr int LDW = NP + 32;            // LDS row stride (bf16)
+  static constexpr int SLICE = kKT * LDW;        // bf16 per staged slice
+  static constexpr int STAGE = KS * SLICE;       // bf16 per stage (KS slices)
+  static constexpr int CPR = NP / 8;             // 16-byte chunks per staged row
+  static constexpr int CH = KS * kKT * CPR;      // chunks per stage
+  static constexpr int CPT = (CH + NTH - 1) / NTH;  // chunks per thread
   static constexpr size_t LDS = (size_t)2 * STAGE * 2;
-  static_assert(RG * KS == 4, "4 waves");
+  static_assert(RG * KS == 4, "4 waves per column group");
+  static_assert(NT % CG == 0, "whole column tiles per wave");
   // the K parts' sums pass through the (then free) stages at the end
   static_assert(KS == 1 || LDS >= (size_t)(KS - 1) * RG * NT * 16 * 64 * 4, "reduction buffer");
 };
@@ -69,16 +73,17 @@ struct Cols {
   float *out;     // the generator values
 };
 
-template <int NT, int RG, int KS, bool FUSED>
-__global__ void __launch_bounds__(256, 1)
+template <int NT, int RG, int KS, int CG, bool FUSED>
+__global__ void __launch_bounds__(64 * RG * KS * CG, 1)
 k_gen_proj_wide(const bf16 *__restrict__ h, Cols cols, int64_t M, int K, int n_slabs) {
-  using C = WideCfg<NT, RG, KS>;
+  using C = WideCfg<NT, RG, KS, CG>;
+  constexpr int NTW = C::NTW;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
   bf16 *bs = reinterpret_cast<bf16 *>(lds_raw);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rg = wave % RG, ks = wave / RG;
+  const int rg = wave % RG, ks = (wave / RG) % KS, cg = wave / (RG * KS);
   const int slab = (int)(blockIdx.x % n_slabs);
   const int64_t row0 = (int64_t)(blockIdx.x / n_slabs) * C::BM;
   const int col0 = slab * C::NP;
@@ -94,11 +99,11 @@ k_gen_proj_wide(const bf16 *__restrict__ h, Cols cols, int64_t M, int K, int n_s
   auto load_b = [&](int st) {
 #pragma unroll
     for (int c = 0; c < C::CPT; ++c) {
-      const int e = tid + c * 256;
+      const int e = tid + c * C::NTH;
       const int sl = e / (kKT * C::CPR), e2 = e - sl * (kKT * C::CPR);
       const int r = e2 / C::CPR, gc = col0 + (e2 - r * C::CPR) * 8;
       const int k = (sl * SH + st) * kKT + r;
-      const bool live = (C::CH % 256 == 0 || e < C::CH) && k < K;
+      const bool live = (C::CH % C::NTH == 0 || e < C::CH) && k < K;
       // a chunk lies wholly in one source, or past both (zeros); the other
       // source's load falls outside its buffer and reads zeros, so no lane
       // chooses between resources
@@ -113,8 +118,8 @@ k_gen_proj_wide(const bf16 *__restrict__ h, Cols cols, int64_t M, int K, int n_s
   auto store_b = [&](int buf) {
 #pragma unroll
     for (int c = 0; c < C::CPT; ++c) {
-      const int e = tid + c * 256;
-      if (C::CH % 256 == 0 || e < C::CH) {
+      const int e = tid + c * C::NTH;
+      if (C::CH % C::NTH == 0 || e < C::CH) {
         const int sl = e / (kKT * C::CPR), e2 = e - sl * (kKT * C::CPR);
         const int r = e2 / C::CPR, cc = (e2 - r * C::CPR) * 8;
         *reinterpret_cast<uint4 *>(&bs[buf * C::STAGE + sl * C::SLICE + r * C::LDW + cc]) = breg[c];
@@ -135,10 +140,10 @@ k_gen_proj_wide(const bf16 *__restrict__ h, Cols cols, int64_t M, int K, int n_s
   // rows 8 (gi / 2) + 4 p + (lr / 4) (p = 0, 1), columns 32 n + 16 (gi % 2) +
   // 4 (lr % 4) .. +3; lane l then holds B[8 (l / 32) + i][32 n + l % 32]
   const int lr = lane & 15, gi = lane >> 4;
-  const int boff = (8 * (gi >> 1) + (lr >> 2)) * C::LDW + 16 * (gi & 1) + 4 * (lr & 3);
-  auto bfrags = [&](bf16x8(&b)[NT], int buf, int q) {
+  const int boff = (8 * (gi >> 1) + (lr >> 2)) * C::LDW + 16 * (gi & 1) + 4 * (lr & 3) + 32 * NTW * cg;
+  auto bfrags = [&](bf16x8(&b)[NTW], int buf, int q) {
 #pragma unroll
-    for (int n = 0; n < NT; ++n) {
+    for (int n = 0; n < NTW; ++n) {
       const unsigned char *p = reinterpret_cast<const unsigned char *>(
           &bs[buf * C::STAGE + ks * C::SLICE + 16 * q * C::LDW + 32 * n + boff]);
       const uint2 lo = read_tr16(p);
@@ -147,9 +152,9 @@ k_gen_proj_wide(const bf16 *__restrict__ h, Cols cols, int64_t M, int K, int n_s
     }
   };
 
-  f32x16 acc[NT];
+  f32x16 acc[NTW];
 #pragma unroll
-  for (int n = 0; n < NT; ++n)
+  for (int n = 0; n < NTW; ++n)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[n][i] = 0.f;
 
@@ -167,16 +172,16 @@ k_gen_proj_wide(const bf16 *__restrict__ h, Cols cols, int64_t M, int K, int n_s
   // B loads of st + 2 and the A loads of st + 3 (into the set just used),
   // meet at the barrier.
   auto step = [&](int st, bf16x8(&a)[4], int buf) {
-    bf16x8 bc[NT], bn[NT];
+    bf16x8 bc[NTW], bn[NTW];
     bfrags(bc, buf, 0);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       if (q < 3) bfrags(bn, buf, q + 1);
 #pragma unroll
-      for (int n = 0; n < NT; ++n) acc[n] = mfma32(a[q], bc[n], acc[n]);
+      for (int n = 0; n < NTW; ++n) acc[n] = mfma32(a[q], bc[n], acc[n]);
       if (q < 3) {
 #pragma unroll
-        for (int n = 0; n < NT; ++n) bc[n] = bn[n];
+        for (int n = 0; n < NTW; ++n) bc[n] = bn[n];
       }
     }
     // the other stage was last read in the previous step, before its barrier
@@ -202,6 +207,7 @@ k_gen_proj_wide(const bf16 *__restrict__ h, Cols cols, int64_t M, int K, int n_s
   if (st + 4 < SH) step(st + 4, a1, 0);
 
   if constexpr (KS > 1) {
+    static_assert(CG == 1, "K parts with one column group");
     // K parts 1 .. KS-1 hand their sums to part 0, added in part order
     float *red = reinterpret_cast<float *>(lds_raw);
     auto slot = [&](int part, int n, int i) { return ((((part - 1) * RG + rg) * NT + n) * 16 + i) * 64 + lane; };
@@ -224,8 +230,8 @@ k_gen_proj_wide(const bf16 *__restrict__ h, Cols cols, int64_t M, int K, int n_s
   // D: lane holds D[8 b + 4 (lane / 32) + r][lane % 32] in element 4 b + r
   const int split = FUSED ? cols.N0 : 0;
 #pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    const int col = col0 + 32 * n + (lane & 31);
+  for (int n = 0; n < NTW; ++n) {
+    const int col = col0 + 32 * (NTW * cg + n) + (lane & 31);
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
@@ -241,13 +247,13 @@ k_gen_proj_wide(const bf16 *__restrict__ h, Cols cols, int64_t M, int K, int n_s
   }
 }
 
-template <int NT, int RG, int KS, bool FUSED>
+template <int NT, int RG, int KS, int CG, bool FUSED>
 void launch(const bf16 *h, const Cols &cols, int64_t M, int K, hipStream_t st) {
-  using C = WideCfg<NT, RG, KS>;
+  using C = WideCfg<NT, RG, KS, CG>;
   const size_t lds = C::LDS;
   const int n_slabs = (int)ceil_div(cols.N0 + cols.N1, C::NP);
-  hipLaunchKernelGGL((k_gen_proj_wide<NT, RG, KS, FUSED>), dim3((unsigned)(ceil_div(M, C::BM) * n_slabs)),
-                     dim3(256), lds, st, h, cols, M, K, n_slabs);
+  hipLaunchKernelGGL((k_gen_proj_wide<NT, RG, KS, CG, FUSED>), dim3((unsigned)(ceil_div(M, C::BM) * n_slabs)),
+                     dim3(C::NTH), lds, st, h, cols, M, K, n_slabs);
 }
 
 // One block of 4 waves per CU: 128-row blocks when the blocks number at least
@@ -257,13 +263,17 @@ void launch(const bf16 *h, const Cols &cols, int64_t M, int K, hipStream_t st) {
 template <int NT, bool FUSED>
 void launch_nt(const bf16 *h, const Cols &cols, int64_t M, int K, hipStream_t st) {
   const int64_t slabs = ceil_div(cols.N0 + cols.N1, NT * 32);
+  // 256-column slabs: two column groups of 4 waves, two waves per SIMD (the
+  // second hides the first's A loads; 12 % faster for the fused form, 5 % for
+  // 256 generator columns, than one group)
+  constexpr int CG = NT == 8 ? 2 : 1;
   if constexpr (FUSED) {
-    launch<NT, 4, 1, true>(h, cols, M, K, st);
+    launch<NT, 4, 1, CG, true>(h, cols, M, K, st);
   } else {
     if (ceil_div(M, 128) * slabs >= 256)
-      launch<NT, 4, 1, false>(h, cols, M, K, st);
+      launch<NT, 4, 1, CG, false>(h, cols, M, K, st);
     else
-      launch<NT, 2, 2, false>(h, cols, M, K, st);
+      launch<NT, 2, 2, 1, false>(h, cols, M, K, st);
   }
 }
 
