@@ -83,7 +83,7 @@
 extern "C" {
 #endif
 
-#define DYNCONV_ABI_VERSION 2
+#define DYNCONV_ABI_VERSION 3
 
 #ifndef DYNCONV_API
 #define DYNCONV_API __attribute__((visibility("default")))
@@ -92,8 +92,15 @@ extern "C" {
 /* I/O dtype.  Accumulation is fp32 for both. */
 typedef enum { DYNCONV_FP32 = 0, DYNCONV_BF16 = 1 } dynconv_dtype;
 
-/* Filter-generator parameterisation. */
-typedef enum { DYNCONV_HEADWISE = 0, DYNCONV_LOWRANK = 1 } dynconv_kind;
+/* Filter-generator parameterisation.  DYNCONV_STATIC: no generator, the
+ * filter is the static bias alone, w[t,c,j] = w0[c,j]: the fixed depthwise
+ * short convolution the pages take as the baseline primitive (gist.science
+ * Technical Summary, Problem; the dynamic layer with a zero generator).  With
+ * it, h and d_model are not used (h may be NULL, d_model 0) except by
+ * dynconv_fwd_proj, n_heads, rank, W, A, U and the generator cache are
+ * ignored (the cache holds 0 bytes), w0 is required, and the backward writes
+ * dx and dw0 and fills dh, when given, with zeros (y does not depend on h). */
+typedef enum { DYNCONV_HEADWISE = 0, DYNCONV_LOWRANK = 1, DYNCONV_STATIC = 2 } dynconv_kind;
 
 enum {
   DYNCONV_OK = 0,
@@ -148,7 +155,8 @@ typedef struct {
   const void *W;  /* head-wise [d_model, n_heads*k]; unused otherwise */
   const void *A;  /* low-rank [d_model, rank]; unused otherwise       */
   const void *U;  /* low-rank [rank, D*k]; unused otherwise           */
-  const void *w0; /* static bias [D, k], or NULL for none             */
+  const void *w0; /* static bias [D, k], or NULL for none (required    */
+                  /* with DYNCONV_STATIC)                              */
 } dynconv_gen;
 
 /* Weight gradients, fp32 device pointers, overwritten (not accumulated).

@@ -25,7 +25,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdynconv.so")
 
 DYNCONV_FP32, DYNCONV_BF16 = 0, 1
-DYNCONV_HEADWISE, DYNCONV_LOWRANK = 0, 1
+DYNCONV_HEADWISE, DYNCONV_LOWRANK, DYNCONV_STATIC = 0, 1, 2
+ABI_VERSION = 3
 DYNCONV_WS_CACHED = 2  # or-ed into dynconv_workspace_bytes' pass when the call gets gen_cache
 
 
@@ -109,24 +110,31 @@ def _dtype_code(dt) -> int:
     raise TypeError(f"unsupported I/O dtype {dt}")
 
 
-def make_problem(x: torch.Tensor, h: torch.Tensor, k: int, cu_seqlens=None) -> Problem:
+def make_problem(x: torch.Tensor, h, k: int, cu_seqlens=None) -> Problem:
     """Problem struct from x[B,T,D], h[B,T,d_model] and the filter width k.
 
-    cu_seqlens: None, or packed documents (B must be 1): an int32 device
-    tensor of n_seqs + 1 offsets rising from 0 to T."""
-    if x.dim() != 3 or h.dim() != 3 or h.shape[:2] != x.shape[:2]:
-        raise ValueError(f"expected h[B,T,d] and x[B,T,D], got {tuple(h.shape)} and {tuple(x.shape)}")
+    h may be None for the static filter (d_model 0).  cu_seqlens: None, or
+    packed documents (B must be 1): an int32 device tensor of n_seqs + 1
+    offsets rising from 0 to T."""
+    if x.dim() != 3 or (h is not None and (h.dim() != 3 or h.shape[:2] != x.shape[:2])):
+        raise ValueError(f"expected h[B,T,d] and x[B,T,D], got {None if h is None else tuple(h.shape)} "
+                         f"and {tuple(x.shape)}")
     B, T, D = x.shape
+    d = 0 if h is None else h.shape[2]
     if cu_seqlens is None:
-        return Problem(B, T, h.shape[2], D, int(k), _dtype_code(x.dtype), None, 0)
+        return Problem(B, T, d, D, int(k), _dtype_code(x.dtype), None, 0)
     if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
         raise TypeError("cu_seqlens must be a contiguous 1-d int32 tensor")
-    return Problem(B, T, h.shape[2], D, int(k), _dtype_code(x.dtype), cu_seqlens.data_ptr(),
-                   cu_seqlens.numel() - 1)
+    return Problem(B, T, d, D, int(k), _dtype_code(x.dtype), cu_seqlens.data_ptr(), cu_seqlens.numel() - 1)
 
 
 def make_gen(W=None, A=None, U=None, w0=None, n_heads: int = 0) -> Gen:
-    """Generator struct: head-wise when W is given, else low-rank (A, U)."""
+    """Generator struct: head-wise when W is given, low-rank when A and U
+    are, the static filter (w0 alone) when none of them is."""
+    if W is None and A is None and U is None:
+        if w0 is None:
+            raise ValueError("the static filter needs w0")
+        return Gen(DYNCONV_STATIC, 0, 0, 0, None, None, None, _ptr(w0))
     if W is not None:
         if n_heads <= 0:
             raise ValueError("head-wise generator needs n_heads")
@@ -185,7 +193,7 @@ def dynconv_fwd(h, x, *, k, W=None, A=None, U=None, w0=None, n_heads=0, y=None, 
     gen = make_gen(W, A, U, w0, n_heads)
     if y is None:
         y = torch.empty_like(x)
-    if gen_cache is None and want_cache:
+    if gen_cache is None and want_cache and gen.kind != DYNCONV_STATIC:
         n = gen.n_heads * k if gen.kind == DYNCONV_HEADWISE else gen.rank
         gen_cache = torch.empty(x.shape[0] * x.shape[1], n, dtype=torch.float32, device=x.device)
     nbytes = dynconv_workspace_bytes(prob, gen, 0 | (DYNCONV_WS_CACHED if gen_cache is not None else 0))
@@ -209,7 +217,7 @@ def dynconv_fwd_proj(h, Wp, *, k, W=None, A=None, U=None, w0=None, n_heads=0, x=
     gen = make_gen(W, A, U, w0, n_heads)
     if y is None:
         y = torch.empty_like(x)
-    if gen_cache is None and want_cache:
+    if gen_cache is None and want_cache and gen.kind != DYNCONV_STATIC:
         n = gen.n_heads * k if gen.kind == DYNCONV_HEADWISE else gen.rank
         gen_cache = torch.empty(B * T, n, dtype=torch.float32, device=h.device)
     nbytes = dynconv_workspace_bytes(prob, gen, 0 | (DYNCONV_WS_CACHED if gen_cache is not None else 0))
@@ -245,11 +253,13 @@ def dynconv_bwd(h, x, dy, *, k, W=None, A=None, U=None, w0=None, n_heads=0, gen_
     f32 = dict(dtype=torch.float32, device=dev)
     o = dict(out or {})
     o.setdefault("dx", torch.empty_like(x))
-    if need_dh:
+    if need_dh and h is not None:
         o.setdefault("dh", torch.empty_like(h))
     if need_dw0:
         o.setdefault("dw0", torch.empty(prob.D, k, **f32))
-    if gen.kind == DYNCONV_HEADWISE:
+    if gen.kind == DYNCONV_STATIC:
+        pass
+    elif gen.kind == DYNCONV_HEADWISE:
         o.setdefault("dW", torch.empty(prob.d_model, gen.n_heads * k, **f32))
     else:
         o.setdefault("dA", torch.empty(prob.d_model, gen.rank, **f32))
@@ -268,7 +278,7 @@ def dynconv_decode(h, x, state, *, k, W=None, A=None, U=None, w0=None, n_heads=0
     """One decoding step: h [B, d_model], x [B, D], state [B, k-1, D] (updated
     in place; None when k == 1).  Returns y [B, D]."""
     B, D = x.shape
-    prob = Problem(B, 1, h.shape[-1], D, k, _dtype_code(x.dtype), None, 0)
+    prob = Problem(B, 1, 0 if h is None else h.shape[-1], D, k, _dtype_code(x.dtype), None, 0)
     gen = make_gen(W, A, U, w0, n_heads)
     if y is None:
         y = torch.empty_like(x)
@@ -281,8 +291,9 @@ def dynconv_decode(h, x, state, *, k, W=None, A=None, U=None, w0=None, n_heads=0
 class DynConvFn(torch.autograd.Function):
     """autograd wrapper: y = DynConvFn.apply(h, x, W, A, U, w0, k, n_heads[, cu_seqlens]).
 
-    Pass W (head-wise, with n_heads) or A and U (low-rank); unused weights
-    are None; cu_seqlens packs documents into one row.  The forward keeps the
+    Pass W (head-wise, with n_heads) or A and U (low-rank), or none of them
+    for the static filter (w0 alone; h may then be None); unused weights are
+    None; cu_seqlens packs documents into one row.  The forward keeps the
     fp32 generator cache for the backward.
     """
 

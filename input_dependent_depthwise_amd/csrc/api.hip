@@ -39,11 +39,15 @@ inline bool overlap(const Range &a, const Range &b) {
 int check_problem(const dynconv_problem *p, const dynconv_gen *g, Shape &s) {
   if (!p || !g) return DYNCONV_E_NULL;
   if (p->dtype != DYNCONV_FP32 && p->dtype != DYNCONV_BF16) return DYNCONV_E_DTYPE;
-  if (g->kind != DYNCONV_HEADWISE && g->kind != DYNCONV_LOWRANK) return DYNCONV_E_DTYPE;
+  if (g->kind != DYNCONV_HEADWISE && g->kind != DYNCONV_LOWRANK && g->kind != DYNCONV_STATIC)
+    return DYNCONV_E_DTYPE;
   if (p->k < 1 || p->k > 8) return DYNCONV_E_K;
-  if (p->B < 0 || p->T < 0 || p->d_model <= 0 || p->D <= 0) return DYNCONV_E_SHAPE;
+  const bool stat = g->kind == DYNCONV_STATIC;  // h is not read: d_model may be 0
+  if (p->B < 0 || p->T < 0 || p->D <= 0 || (stat ? p->d_model < 0 : p->d_model <= 0)) return DYNCONV_E_SHAPE;
   int N;
-  if (g->kind == DYNCONV_HEADWISE) {
+  if (stat) {
+    N = 0;
+  } else if (g->kind == DYNCONV_HEADWISE) {
     if (g->n_heads <= 0 || p->D % g->n_heads != 0) return DYNCONV_E_SHAPE;
     if ((int64_t)g->n_heads * p->k > 256) return DYNCONV_E_LIMIT;
     N = g->n_heads * p->k;
@@ -56,7 +60,8 @@ int check_problem(const dynconv_problem *p, const dynconv_gen *g, Shape &s) {
   const int64_t lim = (int64_t)1 << 31;
   if (p->B > lim || p->T > lim) return DYNCONV_E_LIMIT;
   const int64_t BT = p->B * p->T;
-  if (BT > 0 && (BT > lim / p->D || BT > lim / p->d_model || BT > lim / N)) return DYNCONV_E_LIMIT;
+  if (BT > 0 && (BT > lim / p->D || (p->d_model > 0 && BT > lim / p->d_model) || (N > 0 && BT > lim / N)))
+    return DYNCONV_E_LIMIT;
   if (p->D * p->k > lim / 256 || p->d_model * N > lim) return DYNCONV_E_LIMIT;
   if (p->cu_seqlens) {  // packed documents: one row, at least one document
     if (p->B != 1 || p->n_seqs < 1) return DYNCONV_E_SHAPE;
@@ -71,11 +76,12 @@ int check_problem(const dynconv_problem *p, const dynconv_gen *g, Shape &s) {
   s.d = p->d_model;
   s.D = p->D;
   s.k = p->k;
-  s.kind = g->kind;
-  s.n_heads = g->kind == DYNCONV_HEADWISE ? g->n_heads : 0;
+  s.stat = stat;
+  s.kind = stat ? DYNCONV_HEADWISE : g->kind;
+  s.n_heads = stat ? 1 : (g->kind == DYNCONV_HEADWISE ? g->n_heads : 0);
   s.rank = g->kind == DYNCONV_LOWRANK ? g->rank : 0;
   s.N = N;
-  s.hd = g->kind == DYNCONV_HEADWISE ? (int)(p->D / g->n_heads) : 0;
+  s.hd = stat ? (int)p->D : (g->kind == DYNCONV_HEADWISE ? (int)(p->D / g->n_heads) : 0);
   return DYNCONV_OK;
 }
 
@@ -90,6 +96,7 @@ struct Plan {
   size_t mp = 0;     // generator weight padded to Np columns (bf16)
   size_t dmp = 0;    // per-range dW / dA partials, fp32
   size_t seqpos = 0; // packed documents: per-token position table, uint16 [BT]
+  size_t zero = 0;   // static filter: k zero generator values, read in place of u
   size_t total = 0;
 };
 
@@ -98,14 +105,14 @@ struct Plan {
 // kernels, which address single elements.
 inline bool vec_rows(const Shape &s, int dtype) {
   const int64_t vec = dtype == DYNCONV_BF16 ? 8 : 4;
-  return s.D % vec == 0 && s.d % vec == 0;
+  return s.D % vec == 0 && (s.stat || s.d % vec == 0);
 }
-inline bool mfma_proj(const Shape &s, int dtype) { return dtype == DYNCONV_BF16 && s.d % 8 == 0; }
+inline bool mfma_proj(const Shape &s, int dtype) { return !s.stat && dtype == DYNCONV_BF16 && s.d % 8 == 0; }
 inline bool fast_lowrank(const Shape &s, int dtype) {
   return dtype == DYNCONV_BF16 && s.kind == DYNCONV_LOWRANK && vec_rows(s, dtype) && fwd_lowrank_supported(s);
 }
 inline bool fast_bwd(const Shape &s, int dtype) {
-  return dtype == DYNCONV_BF16 && vec_rows(s, dtype) && bwd_fused_supported(s) && gen_bwd_supported(s);
+  return dtype == DYNCONV_BF16 && vec_rows(s, dtype) && bwd_fused_supported(s) && (s.stat || gen_bwd_supported(s));
 }
 
 // pass: 0 forward, 1 backward; `cached`: the caller passes gen_cache, so no
@@ -122,6 +129,7 @@ Plan plan(const Shape &s, int dtype, int pass, bool cached) {
   // few groups past the last token)
   if (s.packed) pl.seqpos = take((size_t)s.BT * sizeof(uint16_t) + 128);
   if (!cached) pl.cache = take((size_t)s.BT * s.N * sizeof(float));
+  if (s.stat) pl.zero = take((size_t)s.k * sizeof(float));
   // the projection runs in the forward, and in the backward only to rebuild a missing cache
   if (mfma_proj(s, dtype) && (pass == 0 || !cached)) pl.mt = take(gen_proj_mfma_ws_bytes(s));
   if (pass == 1) {
@@ -130,9 +138,11 @@ Plan plan(const Shape &s, int dtype, int pass, bool cached) {
       pl.gpart = take((size_t)L.n_slices * s.BT * L.R * sizeof(float));
       if (s.kind == DYNCONV_LOWRANK) pl.dup = take((size_t)L.n_ranges * s.N * s.D * s.k * sizeof(float));
       pl.dw0p = take((size_t)L.n_ranges * s.D * s.k * sizeof(float));
-      pl.g = take(gen_bwd_g_bytes(s));
-      pl.mp = take(gen_bwd_mp_bytes(s));
-      pl.dmp = take(gen_bwd_part_bytes(s));
+      if (!s.stat) {
+        pl.g = take(gen_bwd_g_bytes(s));
+        pl.mp = take(gen_bwd_mp_bytes(s));
+        pl.dmp = take(gen_bwd_part_bytes(s));
+      }
     } else {
       pl.g = take((size_t)s.BT * s.N * sizeof(float));
     }
@@ -168,6 +178,10 @@ Sizes sizes(const Shape &s, int eb, const dynconv_problem *p) {
 }
 
 int check_weights(const Shape &s, const dynconv_gen *g) {
+  if (s.stat) {  // only the bias is read
+    if (!g->w0) return DYNCONV_E_NULL;
+    return aligned16(g->w0) ? DYNCONV_OK : DYNCONV_E_ALIGN;
+  }
   if (s.kind == DYNCONV_HEADWISE && !g->W) return DYNCONV_E_NULL;
   if (s.kind == DYNCONV_LOWRANK && (!g->A || !g->U)) return DYNCONV_E_NULL;
   const void *ws[] = {g->W, g->A, g->U, g->w0};
@@ -194,7 +208,7 @@ int fwd_validate(const dynconv_problem *p, const dynconv_gen *g, const void *h, 
   int rc = check_problem(p, g, s);
   if (rc) return rc;
   if (s.BT == 0) return DYNCONV_OK;
-  if (!h || !x || !y) return DYNCONV_E_NULL;
+  if ((!h && !s.stat) || !x || !y) return DYNCONV_E_NULL;
   if ((rc = check_weights(s, g))) return rc;
   const void *ptrs[] = {h, x, y, gen_cache, workspace};
   for (const void *q : ptrs)
@@ -226,6 +240,10 @@ int fwd_launch(const dynconv_problem *p, Shape s, int dtype, const dynconv_gen *
                void *y, void *gen_cache, void *workspace, const Plan &pl, hipStream_t stream,
                const void *Wp = nullptr) {
   float *cache = gen_cache ? (float *)gen_cache : (float *)((char *)workspace + pl.cache);
+  if (s.stat) {  // no generator: the kernels read k zeros (or nothing, N = 0) in place of u
+    cache = (float *)((char *)workspace + pl.zero);
+    zero_fill(cache, s.k, stream);
+  }
   if (s.packed) {
     uint16_t *sp = (uint16_t *)((char *)workspace + pl.seqpos);
     seqpos_fill(p->cu_seqlens, p->n_seqs, s.BT, sp, stream);
@@ -233,14 +251,16 @@ int fwd_launch(const dynconv_problem *p, Shape s, int dtype, const dynconv_gen *
   }
   int rc;
   if (Wp && dtype == DYNCONV_BF16 && proj_fused_ok(s)) {
-    rc = proj_fused(s, h, Wp, s.kind == DYNCONV_HEADWISE ? g->W : g->A, const_cast<void *>(x), cache, stream);
+    // (static filter: no generator columns; the weight is never read)
+    const void *M = s.stat ? nullptr : (s.kind == DYNCONV_HEADWISE ? g->W : g->A);
+    rc = proj_fused(s, h, Wp, M, const_cast<void *>(x), cache, stream);
   } else {
     if (Wp) {
       rc = dtype == DYNCONV_BF16 ? simple_proj<bf16>(s, h, Wp, const_cast<void *>(x), stream)
                                  : simple_proj<float>(s, h, Wp, const_cast<void *>(x), stream);
       if (rc) return rc;
     }
-    rc = gen_proj(s, dtype, g, h, cache, workspace, pl, stream);
+    rc = s.stat ? 0 : gen_proj(s, dtype, g, h, cache, workspace, pl, stream);
   }
   if (rc) return rc;
   if (s.kind == DYNCONV_HEADWISE && vec_rows(s, dtype)) {
@@ -369,7 +389,8 @@ int dynconv_fwd_proj(const dynconv_problem *p, const dynconv_gen *g, const void 
   Plan pl;
   int rc = fwd_validate(p, g, h, x, y, gen_cache, workspace, workspace_bytes, true, s, pl);
   if (rc || s.BT == 0) return rc;
-  if (!Wp) return DYNCONV_E_NULL;
+  if (!Wp || !h) return DYNCONV_E_NULL;
+  if (s.d <= 0) return DYNCONV_E_SHAPE;
   if (!aligned16(Wp)) return DYNCONV_E_ALIGN;
   // x is written here: it may overlap no input and no other output (the
   // checks above covered y, the cache and the workspace against x)
@@ -405,7 +426,7 @@ int dynconv_decode(const dynconv_problem *p, const dynconv_gen *g, const void *h
   if (rc) return rc;
   if (p->T != 1 || s.packed) return DYNCONV_E_SHAPE;
   if (s.B == 0) return DYNCONV_OK;
-  if (!h || !x || !y || (s.k > 1 && !state)) return DYNCONV_E_NULL;
+  if ((!h && !s.stat) || !x || !y || (s.k > 1 && !state)) return DYNCONV_E_NULL;
   if ((rc = check_weights(s, g))) return rc;
   if (s.B > 65535) return DYNCONV_E_LIMIT;  // grid rows of four sequences stay far below the limit
   const void *ptrs[] = {h, x, y, state};
@@ -434,8 +455,15 @@ int dynconv_bwd(const dynconv_problem *p, const dynconv_gen *g, const void *h, c
   int rc = check_problem(p, g, s);
   if (rc) return rc;
   if (!gg) return DYNCONV_E_NULL;
-  if (s.kind == DYNCONV_HEADWISE && !gg->dW) return DYNCONV_E_NULL;
+  if (!s.stat && s.kind == DYNCONV_HEADWISE && !gg->dW) return DYNCONV_E_NULL;
   if (s.kind == DYNCONV_LOWRANK && (!gg->dA || !gg->dU)) return DYNCONV_E_NULL;
+  // static filter: no generator, no cache; the generator gradients are not written
+  dynconv_gen_grad gs = *gg;
+  if (s.stat) {
+    gs.dW = gs.dA = gs.dU = nullptr;
+    gen_cache = nullptr;
+  }
+  gg = &gs;
   if ((rc = check_weights(s, g))) return rc;
   if (s.BT == 0) {
     // No tokens: the weight gradients are empty sums.  Written by a fill
@@ -450,11 +478,11 @@ int dynconv_bwd(const dynconv_problem *p, const dynconv_gen *g, const void *h, c
     zero_fill(gg->dw0, z0.dw0 / sizeof(float), stream);
     return launch_status();
   }
-  if (!h || !x || !dy || !dx) return DYNCONV_E_NULL;
+  if ((!h && !s.stat) || !x || !dy || !dx) return DYNCONV_E_NULL;
   const void *ptrs[] = {h, x, dy, gen_cache, dx, dh, workspace, gg->dW, gg->dA, gg->dU, gg->dw0};
   for (const void *q : ptrs)
     if (q && !aligned16(q)) return DYNCONV_E_ALIGN;
-  const Plan pl = plan(s, p->dtype, 1, gen_cache != nullptr);
+  const Plan pl = plan(s, p->dtype, 1, gen_cache != nullptr || s.stat);
   if (workspace_bytes < pl.total || (pl.total > 0 && !workspace)) return DYNCONV_E_WORKSPACE;
   const int eb = p->dtype == DYNCONV_BF16 ? 2 : 4;
   const Sizes z = sizes(s, eb, p);
@@ -477,7 +505,13 @@ int dynconv_bwd(const dynconv_problem *p, const dynconv_gen *g, const void *h, c
     s.seqpos = sp;
   }
   const float *cache = (const float *)gen_cache;
-  if (!cache) {
+  if (s.stat) {
+    float *c = (float *)((char *)workspace + pl.zero);
+    zero_fill(c, s.k, stream);
+    cache = c;
+    if (dh) zero_fill_bytes(dh, (size_t)s.BT * s.d * (p->dtype == DYNCONV_BF16 ? 2 : 4), stream);
+    dh = nullptr;
+  } else if (!cache) {
     float *c = (float *)((char *)workspace + pl.cache);
     if ((rc = gen_proj(s, p->dtype, g, h, c, workspace, pl, stream))) return rc;
     cache = c;
@@ -485,7 +519,7 @@ int dynconv_bwd(const dynconv_problem *p, const dynconv_gen *g, const void *h, c
   char *ws = (char *)workspace;
   if (fast_bwd(s, p->dtype)) {
     const BwdLayout L = bwd_layout(s);
-    const GenBwdLayout G = gen_bwd_layout(s);
+    const GenBwdLayout G = s.stat ? GenBwdLayout{} : gen_bwd_layout(s);
     float *gpart = (float *)(ws + pl.gpart), *dUp = (float *)(ws + pl.dup), *dw0p = (float *)(ws + pl.dw0p);
     rc = s.kind == DYNCONV_HEADWISE
              ? bwd_headwise(s, L, cache, g->w0, x, dy, dx, gpart, dw0p, stream)
@@ -493,11 +527,11 @@ int dynconv_bwd(const dynconv_problem *p, const dynconv_gen *g, const void *h, c
     if (rc) return rc;
     const void *M = s.kind == DYNCONV_HEADWISE ? g->W : g->A;
     float *dMp = (float *)(ws + pl.dmp);
-    if ((rc = gen_bwd(s, gpart, L.n_slices, L.R, L.Dt, h, M, (bf16 *)(ws + pl.g), (bf16 *)(ws + pl.mp), dh,
-                      dMp, stream)))
+    if (!s.stat && (rc = gen_bwd(s, gpart, L.n_slices, L.R, L.Dt, h, M, (bf16 *)(ws + pl.g),
+                                 (bf16 *)(ws + pl.mp), dh, dMp, stream)))
       return rc;
     const int64_t Dk = s.D * s.k, dN = s.d * s.N;
-    float *dM = s.kind == DYNCONV_HEADWISE ? gg->dW : gg->dA;
+    float *dM = s.stat ? nullptr : (s.kind == DYNCONV_HEADWISE ? gg->dW : gg->dA);
     if ((rc = finalize(dUp, s.kind == DYNCONV_LOWRANK ? gg->dU : nullptr, (int64_t)s.N * Dk, L.n_ranges,
                        dw0p, gg->dw0, Dk, L.n_ranges, dMp, dM, dN, G.n_ranges, stream)))
       return rc;

@@ -74,6 +74,9 @@ struct Shape {
   // 255 (more than any tap reaches); NULL when every row is one sequence
   const uint16_t *seqpos;
   bool packed;  // the problem has packed documents (seqpos is set before any conv kernel)
+  // static filter only (no generator): head-wise in form, one head of D
+  // channels, N = 0 generator values (the kernels read zeros for u)
+  bool stat;
 };
 
 // Position of token row r in its sequence, and the tokens after it there

@@ -167,12 +167,14 @@ __device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
 
 // S: lanes per head when heads are 1..16 lanes wide and aligned to spans; 0:
 // any head width that is a multiple of CPL (prefix sums); -1 (CPL = 8): head
-// widths of 4 mod 8, at least 12 (prefix sums over channel quads).  VAR:
-// packed documents (positions from the per-token table).
+// widths of 4 mod 8, at least 12 (prefix sums over channel quads); -2: static
+// filter, no generator (no du at all).  VAR: packed documents (positions from
+// the per-token table).
 template <int K, int CPL, int S, bool VAR>
 __global__ void __launch_bounds__(256, 2)
 k_bwd_hw(Params P) {
-  constexpr bool QUAD = S < 0;
+  constexpr bool QUAD = S == -1;
+  constexpr bool NODU = S == -2;
   static_assert(!QUAD || CPL == 8, "quad heads: 8 channels per lane");
   constexpr int NP = CPL / 2;        // bf16 pairs per lane
   constexpr int SPAN = 64 * CPL;
@@ -367,12 +369,14 @@ k_bwd_hw(Params P) {
           for (int j = 0; j < K; ++j) {
             if (j == 0 || pos >= j) {
               const int xs = (i - j) & (XS - 1);
+              if constexpr (!NODU) {
 #pragma unroll
-              for (int p = 0; p < NP; ++p) {
-                if (QUAD && p >= 2)
-                  valsb[j] = dot2(xr[xs][p], dw[p], valsb[j]);
-                else
-                  vals[j] = dot2(xr[xs][p], dw[p], vals[j]);
+                for (int p = 0; p < NP; ++p) {
+                  if (QUAD && p >= 2)
+                    valsb[j] = dot2(xr[xs][p], dw[p], valsb[j]);
+                  else
+                    vals[j] = dot2(xr[xs][p], dw[p], vals[j]);
+                }
               }
               if (main) {
 #pragma unroll
@@ -428,7 +432,8 @@ k_bwd_hw(Params P) {
 #pragma unroll
         for (int p = 0; p < NH; ++p) asm volatile("" ::"v"(held[p]));
         // du of this token: sum over the lanes of each head
-        if constexpr (S > 0) {
+        if constexpr (NODU) {
+        } else if constexpr (S > 0) {
           if (t < t_b) {
             group_reduce4<S>(vals, lane);
             const int p = lane % S;
@@ -572,8 +577,8 @@ BwdLayout bwd_headwise_layout(const Shape &s) {
     const int n = (int)(c1 / s.hd - c0 / s.hd + 1);
     if (n > sl) sl = n;
   }
-  L.SL = sl;
-  L.R = sl * s.k;
+  L.SL = s.stat ? 0 : sl;  // static filter: no du partials
+  L.R = L.SL * s.k;
   return L;
 }
 
@@ -604,7 +609,9 @@ int bwd_headwise(const Shape &s, const BwdLayout &L, const float *u, const void 
   const int cpl = hw_cpl(s);
   const int lanes_per_head = s.hd / cpl;
   int S = 0;
-  if (hw_quad(s))
+  if (s.stat)
+    S = -2;
+  else if (hw_quad(s))
     S = -1;
   else if (lanes_per_head == 1 || lanes_per_head == 2 || lanes_per_head == 4 || lanes_per_head == 8 ||
       lanes_per_head == 16)
@@ -627,6 +634,7 @@ int bwd_headwise(const Shape &s, const BwdLayout &L, const float *u, const void 
     case 8: HW(K_, 8, 8); break;       \
     case 16: HW(K_, 8, 16); break;     \
     case -1: HW(K_, 8, -1); break;     \
+    case -2: HW(K_, 8, -2); break;     \
     default: HW(K_, 8, 0); break;      \
   }
 #define HW_K(K_)                         \

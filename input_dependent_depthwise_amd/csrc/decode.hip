@@ -48,7 +48,7 @@ k_decode_one(Shape s, const T *__restrict__ h, const T *__restrict__ W, const T 
   if (!lowrank) {
     e0 = c0 / s.hd;
     const int e1 = (min(c0 + kThreads, D) - 1) / s.hd;
-    nv = (e1 - e0 + 1) * K;
+    nv = s.stat ? 0 : (e1 - e0 + 1) * K;  // static filter: no generator values
   }
   const T *M = lowrank ? A : W;
   const int ldm = s.N;
@@ -84,7 +84,7 @@ k_decode_one(Shape s, const T *__restrict__ h, const T *__restrict__ W, const T 
       v = 0.f;
       for (int q = 0; q < s.rank; ++q) v = fmaf(gv[q], to_f32(U[(int64_t)q * D * K + (int64_t)c * K + j]), v);
     } else {
-      v = gv[(c / s.hd - e0) * K + j];
+      v = s.stat ? 0.f : gv[(c / s.hd - e0) * K + j];
     }
     w[j] = w0 ? v + to_f32(w0[(int64_t)c * K + j]) : v;
   }
@@ -129,7 +129,7 @@ k_decode(Shape s, const T *__restrict__ h, const T *__restrict__ W, const T *__r
   if (!lowrank) {
     e0 = c0 / s.hd;
     const int e1 = (min(c0 + kThreads, D) - 1) / s.hd;
-    nv = (e1 - e0 + 1) * K;
+    nv = s.stat ? 0 : (e1 - e0 + 1) * K;  // static filter: no generator values
   }
   const T *M = lowrank ? A : W;
   const int ldm = s.N;                    // row length of A (rank) or W (n_heads*k)
@@ -187,7 +187,7 @@ k_decode(Shape s, const T *__restrict__ h, const T *__restrict__ W, const T *__r
       }
     } else {
 #pragma unroll
-      for (int r = 0; r < kBG; ++r) w[r][j] = gv[r][(c / s.hd - e0) * K + j];
+      for (int r = 0; r < kBG; ++r) w[r][j] = s.stat ? 0.f : gv[r][(c / s.hd - e0) * K + j];
     }
     if (w0) {
       const float bias = to_f32(w0[(int64_t)c * K + j]);

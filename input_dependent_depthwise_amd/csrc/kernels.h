@@ -12,6 +12,8 @@ void trace_end(bool armed, hipStream_t st);
 
 // Writes n zeros at p (no-op when p is NULL or n is 0).
 void zero_fill(float *p, int64_t n, hipStream_t st);
+// Writes nbytes (a multiple of 2) of zeros at p.
+void zero_fill_bytes(void *p, size_t nbytes, hipStream_t st);
 
 // Packed documents: the per-token position table of Shape::seqpos from the
 // document offsets cu[0 .. n_seqs] (simple_kernels.hip).

@@ -271,6 +271,11 @@ __global__ void __launch_bounds__(256) k_zero(float *__restrict__ p, int64_t n) 
   if (i < n) p[i] = 0.f;
 }
 
+__global__ void __launch_bounds__(256) k_zero16(uint16_t *__restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
@@ -278,6 +283,11 @@ static inline dim3 grid1(int64_t n) { return dim3((unsigned)ceil_div(n, 256)); }
 
 void zero_fill(float *p, int64_t n, hipStream_t st) {
   if (p && n > 0) hipLaunchKernelGGL(k_zero, grid1(n), dim3(256), 0, st, p, n);
+}
+
+void zero_fill_bytes(void *p, size_t nbytes, hipStream_t st) {
+  const int64_t n = (int64_t)(nbytes / 2);
+  if (p && n > 0) hipLaunchKernelGGL(k_zero16, grid1(n), dim3(256), 0, st, (uint16_t *)p, n);
 }
 
 template <typename T>
@@ -317,6 +327,7 @@ int simple_bwd(const Shape &s, const float *gen, const void *W, const void *A, c
   if (gg.dw0)
     hipLaunchKernelGGL(k_dw0_simple<T>, grid1(s.D * s.k), dim3(256), 0, st, s, (const T *)x,
                        (const T *)dy, gg.dw0);
+  if (s.stat) return 0;  // no generator (the caller has cleared dh)
   if (s.kind == DYNCONV_HEADWISE) {
     hipLaunchKernelGGL(k_du_simple<T>, grid1(s.BT * s.N), dim3(256), 0, st, s, (const T *)x,
                        (const T *)dy, g);

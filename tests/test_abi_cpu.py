@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert dc.dynconv_abi_version() == 2
+    assert dc.dynconv_abi_version() == dc.ABI_VERSION == 3
     for code in (OK, E_NULL, E_SHAPE, E_K, E_DTYPE, E_ALIGN, E_ALIAS, E_WORKSPACE, E_HIP, E_LIMIT, E_SCRATCH):
         s = dc.dynconv_status_str(code)
         assert s and s != "unknown status"
@@ -406,3 +406,52 @@ def test_packed_workspace_holds_the_position_table(L):
 
 def test_decode_refuses_packing(L):
     assert dec(L, packed(T=1), gen_hw()) == E_SHAPE
+
+
+def gen_static(w0=True):
+    return Gen(dc.DYNCONV_STATIC, 0, 0, 0, None, None, None, addr(13) if w0 else None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("fwd_no_w0", E_NULL), ("fwd_empty", OK), ("fwd_h_null_ws_small", E_WORKSPACE), ("fwd_d_neg", E_SHAPE),
+    ("fwd_w0_align", E_ALIGN), ("bwd_no_gen_grads_ws_small", E_WORKSPACE), ("bwd_no_w0", E_NULL),
+    ("dec_empty", OK), ("dec_no_state", E_NULL), ("proj_h_null", E_NULL), ("kind3", E_DTYPE),
+])
+def test_static_validation(L, case, expect):
+    """The static filter (no generator): h and the generator weights are not
+    needed (d_model may be 0), w0 is; the cache holds 0 bytes."""
+    p, g = prob(d=0), gen_static()
+    if case == "fwd_no_w0":
+        rc = fwd(L, p, gen_static(w0=False), h=None)
+    elif case == "fwd_empty":
+        rc = fwd(L, prob(B=0, d=0), g, h=None)
+    elif case == "fwd_h_null_ws_small":
+        rc = fwd(L, p, g, h=None, ws_bytes=16)
+    elif case == "fwd_d_neg":
+        rc = fwd(L, prob(d=-1), g, h=None)
+    elif case == "fwd_w0_align":
+        g.w0 = addr(13) + 8
+        rc = fwd(L, p, g, h=None)
+    elif case == "bwd_no_gen_grads_ws_small":
+        rc = bwd(L, p, g, h=None, dh=None, gg=GenGrad(None, None, None, addr(9)), ws_bytes=16)
+    elif case == "bwd_no_w0":
+        rc = bwd(L, p, gen_static(w0=False), h=None, dh=None, gg=GenGrad(None, None, None, addr(9)))
+    elif case == "dec_empty":
+        rc = L.dynconv_decode(ctypes.byref(prob(B=0, T=1, d=0)), ctypes.byref(g), None, addr(2), addr(4),
+                              addr(3), None)
+    elif case == "dec_no_state":
+        rc = L.dynconv_decode(ctypes.byref(prob(B=2, T=1, d=0)), ctypes.byref(g), None, addr(2), None,
+                              addr(3), None)
+    elif case == "proj_h_null":
+        rc = fwd_pj(L, prob(d=64), g, h=None)
+    else:
+        g.kind = 3
+        rc = fwd(L, p, g)
+    assert rc == expect
+
+
+def test_static_sizes(L):
+    p, g = prob(d=0), gen_static()
+    assert dc.dynconv_gen_cache_bytes(p, g) == 0
+    assert dc.dynconv_workspace_bytes(p, g, 0) >= 4 * p.k  # the k zero generator values
+    assert dc.dynconv_workspace_bytes(p, g, 1) > 0

@@ -138,3 +138,16 @@ def generate_proj_weight(w: Workload) -> torch.Tensor:
     ``w`` keep their values."""
     g = torch.Generator().manual_seed(w.seed + 1000)
     return (torch.randn(w.d, w.D, generator=g, dtype=torch.float32) * w.d ** -0.5).to(w.torch_dtype)
+
+
+def moe_routing(n_seqs: int, T: int, n_experts: int, seed: int) -> list:
+    """Top-1 routing counts for an MoE layer: counts[b][e] tokens of sequence
+    b go to expert e, drawn with probabilities proportional to 1/(e+1) (a
+    skewed load, so some experts get few or no tokens of a sequence)."""
+    g = torch.Generator().manual_seed(seed)
+    p = torch.tensor([1.0 / (e + 1) ** 2 for e in range(n_experts)])
+    counts = []
+    for _ in range(n_seqs):
+        pick = torch.multinomial(p, T, replacement=True, generator=g)
+        counts.append([int((pick == e).sum()) for e in range(n_experts)])
+    return counts
