@@ -137,9 +137,15 @@ __device__ __forceinline__ void bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
   }
 }
 
-template <int K>
-__device__ __forceinline__ void bload_u(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, float (&u)[4]) {
-  if constexpr (K == 4) {
+template <int K, int KU>
+__device__ __forceinline__ void bload_u(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, float (&u)[KU]) {
+  if constexpr (K > 4) {  // taps 0..3, then the rest
+    float lo[4], hi[4];
+    bload_u<4, 4>(r, voff, soff, lo);
+    bload_u<K - 4, 4>(r, voff + 16u, soff, hi);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) u[j] = lo[j], u[4 + j] = hi[j];
+  } else if constexpr (K == 4) {
     const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
     u[0] = __uint_as_float(v[0]), u[1] = __uint_as_float(v[1]), u[2] = __uint_as_float(v[2]),
     u[3] = __uint_as_float(v[3]);
@@ -176,15 +182,19 @@ k_bwd_hw(Params P) {
   constexpr bool QUAD = S == -1;
   constexpr bool NODU = S == -2;
   static_assert(!QUAD || CPL == 8, "quad heads: 8 channels per lane");
+  static_assert(K <= 4 || (CPL == 4 && S <= 0 && S != -1), "5..8 taps: 4 channels per lane, prefix sums");
   constexpr int NP = CPL / 2;        // bf16 pairs per lane
   constexpr int SPAN = 64 * CPL;
   // Tokens loaded ahead.  Eight (with rings twice as deep) measured no
   // faster: the compiler's wait counts across the per-token branches then
   // stop short of the deeper rings.
   constexpr int PD = 4;
-  constexpr int XS = 2 * PD;         // x ring slots: the k-tap history plus the loads in flight
-  constexpr int YS = PD;             // dy and u ring slots
-  constexpr int BLK = 2 * PD;        // tokens per unrolled block
+  constexpr int KU = K <= 4 ? 4 : 8;             // tap slots (u, bias, du sums)
+  constexpr int AR = KU;                         // dx accumulators: tokens still open (slot = (s - t_a) mod AR)
+  constexpr int XS = K <= 4 ? 2 * PD : 4 * PD;   // x ring slots: the k-1 history plus the loads in flight
+  constexpr int YS = PD;                         // dy and u ring slots
+  constexpr int BLK = XS;                        // tokens per unrolled block
+  static_assert(XS >= K + PD, "x ring");
   const Shape &s = P.s;
 
   __shared__ __attribute__((aligned(16))) float dwred[4][64 * CPL * K];
@@ -206,7 +216,7 @@ k_bwd_hw(Params P) {
 
   // per-lane bias: CPL*K contiguous bf16 at w0[cc*K], read as dwords with
   // unconditional buffer loads (no bias: an empty buffer, every load reads 0)
-  float w0r[CPL][4];
+  float w0r[CPL][KU];
   {
     const auto rw = rsrc(P.w0, P.w0 ? (uint32_t)(Dc * K * 2) : 0u);
     constexpr int NW = CPL * K / 2;
@@ -216,7 +226,7 @@ k_bwd_hw(Params P) {
 #pragma unroll
     for (int i = 0; i < CPL; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < KU; ++j) {
         const int el = i * K + j;
         w0r[i][j] = j < K ? __uint_as_float((el & 1) ? (wv[el >> 1] & 0xffff0000u) : (wv[el >> 1] << 16)) : 0.f;
       }
@@ -279,10 +289,10 @@ k_bwd_hw(Params P) {
     // t-3 .. t+PD (the k-tap history plus the loads in flight), dy and u in YS
     // (slot = (t - t_a) mod YS) holding tokens t .. t+PD
     uint32_t xr[XS][NP], dyr[YS][NP];
-    float ur[YS][4], ur2[YS][4];  // u of the lane's head (quad heads: of each quad's head)
-    float acc[4][CPL];  // dx accumulators (slot = (s - t_a) mod 4)
+    float ur[YS][KU], ur2[YS][KU];  // u of the lane's head (quad heads: of each quad's head)
+    float acc[AR][CPL];             // dx accumulators
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < AR; ++a)
 #pragma unroll
       for (int i = 0; i < CPL; ++i) acc[a][i] = 0.f;
 
@@ -302,7 +312,7 @@ k_bwd_hw(Params P) {
     // x history before t_a (the taps that reach before the sequence start are
     // skipped by the position tests, not zeroed)
 #pragma unroll
-    for (int j = 3; j >= 1; --j) {
+    for (int j = KU - 1; j >= 1; --j) {
       if (j < K) bload<CPL>(rx, voff_x, row(t_a - j) * row_x, xr[XS - j]);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -311,8 +321,8 @@ k_bwd_hw(Params P) {
       const uint32_t r = row(t);
       bload<CPL>(rx, voff_x, r * row_x, xr[xs]);
       bload<CPL>(rdy, voff_x, r * row_x, dyr[xs & (YS - 1)]);
-      bload_u<K>(ru, voff_u, r * row_u, ur[xs & (YS - 1)]);
-      if constexpr (QUAD) bload_u<K>(ru, voff_u2, r * row_u, ur2[xs & (YS - 1)]);
+      bload_u<K, KU>(ru, voff_u, r * row_u, ur[xs & (YS - 1)]);
+      if constexpr (QUAD) bload_u<K, KU>(ru, voff_u2, r * row_u, ur2[xs & (YS - 1)]);
     };
     // (issued in the loop's own order, so that the wait counts the compiler
     // derives at the loop head hold for the first pass too)
@@ -325,7 +335,7 @@ k_bwd_hw(Params P) {
     // Registers of the last stores stay reserved until the next token's loads
     // are issued: on this target a register read by a pending store can only be
     // rewritten after a vmcnt wait, which would also drain the loads in flight.
-    constexpr int NH = NP + (QUAD ? 8 : 4);
+    constexpr int NH = NP + (QUAD ? 8 : KU);
     uint32_t held[NH];  // dx of this token, du of the previous one
 #pragma unroll
     for (int p = 0; p < NH; ++p) held[p] = 0u;
@@ -343,8 +353,9 @@ k_bwd_hw(Params P) {
 #pragma unroll
       for (int i = 0; i < BLK; ++i) {
         const int t = tg + i;
-        float vals[4] = {0.f, 0.f, 0.f, 0.f};
-        float valsb[4] = {0.f, 0.f, 0.f, 0.f};  // quad heads: the second quad's sums
+        float vals[KU], valsb[KU];  // (quad heads: valsb = the second quad's sums)
+#pragma unroll
+        for (int j = 0; j < KU; ++j) vals[j] = 0.f, valsb[j] = 0.f;
         // a token past the batch end starts a new "sequence" (its loads were clamped)
         if constexpr (VAR) pos = t < BT ? (int)((pc[i >> 2] >> (16 * (i & 3))) & 255u) : 0;
         if (t < t_end) {
@@ -391,7 +402,7 @@ k_bwd_hw(Params P) {
 #pragma unroll
             for (int c = 0; c < CPL; ++c) {
               const float u0 = (QUAD && c >= 4) ? ur2[i & (YS - 1)][0] : ur[i & (YS - 1)][0];
-              acc[i & 3][c] = fmaf(u0 + w0r[c][0], dyf[c], dyf[c]);
+              acc[i & (AR - 1)][c] = fmaf(u0 + w0r[c][0], dyf[c], dyf[c]);
             }
           }
 #pragma unroll
@@ -400,14 +411,14 @@ k_bwd_hw(Params P) {
 #pragma unroll
               for (int c = 0; c < CPL; ++c) {
                 const float uj = (QUAD && c >= 4) ? ur2[i & (YS - 1)][j] : ur[i & (YS - 1)][j];
-                acc[(i - j) & 3][c] = fmaf(uj + w0r[c][j], dyf[c], acc[(i - j) & 3][c]);
+                acc[(i - j) & (AR - 1)][c] = fmaf(uj + w0r[c][j], dyf[c], acc[(i - j) & (AR - 1)][c]);
               }
             }
           }
           // token t-k+1 has all its terms
           const int so = t - (K - 1);
           if (so >= t_a && so < t_b) {
-            const float *a = acc[(i - (K - 1)) & 3];
+            const float *a = acc[(i - (K - 1)) & (AR - 1)];
             uint32_t o[NP];
 #pragma unroll
             for (int p = 0; p < NP; ++p) {
@@ -493,9 +504,13 @@ k_bwd_hw(Params P) {
         } else {
           // any head width: head sums as differences of the wave's prefix sums
           if (t < t_b) {
-            float hs[4];
+            float hs[KU];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < KU; ++j) {
+              if (j >= K) {
+                hs[j] = 0.f;
+                continue;
+              }
               const float pre = wave_prefix(vals[j]);
               const float before = __builtin_bit_cast(
                   float, __builtin_amdgcn_ds_bpermute(4 * (hla > 0 ? hla - 1 : 0), __builtin_bit_cast(int, pre)));
@@ -512,7 +527,7 @@ k_bwd_hw(Params P) {
               for (int j = 0; j < K; ++j) buf_store_f32(rg, hlast ? og + (uint32_t)j * 4u : kOutside, hs[j]);
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) held[NP + j] = __float_as_uint(hs[j]);
+            for (int j = 0; j < K; ++j) held[NP + j] = __float_as_uint(hs[j]);
           }
         }
         // keep each token's work in its own scheduling region: interleaving
@@ -545,10 +560,14 @@ k_bwd_hw(Params P) {
 // host side
 // ---------------------------------------------------------------------------
 // channels per lane: 8 when heads are a multiple of 8 wide, or 4 mod 8 and
-// at least 12 (quad heads); 4 for heads of 4 channels
-static bool hw_quad(const Shape &s) { return s.hd % 8 == 4 && s.hd >= 12; }
+// at least 12 (quad heads); 4 for heads of 4 channels, and for 5..8 taps
+// (whose rings take twice the registers) with any head width that is a
+// multiple of 4
+static bool hw_quad(const Shape &s) { return s.k <= 4 && s.hd % 8 == 4 && s.hd >= 12; }
 static int hw_cpl(const Shape &s) {
-  return (s.hd % 8 == 0 || hw_quad(s)) ? 8 : (s.hd % 4 == 0 ? 4 : 0); }
+  if (s.k > 4) return s.hd % 4 == 0 ? 4 : 0;
+  return (s.hd % 8 == 0 || hw_quad(s)) ? 8 : (s.hd % 4 == 0 ? 4 : 0);
+}
 
 BwdLayout bwd_headwise_layout(const Shape &s) {
   BwdLayout L = {};
@@ -559,9 +578,9 @@ BwdLayout bwd_headwise_layout(const Shape &s) {
   // Blocks (4 waves, one per SIMD) resident per CU, from each variant's
   // register count (512 per SIMD lane): the grid is sized to one round of
   // them over the 256 CUs, never more, so no block waits for a second round.
-  static const int kBlocksPerCU[3][4] = {{8, 6, 5, 4},   // 4 channels per lane, k = 1..4
-                                         {6, 3, 3, 2},   // 8 channels per lane
-                                         {5, 3, 2, 2}};  // quad heads
+  static const int kBlocksPerCU[3][8] = {{8, 6, 5, 4, 3, 2, 2, 2},  // 4 channels per lane, k = 1..8
+                                         {6, 3, 3, 2, 0, 0, 0, 0},      // 8 channels per lane
+                                         {5, 3, 2, 2, 0, 0, 0, 0}};     // quad heads
   const int64_t slots = 256 * kBlocksPerCU[hw_quad(s) ? 2 : (cpl == 8)][s.k - 1];
   const int64_t ranges = slots / L.n_slices > 1 ? slots / L.n_slices : 1;
   int64_t l = ceil_div(s.BT, 4 * ranges);  // tokens per wave
@@ -583,7 +602,7 @@ BwdLayout bwd_headwise_layout(const Shape &s) {
 }
 
 bool bwd_headwise_supported(const Shape &s) {
-  if (s.kind != DYNCONV_HEADWISE || s.k > 4 || hw_cpl(s) == 0) return false;
+  if (s.kind != DYNCONV_HEADWISE || s.k > 8 || hw_cpl(s) == 0) return false;
   // 32-bit byte offsets into x, dy, dx, u and the du partials, each tensor
   // below 2 GiB like those of the other tuned kernels
   const int64_t lim = ((int64_t)1 << 31) - 64;
@@ -611,6 +630,8 @@ int bwd_headwise(const Shape &s, const BwdLayout &L, const float *u, const void 
   int S = 0;
   if (s.stat)
     S = -2;
+  else if (s.k > 4)
+    S = 0;  // prefix sums for any head width
   else if (hw_quad(s))
     S = -1;
   else if (lanes_per_head == 1 || lanes_per_head == 2 || lanes_per_head == 4 || lanes_per_head == 8 ||
@@ -643,13 +664,24 @@ int bwd_headwise(const Shape &s, const BwdLayout &L, const float *u, const void 
   } else {                               \
     HW(K_, 4, 1); /* heads of 4 */       \
   }
+#define HW_K8(K_)          \
+  if (S == -2) {           \
+    HW(K_, 4, -2);         \
+  } else {                 \
+    HW(K_, 4, 0);          \
+  }
   switch (s.k) {
     case 1: HW_K(1) break;
     case 2: HW_K(2) break;
     case 3: HW_K(3) break;
     case 4: HW_K(4) break;
+    case 5: HW_K8(5) break;
+    case 6: HW_K8(6) break;
+    case 7: HW_K8(7) break;
+    case 8: HW_K8(8) break;
     default: rc = DYNCONV_E_LIMIT;
   }
+#undef HW_K8
 #undef HW_K
 #undef HW_S8
 #undef HW

@@ -38,6 +38,7 @@ __global__ void __launch_bounds__(256)
 k_fwd_hw_ring(Shape s, const float *__restrict__ u, const bf16 *__restrict__ w0, const bf16 *__restrict__ x,
               bf16 *__restrict__ y, int n_vg, int n_runs, int tpw) {
   constexpr int PD = 4;
+  constexpr int HS = K <= 4 ? 4 : 8;  // x history slots (and tokens per unrolled block)
   const int lane = threadIdx.x & 63;
   // wave-uniform (scalar) run bounds and sequence position
   const int gw = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -86,7 +87,24 @@ k_fwd_hw_ring(Shape s, const float *__restrict__ u, const bf16 *__restrict__ w0,
   float ua[PD][K], ub[PD][K];
   auto load_tok = [&](int slot, int t) {
     xr[slot] = buf_load16(rx, xoff(t));
-    if constexpr (K == 4) {
+    if constexpr (K > 4) {  // taps 0..3 (and 4..7 for 8 taps) as 16-byte loads, the rest one by one
+#pragma unroll
+      for (int q = 0; q < K / 4; ++q) {
+        const uint4 a = buf_load16(ru, uoff(t, ea, 4 * q));
+        ua[slot][4 * q] = __uint_as_float(a.x), ua[slot][4 * q + 1] = __uint_as_float(a.y);
+        ua[slot][4 * q + 2] = __uint_as_float(a.z), ua[slot][4 * q + 3] = __uint_as_float(a.w);
+        if constexpr (S2) {
+          const uint4 c = buf_load16(ru, uoff(t, eb, 4 * q));
+          ub[slot][4 * q] = __uint_as_float(c.x), ub[slot][4 * q + 1] = __uint_as_float(c.y);
+          ub[slot][4 * q + 2] = __uint_as_float(c.z), ub[slot][4 * q + 3] = __uint_as_float(c.w);
+        }
+      }
+#pragma unroll
+      for (int j = K / 4 * 4; j < K; ++j) {
+        ua[slot][j] = buf_load_f32(ru, uoff(t, ea, j));
+        if constexpr (S2) ub[slot][j] = buf_load_f32(ru, uoff(t, eb, j));
+      }
+    } else if constexpr (K == 4) {
       const uint4 a = buf_load16(ru, uoff(t, ea, 0));
       ua[slot][0] = __uint_as_float(a.x), ua[slot][1] = __uint_as_float(a.y);
       ua[slot][2] = __uint_as_float(a.z), ua[slot][3] = __uint_as_float(a.w);
@@ -112,9 +130,9 @@ k_fwd_hw_ring(Shape s, const float *__restrict__ u, const bf16 *__restrict__ w0,
     }
   };
 
-  // history: xf[(i - j) & 3] holds x[t - j] (fp32) at step i; rows of the
+  // history: xf[(i - j) mod HS] holds x[t - j] (fp32) at step i; rows of the
   // previous sequence read as zero
-  float xf[4][8];
+  float xf[HS][8];
   int pos = 0;
   uint64_t pq = 0;  // VAR: table entries of the next four tokens (t_lo and tpw are multiples of 4)
   const uint64_t *sp4 = reinterpret_cast<const uint64_t *>(s.seqpos);
@@ -125,9 +143,9 @@ k_fwd_hw_ring(Shape s, const float *__restrict__ u, const bf16 *__restrict__ w0,
     pos = t_lo % T;
   }
 #pragma unroll
-  for (int j = 1; j < 4; ++j) {
+  for (int j = 1; j < HS; ++j) {
     const uint4 r = buf_load16(rx, (j < K && pos - j >= 0) ? xoff(t_lo - j) : kOutside);
-    cvt(r, xf[(4 - j) & 3]);
+    cvt(r, xf[(HS - j) & (HS - 1)]);
   }
   // the loop issues, per token, a store and then the loads PD tokens ahead;
   // the prologue keeps that order (its stores fall outside y and are
@@ -140,20 +158,29 @@ k_fwd_hw_ring(Shape s, const float *__restrict__ u, const bf16 *__restrict__ w0,
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  const int n_iter = (t_hi - t_lo + 3) & ~3;
-  for (int it = 0; it < n_iter; it += 4) {
-    const uint64_t pc = pq;
-    if constexpr (VAR) pq = sp4[(t_lo + it + 4) >> 2];
+  // (blocks of HS tokens; tokens past t_hi load nothing and store nothing)
+  const int n_iter = (t_hi - t_lo + HS - 1) / HS * HS;
+  for (int it = 0; it < n_iter; it += HS) {
+    uint64_t pc[HS / 4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int q = 0; q < HS / 4; ++q) {
+      if constexpr (VAR) {
+        pc[q] = q == 0 ? pq : sp4[((t_lo + it) >> 2) + q];
+      } else {
+        pc[q] = 0;
+      }
+    }
+    if constexpr (VAR) pq = sp4[(t_lo + it + HS) >> 2];
+#pragma unroll
+    for (int i = 0; i < HS; ++i) {
       const int t = t_lo + it + i;
-      cvt(xr[i], xf[i]);
-      if constexpr (VAR) pos = (int)((pc >> (16 * i)) & 255u);
+      cvt(xr[i & (PD - 1)], xf[i]);
+      if constexpr (VAR) pos = (int)((pc[i >> 2] >> (16 * (i & 3))) & 255u);
       if (pos == 0) {  // a new sequence starts: no history
 #pragma unroll
-        for (int j = 1; j < 4; ++j)
+        for (int j = 1; j < HS; ++j)
 #pragma unroll
-          for (int c = 0; c < 8; ++c) xf[(i + 4 - j) & 3][c] = 0.f;
+          for (int c = 0; c < 8; ++c) xf[(i + HS - j) & (HS - 1)][c] = 0.f;
       }
       float out[8];
 #pragma unroll
@@ -161,8 +188,9 @@ k_fwd_hw_ring(Shape s, const float *__restrict__ u, const bf16 *__restrict__ w0,
         float a = xf[i][c];
 #pragma unroll
         for (int j = 0; j < K; ++j) {
-          const float uj = S2 ? (((second >> c) & 1) ? ub[i][j] : ua[i][j]) : ua[i][j];
-          a = fmaf(uj + b[c][j], xf[(i + 4 - j) & 3][c], a);
+          const int sl = i & (PD - 1);
+          const float uj = S2 ? (((second >> c) & 1) ? ub[sl][j] : ua[sl][j]) : ua[sl][j];
+          a = fmaf(uj + b[c][j], xf[(i + HS - j) & (HS - 1)][c], a);
         }
         out[c] = a;
       }
@@ -172,7 +200,7 @@ k_fwd_hw_ring(Shape s, const float *__restrict__ u, const bf16 *__restrict__ w0,
         w[q] = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)out[2 * q]) |
                ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)out[2 * q + 1]) << 16);
       buf_store16(ry, xoff(t), make_uint4(w[0], w[1], w[2], w[3]));
-      load_tok(i, t + PD);
+      load_tok(i & (PD - 1), t + PD);
       if constexpr (!VAR) pos = pos + 1 == T ? 0 : pos + 1;
     }
   }
@@ -279,14 +307,15 @@ void launch(const Shape &s, const float *u, const void *w0, const void *x, void 
 // 32-bit offsets
 static bool ring_ok(const Shape &s) {
   const int64_t lim = ((int64_t)1 << 30);
-  return s.k <= 4 && s.hd >= 8 && s.D % 8 == 0 && s.BT * s.D < lim && s.BT * s.N * 2 < lim;
+  return s.hd >= 8 && s.D % 8 == 0 && s.BT * s.D < lim && s.BT * s.N * 2 < lim;
 }
 
 template <int K, bool S2>
 static void launch_ring(const Shape &s, const float *u, const void *w0, const void *x, void *y, hipStream_t st) {
   const int n_vg = (int)ceil_div(s.D, 512);
-  // about three waves per SIMD, runs of a multiple of 4 tokens
-  int tpw = (int)ceil_div(s.BT * n_vg, 3 * 4 * 256);
+  // about three waves per SIMD (two for 5..8 taps, which hold that many),
+  // runs of a multiple of 4 tokens
+  int tpw = (int)ceil_div(s.BT * n_vg, (K <= 4 ? 3 : 2) * 4 * 256);
   tpw = std::max(16, (tpw + 3) & ~3);
   const int n_runs = (int)ceil_div(s.BT, tpw);
   const int waves = n_vg * n_runs;
@@ -313,7 +342,15 @@ int fwd_headwise(const Shape &s, const float *u, const void *w0, const void *x, 
       case 6: launch_ring<3, false>(s, u, w0, x, y, st); break;
       case 7: launch_ring<3, true>(s, u, w0, x, y, st); break;
       case 8: launch_ring<4, false>(s, u, w0, x, y, st); break;
-      default: launch_ring<4, true>(s, u, w0, x, y, st); break;
+      case 9: launch_ring<4, true>(s, u, w0, x, y, st); break;
+      case 10: launch_ring<5, false>(s, u, w0, x, y, st); break;
+      case 11: launch_ring<5, true>(s, u, w0, x, y, st); break;
+      case 12: launch_ring<6, false>(s, u, w0, x, y, st); break;
+      case 13: launch_ring<6, true>(s, u, w0, x, y, st); break;
+      case 14: launch_ring<7, false>(s, u, w0, x, y, st); break;
+      case 15: launch_ring<7, true>(s, u, w0, x, y, st); break;
+      case 16: launch_ring<8, false>(s, u, w0, x, y, st); break;
+      default: launch_ring<8, true>(s, u, w0, x, y, st); break;
     }
   } else if (s.k <= 4)
     launch<T, 4>(s, u, w0, x, y, st);

@@ -73,6 +73,14 @@ SMALL = [
     # K tail (d_model 200, 136), ragged row blocks, columns padded to the 32-column tile (72)
     Workload("hw_bf16_N256_ragged", B=1, T=333, d=200, D=512, k=4, kind=HEADWISE, n_heads=64, seed=57),
     Workload("hw_bf16_N72", B=2, T=150, d=136, D=1152, k=4, kind=HEADWISE, n_heads=18, seed=58),
+    # 5..8 taps on the tuned head-wise kernels (4 channels per lane in the
+    # backward): straddling heads (68, 12), heads of 4 channels, a ragged
+    # sequence, and a slice of the 2B QKV shape that spans many blocks
+    Workload("hw_bf16_k5_hd68", B=2, T=130, d=96, D=544, k=5, kind=HEADWISE, n_heads=8, seed=41),
+    Workload("hw_bf16_k6_hd12", B=1, T=200, d=32, D=96, k=6, kind=HEADWISE, n_heads=8, seed=42),
+    Workload("hw_bf16_k7_hd4", B=2, T=77, d=16, D=64, k=7, kind=HEADWISE, n_heads=16, seed=43),
+    Workload("hw_bf16_k8_hd128_ragged", B=2, T=333, d=64, D=1024, k=8, kind=HEADWISE, n_heads=8, seed=44),
+    Workload("hw_bf16_k6_2b_slice", B=1, T=4096, d=128, D=3072, k=6, kind=HEADWISE, n_heads=24, seed=45),
     # more wide weights: 96 and 160 columns with d_model tails (200, 136)
     Workload("hw_bf16_N96_d200", B=2, T=333, d=200, D=768, k=4, kind=HEADWISE, n_heads=24, seed=59),
     Workload("hw_bf16_N160_d136", B=1, T=200, d=136, D=1280, k=4, kind=HEADWISE, n_heads=40, seed=60),
@@ -367,6 +375,8 @@ PACKED = [
     Workload("pk_hw_fp32_k5", B=1, T=308, d=32, D=48, k=5, kind=HEADWISE, n_heads=3, dtype="fp32", seed=80),
     Workload("pk_lr_fp32", B=1, T=308, d=32, D=64, k=4, kind=LOWRANK, rank=8, dtype="fp32", seed=81),
     Workload("pk_lr_bf16_D100", B=1, T=308, d=64, D=100, k=3, kind=LOWRANK, rank=16, seed=82),
+    Workload("pk_hw_bf16_k8", B=1, T=308, d=64, D=512, k=8, kind=HEADWISE, n_heads=8, seed=84),
+    Workload("pk_hw_bf16_k6_hd68", B=1, T=308, d=64, D=544, k=6, kind=HEADWISE, n_heads=8, seed=85),
 ]
 
 
