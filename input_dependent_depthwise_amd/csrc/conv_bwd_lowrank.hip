@@ -45,8 +45,10 @@ constexpr int kCW = 16;          // channels per wave
 // Waves per block: 4 (64 channels) when rank <= 16, else 8 (128 channels).
 // Two 4-wave blocks share a CU, so one block's barriers overlap the other's
 // work; with a larger rank the per-slice dz partials (rank floats per token
-// and slice) grow too much for the narrower slices.
-inline int waves_for(const Shape &s) { return s.rank <= 16 ? 4 : 8; }
+// and slice) grow too much for the narrower slices.  Filters of 5..8 taps
+// take 4-wave blocks of one wave per SIMD: their U fragments and dU
+// accumulators need more registers than two waves per SIMD leave.
+inline int waves_for(const Shape &s) { return (s.rank <= 16 || s.k > 4) ? 4 : 8; }
 constexpr int kGRow = 40;        // LDS row of the token-contiguous z^T tile: 32 tokens + pad (bf16)
 // G of one tap in LDS: 32 token rows of 16 channels (32 bytes), 128 bytes of
 // pad after every 8 rows and the row's four 8-byte channel quads swapped in
@@ -91,7 +93,7 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 // its document come from the per-token table, loaded with the tile's other
 // operands; every tile takes the masked path).
 template <int K, int KQ, int NQ, int kW, bool VAR>
-__global__ void __launch_bounds__(kW * 64, 2)
+__global__ void __launch_bounds__(kW * 64, K <= 4 ? 2 : 1)
 k_bwd_lr(Params P) {
   constexpr int kDt = kW * kCW;    // channels per block
   // LDS row of the x / dy tiles (bf16 elements): 36 or 68 dwords, so that the
@@ -500,7 +502,7 @@ BwdLayout bwd_layout(const Shape &s) {
 
 bool bwd_lowrank_supported(const Shape &s) {
   // 32-bit element and byte offsets: x, dy, dx below 2 GiB
-  return s.kind == DYNCONV_LOWRANK && s.D % 16 == 0 && s.k <= 4 && s.rank >= 1 && s.rank <= 32 &&
+  return s.kind == DYNCONV_LOWRANK && s.D % 16 == 0 && s.k <= 8 && s.rank >= 1 && s.rank <= 32 &&
          s.BT * s.D * 2 < ((int64_t)1 << 31) - 64;
 }
 
@@ -554,13 +556,23 @@ int bwd_lowrank(const Shape &s, const BwdLayout &L, const float *z, const void *
   else if (KQ == 1 && NQ == 2 && kw == 8) LR(K_, 1, 2, 8);  \
   else if (KQ == 2 && NQ == 2 && kw == 8) LR(K_, 2, 2, 8);  \
   else rc = DYNCONV_E_LIMIT;
+#define LR_K8(K_)                                           \
+  if (KQ == 1 && NQ == 1) LR(K_, 1, 1, 4);                  \
+  else if (KQ == 1 && NQ == 2) LR(K_, 1, 2, 4);             \
+  else if (KQ == 2 && NQ == 2) LR(K_, 2, 2, 4);             \
+  else rc = DYNCONV_E_LIMIT;
   switch (s.k) {
     case 1: LR_K(1) break;
     case 2: LR_K(2) break;
     case 3: LR_K(3) break;
     case 4: LR_K(4) break;
+    case 5: LR_K8(5) break;
+    case 6: LR_K8(6) break;
+    case 7: LR_K8(7) break;
+    case 8: LR_K8(8) break;
     default: rc = DYNCONV_E_LIMIT;
   }
+#undef LR_K8
 #undef LR_K
 #undef LR
   trace_end(tr, st);

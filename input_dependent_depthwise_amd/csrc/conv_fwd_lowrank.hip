@@ -14,7 +14,8 @@
 // tokens of a tile, K is the rank.  Lane l owns token l%32 and the 8
 // channels 8*(l/32)..+7 of a 16-channel group; two MFMAs ("quads" p = 0, 1)
 // give it taps 0..3 of channels 8*(l/32)+4p+b (b = 0..3) in accumulator
-// elements 4b+r (k <= 4; wider filters take the plain VALU kernel).  The bias w0
+// elements 4b+r; filters of 5..8 taps take a second pair of MFMAs per group
+// for taps 4..7 ("tap halves").  The bias w0
 // enters the same MFMA chain as one extra K row: the B operand (z) carries a
 // constant 1 at q = r and the A operand carries w0 there, so the filter
 // leaves the matrix core complete.  Each lane gathers its A-operand values
@@ -46,6 +47,7 @@ template <int K, int KQ, bool VAR>
 __global__ void __launch_bounds__(256)
 k_fwd_lowrank(Shape s, const float *__restrict__ z, const bf16 *__restrict__ U, const bf16 *__restrict__ w0,
               const bf16 *__restrict__ x, bf16 *__restrict__ y, int tpb, int n_tiles) {
+  constexpr int TH = K > 4 ? 2 : 1;     // tap halves (taps 0..3, 4..7)
   constexpr int KH = K - 1;             // history rows
   constexpr int ZW = KQ * 16, ZWP = ZW + 8;
   constexpr int CH = kDt / 8;           // 16-byte chunks per row
@@ -68,16 +70,15 @@ k_fwd_lowrank(Shape s, const float *__restrict__ z, const bf16 *__restrict__ U, 
     if (q >= rank) (&zs[0][0])[e] = (bf16)(q == rank ? 1.f : 0.f);
   }
 
-  // A fragments for this wave's groups [g][p][kq], gathered by each lane from
-  // U and w0: row m = tl is (channel 16gg + 8((m/4)%2) + 4p + m/8, tap m%4),
-  // K index q = 16kq + 8hh + i is U's row for q < r, the bias w0 for q = r,
-  // zero beyond (and for taps >= k)
-  bf16x8 af[kCPW][2][KQ];
+  // A fragments for this wave's groups [g][p][th][kq], gathered by each lane
+  // from U and w0: row m = tl is (channel 16gg + 8((m/4)%2) + 4p + m/8, tap
+  // 4th + m%4), K index q = 16kq + 8hh + i is U's row for q < r, the bias w0
+  // for q = r, zero beyond (and for taps >= k)
+  bf16x8 af[kCPW][2][TH][KQ];
   bool glive[kCPW];
   {
     const auto ru = make_rsrc(U, (uint32_t)((int64_t)rank * D * K * 2));
     const auto rw = make_rsrc(w0, w0 ? (uint32_t)(D * K * 2) : 0u);  // no bias: every load reads 0
-    const int j = tl % 4;
     const int kqb = rank / 16, ib = rank % 8, hb = (rank / 8) % 2;  // where q = rank sits
 #pragma unroll
     for (int g = 0; g < kCPW; ++g) {
@@ -86,20 +87,24 @@ k_fwd_lowrank(Shape s, const float *__restrict__ z, const bf16 *__restrict__ U, 
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
         const int c = cblk + 16 * gl + 8 * ((tl / 4) % 2) + 4 * p + tl / 8;
-        const bool ok = glive[g] && j < K;
-        const float bias =
-            bf16_bits_to_float(__builtin_amdgcn_raw_buffer_load_b16(rw, ok && hh == hb ? (uint32_t)((c * K + j) * 2) : kOutside, 0, 0));
 #pragma unroll
-        for (int kq = 0; kq < KQ; ++kq) {
-          float v[8];
+        for (int th = 0; th < TH; ++th) {
+          const int j = 4 * th + tl % 4;
+          const bool ok = glive[g] && j < K;
+          const float bias = bf16_bits_to_float(
+              __builtin_amdgcn_raw_buffer_load_b16(rw, ok && hh == hb ? (uint32_t)((c * K + j) * 2) : kOutside, 0, 0));
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int q = 16 * kq + 8 * hh + i;
-            const uint32_t off = ok && q < rank ? (uint32_t)((q * D * K + c * K + j) * 2) : kOutside;
-            v[i] = bf16_bits_to_float(__builtin_amdgcn_raw_buffer_load_b16(ru, off, 0, 0)) +
-                   (kq == kqb && i == ib ? bias : 0.f);
+          for (int kq = 0; kq < KQ; ++kq) {
+            float v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const int q = 16 * kq + 8 * hh + i;
+              const uint32_t off = ok && q < rank ? (uint32_t)((q * D * K + c * K + j) * 2) : kOutside;
+              v[i] = bf16_bits_to_float(__builtin_amdgcn_raw_buffer_load_b16(ru, off, 0, 0)) +
+                     (kq == kqb && i == ib ? bias : 0.f);
+            }
+            af[g][p][th][kq] = pack_bf16x8(v);
           }
-          af[g][p][kq] = pack_bf16x8(v);
         }
       }
     }
@@ -198,16 +203,21 @@ k_fwd_lowrank(Shape s, const float *__restrict__ z, const bf16 *__restrict__ U, 
 #pragma unroll
       for (int i = 0; i < 8; ++i) out[i] = xv[0][i];
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        f32x16 acc = {};
+      for (int p = 0; p < 2; ++p)
 #pragma unroll
-        for (int kq = 0; kq < KQ; ++kq) acc = mfma32(af[g][p][kq], bz[kq], acc);
-        // acc[4b + r] = w[t][channel 4p+b of this half][tap r]
+        for (int th = 0; th < TH; ++th) {
+          f32x16 acc = {};
 #pragma unroll
-        for (int b4 = 0; b4 < 4; ++b4)
+          for (int kq = 0; kq < KQ; ++kq) acc = mfma32(af[g][p][th][kq], bz[kq], acc);
+          // acc[4b + r] = w[t][channel 4p+b of this half][tap 4th + r]
 #pragma unroll
-          for (int j = 0; j < K; ++j) out[4 * p + b4] = fmaf(acc[4 * b4 + j], xv[j][4 * p + b4], out[4 * p + b4]);
-      }
+          for (int b4 = 0; b4 < 4; ++b4)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int j = 4 * th + r;
+              if (j < K) out[4 * p + b4] = fmaf(acc[4 * b4 + r], xv[j][4 * p + b4], out[4 * p + b4]);
+            }
+        }
       uint32_t w[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -230,7 +240,7 @@ k_fwd_lowrank(Shape s, const float *__restrict__ z, const bf16 *__restrict__ U, 
 bool fwd_lowrank_supported(const Shape &s) {
   // 32-bit element and byte offsets into x, y and z
   const int64_t lim = ((int64_t)1 << 31) - 64;
-  return s.D % 16 == 0 && s.rank + 1 <= 64 && s.k <= 4 && s.BT * s.D * 2 < lim && s.BT * s.rank * 4 < lim &&
+  return s.D % 16 == 0 && s.rank + 1 <= 64 && s.k <= 8 && s.BT * s.D * 2 < lim && s.BT * s.rank * 4 < lim &&
          (int64_t)s.rank * s.D * s.k * 2 < lim;
 }
 
@@ -267,7 +277,11 @@ int fwd_lowrank(const Shape &s, const float *z, const void *U, const void *w0, c
     case 1: LAUNCH_K(1) break;
     case 2: LAUNCH_K(2) break;
     case 3: LAUNCH_K(3) break;
-    default: LAUNCH_K(4) break;
+    case 4: LAUNCH_K(4) break;
+    case 5: LAUNCH_K(5) break;
+    case 6: LAUNCH_K(6) break;
+    case 7: LAUNCH_K(7) break;
+    default: LAUNCH_K(8) break;
   }
 #undef LAUNCH_K
 #undef LAUNCH

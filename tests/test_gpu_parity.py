@@ -81,6 +81,15 @@ SMALL = [
     Workload("hw_bf16_k7_hd4", B=2, T=77, d=16, D=64, k=7, kind=HEADWISE, n_heads=16, seed=43),
     Workload("hw_bf16_k8_hd128_ragged", B=2, T=333, d=64, D=1024, k=8, kind=HEADWISE, n_heads=8, seed=44),
     Workload("hw_bf16_k6_2b_slice", B=1, T=4096, d=128, D=3072, k=6, kind=HEADWISE, n_heads=24, seed=45),
+    # 5..8 taps on the matrix-core low-rank kernels (a second tap half in the
+    # forward; one wave per SIMD in the backward): ranks 1 .. 32, bias and no
+    # bias, a slice of the 150M QKV shape
+    Workload("lr_bf16_r16_k5", B=2, T=300, d=128, D=384, k=5, kind=LOWRANK, rank=16, seed=46),
+    Workload("lr_bf16_r32_k8", B=1, T=200, d=256, D=1024, k=8, kind=LOWRANK, rank=32, seed=47),
+    Workload("lr_bf16_r8_k6_T64", B=3, T=64, d=64, D=256, k=6, kind=LOWRANK, rank=8, seed=48, bias_std=0.0),
+    Workload("lr_bf16_r20_k7", B=1, T=200, d=256, D=512, k=7, kind=LOWRANK, rank=20, seed=49),
+    Workload("lr_bf16_r1_k5", B=2, T=64, d=32, D=64, k=5, kind=LOWRANK, rank=1, seed=50),
+    Workload("lr_bf16_k8_150m_slice", B=2, T=2048, d=768, D=2304, k=8, kind=LOWRANK, rank=16, seed=61),
     # more wide weights: 96 and 160 columns with d_model tails (200, 136)
     Workload("hw_bf16_N96_d200", B=2, T=333, d=200, D=768, k=4, kind=HEADWISE, n_heads=24, seed=59),
     Workload("hw_bf16_N160_d136", B=1, T=200, d=136, D=1280, k=4, kind=HEADWISE, n_heads=40, seed=60),
@@ -376,6 +385,8 @@ PACKED = [
     Workload("pk_lr_fp32", B=1, T=308, d=32, D=64, k=4, kind=LOWRANK, rank=8, dtype="fp32", seed=81),
     Workload("pk_lr_bf16_D100", B=1, T=308, d=64, D=100, k=3, kind=LOWRANK, rank=16, seed=82),
     Workload("pk_hw_bf16_k8", B=1, T=308, d=64, D=512, k=8, kind=HEADWISE, n_heads=8, seed=84),
+    Workload("pk_lr_bf16_r16_k8", B=1, T=308, d=128, D=384, k=8, kind=LOWRANK, rank=16, seed=86),
+    Workload("pk_lr_bf16_r32_k6", B=1, T=308, d=64, D=256, k=6, kind=LOWRANK, rank=32, seed=87),
     Workload("pk_hw_bf16_k6_hd68", B=1, T=308, d=64, D=544, k=6, kind=HEADWISE, n_heads=8, seed=85),
 ]
 
