@@ -28,8 +28,10 @@
 //     channels in the accumulator);
 //   * G goes to LDS token-major (8-byte writes) and comes back transposed
 //     (ds_read_b64_tr_b16, four tokens of one channel per lane) as the A
-//     operand of D[channel][q] = G^T z over the tile's 32 tokens (dU); the
-//     same fragment dotted with ones gives dw0.
+//     operand of D[channel][q] = G^T z over the tile's 32 tokens (dU);
+//   * dw0 sums the fp32 G products (before their rounding to bf16) per lane
+//     in its own LDS slots (no registers held across the walk),
+//     then over the lanes at the end.
 // The block's waves' dz meet in LDS; the block writes one partial per (slice,
 // token).  The global loads of the next tile (or, where registers allow, of
 // the one after) are in flight while a tile is computed.  Matrix-core fragments of U are built by each lane from global
@@ -124,6 +126,7 @@ k_bwd_lr(Params P) {
   __shared__ __attribute__((aligned(16))) bf16 zt[ZC * kGRow + 8];     // z^T: rows q, tokens t0 .. t0+31
   __shared__ __attribute__((aligned(16))) unsigned char gt[kW][2 * kGTap];  // per wave: G of a tap pair
   __shared__ __attribute__((aligned(16))) float red[kW][64 * RVP];     // per wave: dz partial of a tile
+  __shared__ float dwl[kW][4 * K * 64];  // per lane: dw0 of its 4 channels x K taps, [tap*4 + r][lane]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -178,10 +181,10 @@ k_bwd_lr(Params P) {
     }
 
   f32x4 dUacc[K][NQ];
-  float dw0acc[K];
 #pragma unroll
   for (int j = 0; j < K; ++j) {
-    dw0acc[j] = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dwl[wave][(4 * j + r) * 64 + lane] = 0.f;  // (only this lane touches its slots)
 #pragma unroll
     for (int nq = 0; nq < NQ; ++nq) dUacc[j][nq] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -264,7 +267,6 @@ k_bwd_lr(Params P) {
   if (NSET > 1 && tile_hi > tile_lo + 1) prefetch(NSET - 1, tile_lo + 1);
   const auto rdx = make_rsrc(P.dx, (uint32_t)(s.BT * s.D * 2));
   const auto rg = make_rsrc(P.gpart + (int64_t)blockIdx.x * s.BT * rank, (uint32_t)(s.BT * rank * 4));
-  const uint32_t ones = 0x3f803f80u;     // bf16 pair (1, 1)
   // store offsets at tile 0 (the range checks of rdx / rg drop rows past BT
   // and masked slots): dx of the lane's token n, channels cw+4g .. +3; the dz
   // partial of thread -> (q, token), token fastest (consecutive threads read
@@ -386,6 +388,8 @@ k_bwd_lr(Params P) {
           gv[tb][2 * p + 1] = dot2z(xw[p], dhi[tb][p]);
         }
       }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dwl[wave][(4 * j + r) * 64 + lane] += gv[0][r] + gv[1][r];
       // G of tap j rounded to bf16 once, channel pairs; token-major copy in LDS
       const bool odd = j & 1;
       uint32_t gq[2][2];
@@ -416,8 +420,7 @@ k_bwd_lr(Params P) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // dU: A[m = channel n][k = token 8g + i] = G of the tap; B = z^T.  dw0: the
-      // same fragment dotted with ones.
+      // dU: A[m = channel n][k = token 8g + i] = G of the tap; B = z^T
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         const int jt = 2 * jp + jj;
@@ -427,7 +430,6 @@ k_bwd_lr(Params P) {
           const uint4 raw = make_uint4(lo.x, lo.y, hi.x, hi.y);
 #pragma unroll
           for (int nq = 0; nq < NQ; ++nq) dUacc[jt][nq] = mfma16(as_bf16x8(raw), zb[nq], dUacc[jt][nq]);
-          dw0acc[jt] = dot2(raw.w, ones, dot2(raw.z, ones, dot2(raw.y, ones, dot2(raw.x, ones, dw0acc[jt]))));
         }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -469,12 +471,17 @@ k_bwd_lr(Params P) {
   // ---- block epilogue: dU and dw0 partials of this token range ----
 #pragma unroll
   for (int j = 0; j < K; ++j) {
-    // dw0: lanes n, n+16, n+32, n+48 hold the same (channel, tap), different tokens
-    float v = dw0acc[j];
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    const int64_t c = cw + n;
-    if (lane < 16 && c < s.D) P.dw0p[(int64_t)blockIdx.y * Dk + c * K + j] = v;
+    // dw0: the 16 lanes of one g hold the same channels, different tokens
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float v = dwl[wave][(4 * j + r) * 64 + lane];
+      v += __shfl_xor(v, 1);
+      v += __shfl_xor(v, 2);
+      v += __shfl_xor(v, 4);
+      v += __shfl_xor(v, 8);
+      const int64_t c = cw + 4 * g + r;
+      if (n == 0 && c < s.D) P.dw0p[(int64_t)blockIdx.y * Dk + c * K + j] = v;
+    }
     // dU: lane holds D[m = 4g + r][q - 16nq = n] = dU[q][(cw + 4g + r) * k + j]
 #pragma unroll
     for (int nq = 0; nq < NQ; ++nq)
