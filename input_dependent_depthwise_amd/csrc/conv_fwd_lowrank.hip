@@ -23,8 +23,11 @@
 // starts and holds them in VGPRs while the block walks its tokens.
 //
 // x rows t-k+1 .. t are read from an LDS tile (16-byte reads, rows padded
-// to spread banks) that the block fills with coalesced 16-byte loads; y is
-// written as 16-byte stores.  HBM roofline: per token 2*D*2 bytes of x and y
+// to spread banks) that the block fills with coalesced 16-byte loads.  y goes
+// through an LDS tile too (double-buffered): the lanes, which own tokens,
+// write it there, and after the next tile's barrier the block stores it
+// row-contiguous, four rows of 256 bytes per wave instruction (a store
+// straight from the token-owning lanes would cover 32 rows x 32 bytes).  HBM roofline: per token 2*D*2 bytes of x and y
 // plus 4*r bytes of z.
 #include "kernels.h"
 #include "bufio.h"
@@ -56,6 +59,7 @@ k_fwd_lowrank(Shape s, const float *__restrict__ z, const bf16 *__restrict__ U, 
   constexpr int kSLoads = (32 * ZW + 255) / 256;
   __shared__ __attribute__((aligned(16))) unsigned char xs[2][kXRows * kRowB];
   __shared__ __attribute__((aligned(16))) bf16 zs[2][32 * ZWP + 8];  // + a spare slot for unused z loads
+  __shared__ __attribute__((aligned(16))) unsigned char ys[2][32 * kRowB];  // y of a tile, same row layout as x
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, tl = lane & 31;
@@ -128,11 +132,18 @@ k_fwd_lowrank(Shape s, const float *__restrict__ z, const bf16 *__restrict__ U, 
     v_gbase[q] = ok ? (uint32_t)((r - KH) * D + cblk + c16 * 8) * 2u : kOutside;
     v_loff[q] = r * kRowB + c16 * 16;
   }
-  // y store offset at tile 0 of the lane's token and 8 channels, per group
-  uint32_t y_base[kCPW];
+  // y store slots (from the LDS tile): chunk e = tid + 256 q is row e / CH,
+  // 16-byte chunk e % CH; offset at tile 0, kOutside past the slice's channels
+  constexpr int kYS = 32 * CH / 256;  // stores per thread and tile
+  uint32_t y_base[kYS];
+  int y_loff[kYS];
 #pragma unroll
-  for (int g = 0; g < kCPW; ++g)
-    y_base[g] = glive[g] ? (uint32_t)(tl * D + cblk + (wave * kCPW + g) * 16 + hh * 8) * 2u : kOutside;
+  for (int q = 0; q < kYS; ++q) {
+    const int e = tid + q * 256;
+    const int r = e / CH, c16 = e % CH;
+    y_base[q] = c16 * 8 < nch ? (uint32_t)(r * D + cblk + c16 * 8) * 2u : kOutside;
+    y_loff[q] = r * kRowB + c16 * 16;
+  }
   uint32_t s_gbase[kSLoads];
   int s_loff[kSLoads];
 #pragma unroll
@@ -163,6 +174,16 @@ k_fwd_lowrank(Shape s, const float *__restrict__ z, const bf16 *__restrict__ U, 
       ppre[set] = __builtin_amdgcn_raw_buffer_load_b16(rp, tin ? (uint32_t)(tile * 32 + tl) * 2u : kOutside, 0, 0);
   };
 
+  // y of a tile from its LDS tile (rows past BT fall outside ry; tiles past
+  // the block's range store nothing)
+  auto store_y = [&](const int set, const int tile) {
+    const bool tin = tile >= tile_lo && tile < tile_hi;
+    const uint32_t ystep = (uint32_t)(tile * 32 * D) * 2u;
+#pragma unroll
+    for (int q = 0; q < kYS; ++q)
+      buf_store16(ry, tin ? y_base[q] + ystep : kOutside, *reinterpret_cast<const uint4 *>(ys[set] + y_loff[q]));
+  };
+
   auto step = [&](const int set, const int tile) {
     // ---- stage this tile, then start loading the one two ahead ----
 #pragma unroll
@@ -173,12 +194,10 @@ k_fwd_lowrank(Shape s, const float *__restrict__ z, const bf16 *__restrict__ U, 
     // (read before the prefetch below refills the set)
     const int pos = VAR ? (int)(ppre[set] & 255u) : (int)((uint32_t)t % (uint32_t)s.T);
     __syncthreads();
+    // the previous tile's y is complete in the other LDS tile (its writes
+    // precede this barrier); this tile's y tile was last read before it
+    store_y(set ^ 1, tile - 1);
     prefetch(set, tile + 2);
-
-    // y of this tile: rows past BT fall outside ry; tiles past the block's
-    // range store nothing
-    const bool tin = tile < tile_hi;
-    const uint32_t ystep = (uint32_t)(tile * 32 * D) * 2u;
     bf16x8 bz[KQ];
 #pragma unroll
     for (int kq = 0; kq < KQ; ++kq)
@@ -223,16 +242,20 @@ k_fwd_lowrank(Shape s, const float *__restrict__ z, const bf16 *__restrict__ U, 
       for (int i = 0; i < 4; ++i)
         w[i] = (uint32_t)__builtin_bit_cast(uint16_t, (bf16)out[2 * i]) |
                ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)out[2 * i + 1]) << 16);
-      buf_store16(ry, tin ? y_base[g] + ystep : kOutside, make_uint4(w[0], w[1], w[2], w[3]));
+      *reinterpret_cast<uint4 *>(ys[set] + tl * kRowB + cl * 2) = make_uint4(w[0], w[1], w[2], w[3]);
     }
   };
 
   prefetch(0, tile_lo);
   prefetch(1, tile_lo + 1);
-  for (int tile = tile_lo; tile < tile_hi; tile += 2) {
+  int tile = tile_lo;
+  for (; tile < tile_hi; tile += 2) {
     step(0, tile);
     step(1, tile + 1);
   }
+  // the last pair's second tile (set 1) is still in LDS
+  __syncthreads();
+  store_y(1, tile - 1);
 }
 
 }  // namespace lowrank
