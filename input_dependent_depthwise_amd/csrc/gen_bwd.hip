@@ -156,6 +156,7 @@ k_combine(Shape s, const float *__restrict__ gpart, int n_slices, int R, int Dt,
     w[0] = lo;
     w[1] = hi;
   }
+  if (!gT) return;  // g^T not wanted (the wide dM kernel reads g)
   __syncthreads();
   {  // one 8-token piece of one column per thread
     const int nl = tid / (TT / 8), tc = (tid % (TT / 8)) * 8;
@@ -508,6 +509,138 @@ k_dM(const bf16 *__restrict__ h, const bf16 *__restrict__ gT, float *__restrict_
               dM_tiles(q, n_chunks, n_ranges, tpb, n_tiles), lds);
 }
 
+// dMp[range][i, n] for weights of 129..256 columns, on v_mfma_f32_32x32x16_bf16
+// with A = h^T (rows of d x tokens) and B = g (tokens x columns), both read
+// from row-major LDS tiles with ds_read_b64_tr_b16 (g^T is not needed).
+// Block: 8 waves (two per SIMD) over 128 rows of d x 256 columns; wave w
+// takes rows 64 (w & 1) .. +63 and columns 64 (w >> 1) .. +63 (2 x 2
+// fragments of 32 x 32).  Per 32-token tile the block stages h [32][128] and
+// g [32][256] in LDS (double-buffered, one barrier per tile); every thread
+// loads three 16-byte pieces per tile into a ring of four register sets, so
+// four tiles are in flight while one is computed.  Row pitches of 288 and 544
+// bytes put the four rows of each 16-lane transposed read in distinct banks.
+// Tiles past the range, rows past d and columns past Np read as zeros.
+constexpr int kWH = 144;  // LDS row of the h tile (one token): 128 rows of d + pad, bf16
+constexpr int kWG = 272;  // LDS row of the g tile (one token): 256 columns + pad, bf16
+constexpr int kWRing = 8; // register sets in flight (tiles loaded ahead)
+
+__global__ void __launch_bounds__(512, 1)
+k_dM_wide(const bf16 *__restrict__ h, const bf16 *__restrict__ g, float *__restrict__ dMp, int64_t BT, int d,
+          int N, int Np, int n_chunks, int n_ranges, int tpb, int n_tiles, int slots) {
+  __shared__ __attribute__((aligned(16))) bf16 hs[2][32 * kWH];
+  __shared__ __attribute__((aligned(16))) bf16 gs[2][32 * kWG];
+  const int q = xcd_item(slots);
+  if (q >= n_chunks * n_ranges) return;
+  const int range = q / n_chunks, chunk = q - range * n_chunks;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wi = wave & 1, wn = wave >> 1;
+  const int i0 = chunk * 128;
+  const int tile_lo = range * tpb, ntl = min(n_tiles, tile_lo + tpb) - tile_lo;
+  const int n_loop = (ntl + kWRing - 1) / kWRing * kWRing;
+  const int64_t tok_lo = (int64_t)tile_lo * 32;
+  const int64_t tok_n = min(BT, tok_lo + (int64_t)ntl * 32) - tok_lo;
+  const __amdgpu_buffer_rsrc_t rh = make_rsrc(h + tok_lo * d, (uint32_t)(tok_n * d * 2));
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(g + tok_lo * Np, (uint32_t)(tok_n * Np * 2));
+
+  // pieces: 0 -> h (token tid/16, rows i0 + 8 (tid%16)); 1, 2 -> g (token
+  // e/32, columns 8 (e%32), e = tid + 512 (c - 1))
+  const int h_tok = tid >> 4, h_col = (tid & 15) * 8;
+  const uint32_t h_base = i0 + h_col < d ? (uint32_t)((h_tok * d + i0 + h_col) * 2) : kOutside;
+  uint32_t g_base[2];
+  int g_tok[2], g_col[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int e = tid + 512 * c;
+    g_tok[c] = e >> 5;
+    g_col[c] = (e & 31) * 8;
+    g_base[c] = g_col[c] < Np ? (uint32_t)((g_tok[c] * Np + g_col[c]) * 2) : kOutside;
+  }
+  const uint32_t h_step = (uint32_t)(32 * d * 2), g_step = (uint32_t)(32 * Np * 2);
+  auto off = [&](uint32_t base, uint32_t step, int tile) -> uint32_t {
+    return (base == kOutside || tile >= ntl) ? kOutside : base + (uint32_t)tile * step;
+  };
+  uint4 rr[kWRing][3];
+  auto load = [&](int set, int tile) {
+    rr[set][0] = buf_load16(rh, off(h_base, h_step, tile));
+    rr[set][1] = buf_load16(rg, off(g_base[0], g_step, tile));
+    rr[set][2] = buf_load16(rg, off(g_base[1], g_step, tile));
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+
+  // transposed-read addresses (bytes): group G = lane/16 takes columns
+  // 16 (G & 1) .. +15 and tokens 8 (G >> 1) .. +7; lane L = lane%16 reads
+  // token + L/4 at column 4 (L%4)
+  const int G = lane >> 4, L = lane & 15;
+  const int tr_tok = 8 * (G >> 1) + (L >> 2), tr_col = 16 * (G & 1) + 4 * (L & 3);
+  const unsigned char *hs_b = reinterpret_cast<const unsigned char *>(&hs[0][0]);
+  const unsigned char *gs_b = reinterpret_cast<const unsigned char *>(&gs[0][0]);
+  const int ha = (tr_tok * kWH + 64 * wi + tr_col) * 2;
+  const int ga = (tr_tok * kWG + 64 * wn + tr_col) * 2;
+
+  auto step = [&](int set, int tile) {
+    const int buf = set & 1;
+    *reinterpret_cast<uint4 *>(&hs[buf][h_tok * kWH + h_col]) = rr[set][0];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) *reinterpret_cast<uint4 *>(&gs[buf][g_tok[c] * kWG + g_col[c]]) = rr[set][1 + c];
+    __syncthreads();
+    load(set, tile + kWRing);
+    const unsigned char *hb = hs_b + buf * (32 * kWH * 2) + ha;
+    const unsigned char *gb = gs_b + buf * (32 * kWG * 2) + ga;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      bf16x8 af[2], bfr[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const unsigned char *pa = hb + (16 * kh * kWH + 32 * x) * 2;
+        const uint2 a0 = read_tr16(pa), a1 = read_tr16(pa + 4 * kWH * 2);
+        af[x] = as_bf16x8(make_uint4(a0.x, a0.y, a1.x, a1.y));
+        const unsigned char *pb = gb + (16 * kh * kWG + 32 * x) * 2;
+        const uint2 b0 = read_tr16(pb), b1 = read_tr16(pb + 4 * kWG * 2);
+        bfr[x] = as_bf16x8(make_uint4(b0.x, b0.y, b1.x, b1.y));
+      }
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = mfma32(af[a], bfr[b], acc[a][b]);
+    }
+  };
+  // The prologue issues its loads in the loop's order (h, then the two g
+  // pieces, set by set), so that the compiler's wait count at the loop head
+  // is the steady-state one and three sets stay in flight.
+#pragma unroll
+  for (int s = 0; s < kWRing; ++s) {
+    __builtin_amdgcn_sched_barrier(0);
+    rr[s][0] = buf_load16(rh, off(h_base, h_step, s));
+    __builtin_amdgcn_sched_barrier(0);
+    rr[s][1] = buf_load16(rg, off(g_base[0], g_step, s));
+    __builtin_amdgcn_sched_barrier(0);
+    rr[s][2] = buf_load16(rg, off(g_base[1], g_step, s));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  for (int tile = 0; tile < n_loop; tile += kWRing) {
+#pragma unroll
+    for (int s = 0; s < kWRing; ++s) step(s, tile + s);
+  }
+  // D fragment: lane holds D[8b + 4 (lane/32) + r][lane%32] in element 4b + r
+  float *out = dMp + (int64_t)range * d * N;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int col = 64 * wn + 32 * b + (lane & 31);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int i = i0 + 64 * wi + 32 * a + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        if (i < d && col < N) out[(int64_t)i * N + col] = acc[a][b][e];
+      }
+    }
+}
+
 // dh and dM in one launch: dh writes as much as dM reads, and each alone
 // leaves the chip mostly waiting on memory.  Blocks below 8 * dh_slots are
 // dh blocks (512 threads); the others each run two dM items, one per half,
@@ -629,6 +762,15 @@ GenBwdLayout gen_bwd_layout(const Shape &s) {
   int tpb = (int)ceil_div(L.n_tiles, std::max<int64_t>(1, 512 / L.n_chunks));
   tpb += tpb & 1;
   while ((int64_t)tpb * 32 * s.d * 2 >= ((int64_t)1 << 30) && tpb > 2) tpb -= 2;
+  L.wide = L.Np > 128;
+  if (L.wide) {
+    // one block of 8 waves per CU: about 256 (chunk, range) items; whole
+    // rings of four tiles per range
+    tpb = (int)ceil_div(L.n_tiles, std::max<int64_t>(1, 256 / L.n_chunks));
+    tpb = (int)ceil_div(tpb, gbwd::kWRing) * gbwd::kWRing;
+    while ((int64_t)tpb * 32 * std::max<int64_t>(s.d, L.Np) * 2 >= ((int64_t)1 << 30) && tpb > gbwd::kWRing)
+      tpb -= gbwd::kWRing;
+  }
   L.tpb = tpb;
   L.n_ranges = (int)ceil_div(L.n_tiles, tpb);
   L.n_rb = (int)ceil_div(s.d, 256);
@@ -655,7 +797,7 @@ static size_t g_rows_bytes(const Shape &s, const GenBwdLayout &L) {
 
 size_t gen_bwd_g_bytes(const Shape &s) {
   const GenBwdLayout L = gen_bwd_layout(s);
-  return g_rows_bytes(s, L) + (size_t)L.Np * L.BTp * sizeof(bf16);
+  return g_rows_bytes(s, L) + (L.wide ? 0 : (size_t)L.Np * L.BTp * sizeof(bf16));
 }
 size_t gen_bwd_mp_bytes(const Shape &s) { return (size_t)s.d * gen_bwd_layout(s).Np * sizeof(bf16); }
 size_t gen_bwd_part_bytes(const Shape &s) {
@@ -665,7 +807,8 @@ size_t gen_bwd_part_bytes(const Shape &s) {
 int gen_bwd(const Shape &s, const float *gpart, int n_slices, int R, int Dt, const void *h,
             const void *M, bf16 *g, bf16 *Mp, void *dh, float *dMp, hipStream_t st) {
   const GenBwdLayout L = gen_bwd_layout(s);
-  bf16 *gT = (bf16 *)((char *)g + g_rows_bytes(s, L));
+  // the wide dM kernel reads g itself; the others read g^T
+  bf16 *gT = L.wide ? nullptr : (bf16 *)((char *)g + g_rows_bytes(s, L));
   const int span = s.kind == DYNCONV_HEADWISE ? combine_span(s, Dt) : 0;
   if (span > gbwd::kMaxSpan) return DYNCONV_E_LIMIT;
   if (s.kind == DYNCONV_LOWRANK && R == 16 && L.Np == R) {
@@ -727,6 +870,12 @@ int gen_bwd(const Shape &s, const float *gpart, int n_slices, int R, int Dt, con
     }
   }
   const int slots = (int)ceil_div((int64_t)dm_items, 8);
+  if (L.wide) {
+    hipLaunchKernelGGL(gbwd::k_dM_wide, dim3((unsigned)(8 * slots)), dim3(512), 0, st, (const bf16 *)h, g, dMp,
+                       s.BT, (int)s.d, s.N, L.Np, L.n_chunks, L.n_ranges, L.tpb, L.n_tiles, slots);
+    trace_end(tr, st);
+    return 0;
+  }
   switch (L.Np / 16) {
 #define CASE(nb)                                                                                      \
   case nb:                                                                                            \

@@ -97,6 +97,7 @@ struct GenBwdLayout {
   int n_rb;      // 256-row blocks of d_model (dh)
   int tpr;       // tiles per token range of the dh kernel (even)
   int n_tr;      // token ranges of the dh kernel
+  bool wide;     // Np > 128: the dM kernel for wide weights (reads g, no g^T)
 };
 GenBwdLayout gen_bwd_layout(const Shape &s);
 bool gen_bwd_supported(const Shape &s);

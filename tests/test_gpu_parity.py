@@ -93,6 +93,9 @@ SMALL = [
     # more wide weights: 96 and 160 columns with d_model tails (200, 136)
     Workload("hw_bf16_N96_d200", B=2, T=333, d=200, D=768, k=4, kind=HEADWISE, n_heads=24, seed=59),
     Workload("hw_bf16_N160_d136", B=1, T=200, d=136, D=1280, k=4, kind=HEADWISE, n_heads=40, seed=60),
+    # wide weights on several token ranges of the generator-gradient kernels:
+    # 144 columns, d_model 264 (a partial 128-row chunk), 6 taps, ragged T
+    Workload("hw_bf16_N144_k6_d264", B=2, T=700, d=264, D=576, k=6, kind=HEADWISE, n_heads=24, seed=62),
 ]
 
 
