@@ -16,25 +16,22 @@
 // projections, or after any linear layer), so the fused form reads h once
 // for both the layer's input x and the filter generator.
 //
-// Block: 4 waves (one per SIMD) = RG row groups of 32 rows x KS parts of K,
-// over one slab of 32 NT columns (the grid walks row blocks x slabs, slabs
-// fastest, so the slabs of a row block share its rows of h in L2); 256-column
-// slabs take two such groups of 4 waves, each on half the columns.  Per step
-// of 64 k:
-//   * each wave multiplies its 32 rows by every 32-column tile (of its group) of the staged
-//     weight slice on v_mfma_f32_32x32x16_bf16, accumulators resident.  A
-//     fragments are four 16-byte loads per lane straight from h (the 128-byte
-//     run of each row), issued three steps ahead into a ring of three
-//     register sets, so the loads of the next two steps stay in flight across
-//     the barriers;
-//   * the weight slice (64 rows of the slab's columns, contiguous in memory)
-//     is staged row-major in LDS, double-buffered, one barrier per step; its
-//     loads are issued a step ahead, before that step's A loads, so waiting
-//     for them never waits for A.  A B fragment is two ds_read_b64_tr_b16
-//     (four k of one column each); the reads of the next k-substep are issued
-//     before the current substep's MFMAs.  Rows are padded by 64 bytes so that
-//     the four rows a 32-lane pass reads fall on disjoint quarters of the banks.
-// The K parts meet in LDS at the end in a fixed order.
+// Two kernels:
+//   * k_gen_proj_wide, for 64..192 columns.  Block: 4 waves (one per SIMD) =
+//     RG row groups of 32 rows x KS parts of K, over one slab of 32 NT columns.
+//     Per step of 64 k each wave multiplies its 32 rows by every 32-column tile
+//     of the staged weight slice on v_mfma_f32_32x32x16_bf16, accumulators
+//     resident.  A fragments are four 16-byte loads per lane straight from h
+//     (the 128-byte run of each row), issued three steps ahead into a ring of
+//     three register sets; the weight slice (64 rows of the slab's columns) is
+//     staged row-major in LDS, double-buffered, one barrier per step, its loads
+//     issued a step ahead, before that step's A loads.  A B fragment is two
+//     ds_read_b64_tr_b16 (four k of one column each); the reads of the next
+//     k-substep are issued before the current substep's MFMAs.  Rows are padded
+//     by 64 bytes so that the four rows a 32-lane pass reads fall on disjoint
+//     quarters of the banks.
+//   * k_proj_tile, for 193..256 columns and for the fused form (below).
+// (k_gen_proj_wide: the K parts meet in LDS at the end in a fixed order.)
 #include "kernels.h"
 #include "bufio.h"
 #include "mfma.h"
@@ -73,7 +70,7 @@ struct Cols {
   float *out;     // the generator values
 };
 
-template <int NT, int RG, int KS, int CG, bool FUSED>
+template <int NT, int RG, int KS, int CG>
 __global__ void __launch_bounds__(64 * RG * KS * CG, 1)
 k_gen_proj_wide(const bf16 *__restrict__ h, Cols cols, int64_t M, int K, int n_slabs) {
   using C = WideCfg<NT, RG, KS, CG>;
@@ -91,7 +88,6 @@ k_gen_proj_wide(const bf16 *__restrict__ h, Cols cols, int64_t M, int K, int n_s
   const int nrows = (int)min<int64_t>(C::BM, M - row0);
   const auto rh = make_rsrc(h + row0 * K, (uint32_t)((int64_t)nrows * K * 2));
   const auto rw0 = make_rsrc(cols.W0, (uint32_t)((int64_t)K * cols.N0 * 2));
-  const auto rw1 = make_rsrc(cols.W1, FUSED ? (uint32_t)((int64_t)K * cols.N1 * 2) : 0u);
   const int S = (K + kKT - 1) / kKT;  // steps over all of K
   const int SH = (S + KS - 1) / KS;   // steps per K part (the last part may run past K: zeros)
 
@@ -104,15 +100,7 @@ k_gen_proj_wide(const bf16 *__restrict__ h, Cols cols, int64_t M, int K, int n_s
       const int r = e2 / C::CPR, gc = col0 + (e2 - r * C::CPR) * 8;
       const int k = (sl * SH + st) * kKT + r;
       const bool live = (C::CH % C::NTH == 0 || e < C::CH) && k < K;
-      // a chunk lies wholly in one source, or past both (zeros); the other
-      // source's load falls outside its buffer and reads zeros, so no lane
-      // chooses between resources
       breg[c] = buf_load16(rw0, live && gc < cols.N0 ? (uint32_t)(k * cols.N0 + gc) * 2u : kOutside);
-      if constexpr (FUSED) {
-        const uint4 b1 = buf_load16(
-            rw1, live && gc >= cols.N0 && gc < N ? (uint32_t)(k * cols.N1 + gc - cols.N0) * 2u : kOutside);
-        breg[c] = make_uint4(breg[c].x | b1.x, breg[c].y | b1.y, breg[c].z | b1.z, breg[c].w | b1.w);
-      }
     }
   };
   auto store_b = [&](int buf) {
@@ -228,7 +216,6 @@ k_gen_proj_wide(const bf16 *__restrict__ h, Cols cols, int64_t M, int K, int n_s
   }
 
   // D: lane holds D[8 b + 4 (lane / 32) + r][lane % 32] in element 4 b + r
-  const int split = FUSED ? cols.N0 : 0;
 #pragma unroll
   for (int n = 0; n < NTW; ++n) {
     const int col = col0 + 32 * (NTW * cg + n) + (lane & 31);
@@ -238,43 +225,180 @@ k_gen_proj_wide(const bf16 *__restrict__ h, Cols cols, int64_t M, int K, int n_s
       for (int r = 0; r < 4; ++r) {
         const int row = rg * 32 + 8 * b + 4 * (lane >> 5) + r;
         if (col >= N || row >= nrows) continue;
-        const float v = acc[n][4 * b + r];
-        if (FUSED && col < split)
-          cols.xb[(row0 + row) * cols.N0 + col] = (bf16)v;  // round to nearest even
-        else
-          cols.out[(row0 + row) * (N - split) + col - split] = v;
+        cols.out[(row0 + row) * N + col] = acc[n][4 * b + r];
       }
   }
 }
 
-template <int NT, int RG, int KS, int CG, bool FUSED>
+template <int NT, int RG, int KS, int CG>
 void launch(const bf16 *h, const Cols &cols, int64_t M, int K, hipStream_t st) {
   using C = WideCfg<NT, RG, KS, CG>;
   const size_t lds = C::LDS;
-  const int n_slabs = (int)ceil_div(cols.N0 + cols.N1, C::NP);
-  hipLaunchKernelGGL((k_gen_proj_wide<NT, RG, KS, CG, FUSED>), dim3((unsigned)(ceil_div(M, C::BM) * n_slabs)),
+  const int n_slabs = (int)ceil_div(cols.N0, C::NP);
+  hipLaunchKernelGGL((k_gen_proj_wide<NT, RG, KS, CG>), dim3((unsigned)(ceil_div(M, C::BM) * n_slabs)),
                      dim3(C::NTH), lds, st, h, cols, M, K, n_slabs);
 }
 
 // One block of 4 waves per CU: 128-row blocks when the blocks number at least
-// 256, else 64-row blocks with K in two parts.  The fused form always takes
-// 128-row blocks: its slabs are many (the producing projection's D columns),
-// and its two-part variant would spill registers.
-template <int NT, bool FUSED>
+// 256, else 64-row blocks with K in two parts.
+template <int NT>
 void launch_nt(const bf16 *h, const Cols &cols, int64_t M, int K, hipStream_t st) {
-  const int64_t slabs = ceil_div(cols.N0 + cols.N1, NT * 32);
-  // 256-column slabs: two column groups of 4 waves, two waves per SIMD (the
-  // second hides the first's A loads; 12 % faster for the fused form, 5 % for
-  // 256 generator columns, than one group)
-  constexpr int CG = NT == 8 ? 2 : 1;
-  if constexpr (FUSED) {
-    launch<NT, 4, 1, CG, true>(h, cols, M, K, st);
-  } else {
-    if (ceil_div(M, 128) * slabs >= 256)
-      launch<NT, 4, 1, CG, false>(h, cols, M, K, st);
-    else
-      launch<NT, 2, 2, 1, false>(h, cols, M, K, st);
+  if (ceil_div(M, 128) >= 256)
+    launch<NT, 4, 1, 1>(h, cols, M, K, st);
+  else
+    launch<NT, 2, 2, 1>(h, cols, M, K, st);
+}
+
+// Tile kernel for 193..256 generator columns and for the fused form: 8 waves
+// (two per SIMD) over 128 rows x one 256-column slab, wave w on rows 64 (w & 1)
+// .. +63 and columns 64 (w >> 1) .. +63 (2 x 2 fragments of 32 x 32, so every
+// fragment read from LDS serves two MFMAs).  Per step of 32 k the block stages
+// the h tile [128][32] and the weight tile [32][256] in LDS (double-buffered,
+// one barrier per step); every thread loads three 16-byte pieces per step
+// into a ring of eight register sets, so eight steps are in flight.  A
+// fragments are 16-byte reads of h rows (row pitch 80 bytes: the eight rows of
+// a read pass fall on distinct banks); B fragments are two ds_read_b64_tr_b16
+// (row pitch 544 bytes).  Blocks run over the XCDs so that the slabs of one
+// row block share an XCD (and its L2 copy of those rows of h).
+constexpr int kPA = 40;   // LDS row of the h tile: 32 k + pad, bf16
+constexpr int kPB = 272;  // LDS row of the weight tile (one k): 256 columns + pad, bf16
+// TWO: the launch's columns may come from both sources (each piece is loaded
+// from both, one of the two loads falling outside its buffer); else every
+// column of the launch lies in W0.  The launch covers the columns from c_lo
+// on; columns below cols.N0 go to xb when it is given.  R register sets.
+template <bool TWO, int R>
+__global__ void __launch_bounds__(512, 1)
+k_proj_tile(const bf16 *__restrict__ h, Cols cols, int64_t M, int K, int c_lo, int n_slabs, int n_items,
+            int slots) {
+  __shared__ __attribute__((aligned(16))) bf16 as_[2][128 * kPA];
+  __shared__ __attribute__((aligned(16))) bf16 bs_[2][32 * kPB];
+  const int item = (int)(blockIdx.x & 7) * slots + (int)(blockIdx.x >> 3);
+  if (item >= n_items) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave & 1, wc = wave >> 1;
+  const int slab = item % n_slabs;
+  const int64_t row0 = (int64_t)(item / n_slabs) * 128;
+  const int col0 = c_lo + slab * 256;
+  const int N = cols.N0 + cols.N1;
+  const int nrows = (int)min<int64_t>(128, M - row0);
+  const auto rh = make_rsrc(h + row0 * K, (uint32_t)((int64_t)nrows * K * 2));
+  const auto rw0 = make_rsrc(cols.W0, (uint32_t)((int64_t)K * cols.N0 * 2));
+  const auto rw1 = make_rsrc(cols.W1, TWO ? (uint32_t)((int64_t)K * cols.N1 * 2) : 0u);
+  const int S = (K + 31) / 32;
+  const int n_loop = (S + R - 1) / R * R;
+
+  // pieces: 0 -> h (row tid/4, k 8 (tid%4)); 1, 2 -> weight (k e/32, column
+  // 8 (e%32) of the slab, e = tid + 512 (c - 1)); a weight chunk lies wholly
+  // in one source or past both (zeros)
+  const int a_row = tid >> 2, a_k = (tid & 3) * 8;
+  const uint32_t a_base = (uint32_t)((a_row * K + a_k) * 2);
+  int b_r[2], b_c[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int e = tid + 512 * c;
+    b_r[c] = e >> 5;
+    b_c[c] = (e & 31) * 8;
   }
+  uint4 rr[R][3];
+  auto load = [&](int set, int st) {
+    const int k0 = st * 32;
+    rr[set][0] = buf_load16(rh, k0 + a_k < K ? a_base + (uint32_t)(k0 * 2) : kOutside);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int k = k0 + b_r[c], gc = col0 + b_c[c];
+      const bool live = k < K;
+      rr[set][1 + c] = buf_load16(rw0, live && gc < cols.N0 ? (uint32_t)(k * cols.N0 + gc) * 2u : kOutside);
+      if constexpr (TWO) {
+        const uint4 b1 =
+            buf_load16(rw1, live && gc >= cols.N0 && gc < N ? (uint32_t)(k * cols.N1 + gc - cols.N0) * 2u : kOutside);
+        rr[set][1 + c] = make_uint4(rr[set][1 + c].x | b1.x, rr[set][1 + c].y | b1.y, rr[set][1 + c].z | b1.z,
+                                    rr[set][1 + c].w | b1.w);
+      }
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+
+  // A fragment (a, kh): row 64 wr + 32 a + lane%32, k 16 kh + 8 (lane/32) .. +7
+  const int a_rd = ((64 * wr + (lane & 31)) * kPA + 8 * (lane >> 5)) * 2;
+  // B fragment (kh, b): group G = lane/16 takes columns 16 (G & 1) .. +15 and k
+  // 8 (G >> 1) .. +7; lane L = lane%16 reads k + L/4 at column 4 (L%4)
+  const int G = lane >> 4, L = lane & 15;
+  const int b_rd = ((8 * (G >> 1) + (L >> 2)) * kPB + 64 * wc + 16 * (G & 1) + 4 * (L & 3)) * 2;
+  const unsigned char *as_b = reinterpret_cast<const unsigned char *>(&as_[0][0]);
+  const unsigned char *bs_b = reinterpret_cast<const unsigned char *>(&bs_[0][0]);
+
+  auto step = [&](int set, int st) {
+    const int buf = set & 1;
+    *reinterpret_cast<uint4 *>(&as_[buf][a_row * kPA + a_k]) = rr[set][0];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) *reinterpret_cast<uint4 *>(&bs_[buf][b_r[c] * kPB + b_c[c]]) = rr[set][1 + c];
+    __syncthreads();
+    load(set, st + R);
+    const unsigned char *ab = as_b + buf * (128 * kPA * 2) + a_rd;
+    const unsigned char *bb = bs_b + buf * (32 * kPB * 2) + b_rd;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      bf16x8 af[2], bfr[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        af[x] = as_bf16x8(*reinterpret_cast<const uint4 *>(ab + (32 * x * kPA + 16 * kh) * 2));
+        const unsigned char *pb = bb + (16 * kh * kPB + 32 * x) * 2;
+        const uint2 b0 = read_tr16(pb), b1 = read_tr16(pb + 4 * kPB * 2);
+        bfr[x] = as_bf16x8(make_uint4(b0.x, b0.y, b1.x, b1.y));
+      }
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = mfma32(af[a], bfr[b], acc[a][b]);
+    }
+  };
+  // the prologue issues its loads in the loop's order, set by set, so that the
+  // compiler's wait count at the loop head is the steady-state one
+#pragma unroll
+  for (int s = 0; s < R; ++s) {
+    __builtin_amdgcn_sched_barrier(0);
+    load(s, s);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  for (int st = 0; st < n_loop; st += R) {
+#pragma unroll
+    for (int s = 0; s < R; ++s) step(s, st + s);
+  }
+
+  // D: lane holds D[8 b + 4 (lane / 32) + r][lane % 32] in element 4 b + r
+  const int split = cols.xb ? cols.N0 : 0;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int col = col0 + 64 * wc + 32 * b + (lane & 31);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = 64 * wr + 32 * a + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        if (col >= N || row >= nrows) continue;
+        const float v = acc[a][b][e];
+        if (col < split)
+          cols.xb[(row0 + row) * cols.N0 + col] = (bf16)v;  // round to nearest even
+        else
+          cols.out[(row0 + row) * (N - split) + col - split] = v;
+      }
+    }
+}
+
+// columns [c_lo, c_hi) in slabs of 256
+template <bool TWO, int R>
+void launch_tile(const bf16 *h, const Cols &cols, int64_t M, int K, int c_lo, int c_hi, hipStream_t st) {
+  const int n_slabs = (int)ceil_div(c_hi - c_lo, 256);
+  const int n_items = (int)(ceil_div(M, 128) * n_slabs);
+  const int slots = (int)ceil_div(n_items, 8);
+  if (n_items == 0) return;
+  hipLaunchKernelGGL((k_proj_tile<TWO, R>), dim3((unsigned)(8 * slots)), dim3(512), 0, st, h, cols, M, K, c_lo,
+                     n_slabs, n_items, slots);
 }
 
 }  // namespace
@@ -289,14 +413,17 @@ int gen_proj_wide(const Shape &s, const void *h, const void *M, float *out, hipS
   const bf16 *hh = (const bf16 *)h;
   const Cols cols{(const bf16 *)M, nullptr, s.N, 0, nullptr, out};
   const int K = (int)s.d;
+  if (s.N > 192) {
+    launch_tile<false, 8>(hh, cols, s.BT, K, 0, s.N, st);
+    trace_end(tr, st);
+    return 0;
+  }
   switch (ceil_div(s.N, 32)) {
-    case 2: launch_nt<2, false>(hh, cols, s.BT, K, st); break;
-    case 3: launch_nt<3, false>(hh, cols, s.BT, K, st); break;
-    case 4: launch_nt<4, false>(hh, cols, s.BT, K, st); break;
-    case 5: launch_nt<5, false>(hh, cols, s.BT, K, st); break;
-    case 6: launch_nt<6, false>(hh, cols, s.BT, K, st); break;
-    case 7: launch_nt<7, false>(hh, cols, s.BT, K, st); break;
-    default: launch_nt<8, false>(hh, cols, s.BT, K, st); break;
+    case 2: launch_nt<2>(hh, cols, s.BT, K, st); break;
+    case 3: launch_nt<3>(hh, cols, s.BT, K, st); break;
+    case 4: launch_nt<4>(hh, cols, s.BT, K, st); break;
+    case 5: launch_nt<5>(hh, cols, s.BT, K, st); break;
+    default: launch_nt<6>(hh, cols, s.BT, K, st); break;
   }
   trace_end(tr, st);
   return 0;
@@ -312,7 +439,11 @@ bool proj_fused_ok(const Shape &s) {
 int proj_fused(const Shape &s, const void *h, const void *Wp, const void *M, void *x, float *gen, hipStream_t st) {
   const bool tr = trace_begin(DYNCONV_K_GEN_PROJ, st);
   const Cols cols{(const bf16 *)Wp, (const bf16 *)M, (int)s.D, s.N, (bf16 *)x, gen};
-  launch_nt<8, true>((const bf16 *)h, cols, s.BT, (int)s.d, st);
+  // the producing projection's whole slabs read Wp alone; the rest (a slab
+  // holding both weights' columns, then the generator's) read both sources
+  const int whole = (int)(s.D / 256 * 256);
+  launch_tile<false, 8>((const bf16 *)h, cols, s.BT, (int)s.d, 0, whole, st);
+  launch_tile<true, 4>((const bf16 *)h, cols, s.BT, (int)s.d, whole, (int)s.D + s.N, st);
   trace_end(tr, st);
   return 0;
 }
