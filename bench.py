@@ -71,25 +71,93 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def kernel_source_sha() -> str:
+# Sources each roofline kernel is built from (its own file, the headers it
+# includes, the public header): a traffic record counts only while these are
+# unchanged.
+KERNEL_SOURCES = {
+    ("bwd_conv", "headwise"): ["conv_bwd_headwise.hip"],
+    ("bwd_conv", "lowrank"): ["conv_bwd_lowrank.hip", "mfma.h"],
+    ("fwd_conv", "headwise"): ["conv_fwd_headwise.hip"],
+    ("fwd_conv", "lowrank"): ["conv_fwd_lowrank.hip", "mfma.h"],
+}
+COMMON_SOURCES = ["bufio.h", "common.h", "kernels.h", "../../include/dynconv.h"]
+# the symbol of each roofline kernel in a rocprofv3 trace (substring)
+KERNEL_SYMBOLS = {("bwd_conv", "headwise"): "k_bwd_hw", ("bwd_conv", "lowrank"): "k_bwd_lr",
+                  ("fwd_conv", "headwise"): "k_fwd_h", ("fwd_conv", "lowrank"): "k_fwd_lowrank"}
+
+
+def kernel_source_sha(kernel: str, kind: str) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "input_dependent_depthwise_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in KERNEL_SOURCES[(kernel, kind)] + COMMON_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+            h.update(os.path.basename(f).encode() + fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, workload: str):
+def measured_traffic(kernel: str, w: workloads.Workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken from the current kernel sources; else None."""
-    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.json")
+    was taken from the kernel's current sources; else None."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{w.name}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("source_sha") != kernel_source_sha():
+    if rec.get("source_sha") != kernel_source_sha(kernel, w.kind):
         return None
     return rec.get("bytes_per_launch")
+
+
+def _counter_per_dispatch(path: str, counter: str) -> dict:
+    """Mean value of one counter per kernel name from a rocprofv3 counter CSV."""
+    import csv
+    tot, cnt = {}, {}
+    for r in csv.DictReader(open(path)):
+        if r.get("Counter_Name") != counter:
+            continue
+        k = r["Kernel_Name"]
+        tot[k] = tot.get(k, 0.0) + float(r["Counter_Value"])
+        cnt[k] = cnt.get(k, 0) + 1
+    return {k: tot[k] / cnt[k] for k in tot}
+
+
+def traffic_record(args, paths) -> int:
+    """Writes the traffic record of the roofline kernel (and prints a table of
+    every kernel) from four rocprofv3 --pmc CSVs: FETCH_SIZE and WRITE_SIZE of
+    the workload, then of --copy-calibration 512.  Each counter is scaled by
+    what it reads for the plain copy of known size."""
+    w = workloads.WORKLOADS[args.workload]
+    fetch, write, cf, cw = (_counter_per_dispatch(p, c) for p, c in
+                            zip(paths, ("FETCH_SIZE", "WRITE_SIZE", "FETCH_SIZE", "WRITE_SIZE")))
+    copy_kib = 512 * 1024
+    f_scale = copy_kib / max(cf.values())   # the copy reads 512 MiB
+    w_scale = copy_kib / max(cw.values())   # and writes 512 MiB
+    sym = KERNEL_SYMBOLS[(args.roofline_kernel, w.kind)]
+    rows = []
+    for k in sorted(fetch, key=lambda k: -fetch[k] - write.get(k, 0.0)):
+        rd, wr = fetch[k] * f_scale * 1024, write.get(k, 0.0) * w_scale * 1024
+        rows.append((k, fetch[k], write.get(k, 0.0), rd / 1e6, wr / 1e6))
+    dom = [r for r in rows if sym in r[0]]
+    if not dom:
+        print(f"bench.py --traffic-record: no kernel matching {sym}", file=sys.stderr)
+        return 2
+    k, fk, wk, rd, wr = dom[0]
+    alg = algorithmic_bytes(w)[args.roofline_kernel] * w.tokens
+    rec = {"kernel": args.roofline_kernel, "kernel_symbol": k, "workload": w.name,
+           "source_sha": kernel_source_sha(args.roofline_kernel, w.kind),
+           "source_files": KERNEL_SOURCES[(args.roofline_kernel, w.kind)] + COMMON_SOURCES,
+           "bytes_per_launch": int(round((rd + wr) * 1e6)), "fetch_kib_per_dispatch": round(fk, 1),
+           "write_kib_per_dispatch": round(wk, 1), "fetch_scale": round(f_scale, 4),
+           "write_scale": round(w_scale, 4), "algorithmic_bytes_per_launch": alg}
+    out = args.traffic_out or os.path.join(PROFILES, f"traffic_{args.roofline_kernel}_{w.name}.json")
+    with open(out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    print(f"| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled MB read | scaled MB written |")
+    print(f"|---|---|---|---|---|")
+    for k, fk, wk, rd, wr in rows:
+        print(f"| `{k}` | {fk:.0f} | {wk:.0f} | {rd:.1f} | {wr:.1f} |")
+    print(f"\nscales: FETCH_SIZE {f_scale:.4f}, WRITE_SIZE {w_scale:.4f}; record written to {out}")
+    return 0
 
 
 def cpu_baseline(w: workloads.Workload, inp: dict, budget_s: float) -> dict:
@@ -151,7 +219,15 @@ def main() -> int:
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the layer, run --steps device copies of MIB MiB (a plain copy "
                          "kernel of known size, to scale the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--traffic-record", nargs=4, metavar="CSV",
+                    help="no GPU: build the roofline kernel's traffic record from four rocprofv3 "
+                         "--pmc counter CSVs (FETCH_SIZE, WRITE_SIZE of the workload, then of "
+                         "--copy-calibration 512)")
+    ap.add_argument("--traffic-out", default="", help="where --traffic-record writes (default: profiles/)")
     args = ap.parse_args()
+
+    if args.traffic_record:
+        return traffic_record(args, args.traffic_record)
 
     if args.copy_calibration:
         import torch
@@ -290,7 +366,7 @@ def main() -> int:
     value = w.tokens / (ms / 1e3)
     dom_bytes = ab[dom[2]] * w.tokens
     achieved = dom_bytes / (kern_ms / 1e3) / 1e9
-    traffic = measured_traffic(dom[2], w.name)
+    traffic = measured_traffic(dom[2], w)
     line = {
         "metric": "dynconv fwd+bwd tokens/s", "value": round(value, 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
