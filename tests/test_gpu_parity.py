@@ -96,6 +96,9 @@ SMALL = [
     # wide weights on several token ranges of the generator-gradient kernels:
     # 144 columns, d_model 264 (a partial 128-row chunk), 6 taps, ragged T
     Workload("hw_bf16_N144_k6_d264", B=2, T=700, d=264, D=576, k=6, kind=HEADWISE, n_heads=24, seed=62),
+    # 200 generator columns on the 256-column projection tile (a zero column
+    # tail), d_model 136 (a partial 32-k step), 50 heads of 8
+    Workload("hw_bf16_N200_d136", B=2, T=150, d=136, D=400, k=4, kind=HEADWISE, n_heads=50, seed=63),
 ]
 
 
