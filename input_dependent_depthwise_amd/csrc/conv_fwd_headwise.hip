@@ -206,19 +206,22 @@ k_fwd_hw_ring(Shape s, const float *__restrict__ u, const bf16 *__restrict__ w0,
   }
 }
 
-constexpr int kFwdChunk = 32;  // tokens per thread
+// tokens per thread (chunk): 32, or as few as 4 when that is what it takes
+// to give the chip about 64K threads (short inputs are a latency chain per
+// thread otherwise)
+constexpr int kFwdChunk = 32;
 
 template <typename T, int KP>
 __global__ void __launch_bounds__(256)
 k_fwd_headwise(Shape s, const float *__restrict__ u, const T *__restrict__ w0,
-               const T *__restrict__ x, T *__restrict__ y) {
+               const T *__restrict__ x, T *__restrict__ y, int chunk) {
   constexpr int V = Vec<T>::N;
   const int nvec = (int)(s.D / V);
   const int v = blockIdx.x * 64 + threadIdx.x;
   if (v >= nvec) return;
-  const int64_t row0 = ((int64_t)blockIdx.y * 4 + threadIdx.y) * kFwdChunk;
+  const int64_t row0 = ((int64_t)blockIdx.y * 4 + threadIdx.y) * chunk;
   if (row0 >= s.BT) return;
-  const int64_t row1 = row0 + kFwdChunk < s.BT ? row0 + kFwdChunk : s.BT;
+  const int64_t row1 = row0 + chunk < s.BT ? row0 + chunk : s.BT;
   const int c0 = v * V;
   const int k = s.k;
 
@@ -296,9 +299,11 @@ template <typename T, int KP>
 void launch(const Shape &s, const float *u, const void *w0, const void *x, void *y, hipStream_t st) {
   constexpr int V = Vec<T>::N;
   const int64_t nvec = s.D / V;
-  dim3 grid((unsigned)ceil_div(nvec, 64), (unsigned)ceil_div(s.BT, 4 * kFwdChunk));
+  int chunk = (int)std::min<int64_t>(kFwdChunk, ceil_div(s.BT * nvec, (int64_t)1 << 16));
+  chunk = std::max(4, chunk);
+  dim3 grid((unsigned)ceil_div(nvec, 64), (unsigned)ceil_div(s.BT, 4 * chunk));
   hipLaunchKernelGGL((k_fwd_headwise<T, KP>), grid, dim3(64, 4), 0, st, s, u, (const T *)w0,
-                     (const T *)x, (T *)y);
+                     (const T *)x, (T *)y, chunk);
 }
 
 }  // namespace

@@ -185,47 +185,63 @@ k_dz_simple(Shape s, const T *__restrict__ x, const T *__restrict__ dy, const T 
   g[idx] = acc;
 }
 
+
+// Sums over rows for 16 outputs per block: thread (tx, ty) of a 16 x 16
+// block adds term(o, row) for output o = 16 blockIdx.x + tx over rows ty,
+// ty + 16, ... in ascending order; the 16 row groups are then added in order
+// (deterministic).  Consecutive outputs read neighbouring channels of a row.
+template <typename F>
+__device__ __forceinline__ void rows_reduce(int64_t n_out, int64_t rows, F term, float *__restrict__ out) {
+  __shared__ float part[16][17];
+  const int tx = threadIdx.x, ty = threadIdx.y;
+  const int64_t o = (int64_t)blockIdx.x * 16 + tx;
+  float acc = 0.f;
+  if (o < n_out)
+    for (int64_t row = ty; row < rows; row += 16) acc += term(o, row);
+  part[ty][tx] = acc;
+  __syncthreads();
+  if (ty == 0 && o < n_out) {
+    float t = 0.f;
+    for (int r = 0; r < 16; ++r) t += part[r][tx];
+    out[o] = t;
+  }
+}
+
 // low-rank: dU[q, c*k+j] = sum_rows z[row, q] G[row, c, j]
 template <typename T>
 __global__ void __launch_bounds__(256)
 k_dU_simple(Shape s, const float *__restrict__ z, const T *__restrict__ x, const T *__restrict__ dy,
             float *__restrict__ dU) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t Dk = s.D * s.k;
-  if (idx >= (int64_t)s.N * Dk) return;
-  const int q = (int)(idx / Dk);
-  const int64_t m = idx - (int64_t)q * Dk;
-  const int64_t c = m / s.k;
-  const int j = (int)(m - c * s.k);
-  float acc = 0.f;
-  for (int64_t row = 0; row < s.BT; ++row) acc = fmaf(z[row * s.N + q], gtap(s, x, dy, row, c, j), acc);
-  dU[idx] = acc;
+  rows_reduce((int64_t)s.N * Dk, s.BT, [&](int64_t idx, int64_t row) {
+    const int q = (int)(idx / Dk);
+    const int64_t m = idx - (int64_t)q * Dk;
+    const int64_t c = m / s.k;
+    const int j = (int)(m - c * s.k);
+    return z[row * s.N + q] * gtap(s, x, dy, row, c, j);
+  }, dU);
 }
 
 // dw0[c, j] = sum_rows G[row, c, j]
 template <typename T>
 __global__ void __launch_bounds__(256)
 k_dw0_simple(Shape s, const T *__restrict__ x, const T *__restrict__ dy, float *__restrict__ dw0) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= s.D * s.k) return;
-  const int64_t c = idx / s.k;
-  const int j = (int)(idx - c * s.k);
-  float acc = 0.f;
-  for (int64_t row = 0; row < s.BT; ++row) acc += gtap(s, x, dy, row, c, j);
-  dw0[idx] = acc;
+  rows_reduce(s.D * s.k, s.BT, [&](int64_t idx, int64_t row) {
+    const int64_t c = idx / s.k;
+    const int j = (int)(idx - c * s.k);
+    return gtap(s, x, dy, row, c, j);
+  }, dw0);
 }
 
 // dM[i, n] = sum_rows h[row, i] g[row, n]      (dW or dA)
 template <typename T>
 __global__ void __launch_bounds__(256)
 k_dgen_simple(Shape s, const T *__restrict__ h, const float *__restrict__ g, float *__restrict__ dM) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= s.d * s.N) return;
-  const int64_t i = idx / s.N;
-  const int n = (int)(idx - i * s.N);
-  float acc = 0.f;
-  for (int64_t row = 0; row < s.BT; ++row) acc = fmaf(to_f32(h[row * s.d + i]), g[row * s.N + n], acc);
-  dM[idx] = acc;
+  rows_reduce(s.d * s.N, s.BT, [&](int64_t idx, int64_t row) {
+    const int64_t i = idx / s.N;
+    const int n = (int)(idx - i * s.N);
+    return to_f32(h[row * s.d + i]) * g[row * s.N + n];
+  }, dM);
 }
 
 // dh[row, i] = sum_n g[row, n] M[i, n]      (M = W or A)
@@ -280,6 +296,7 @@ __global__ void __launch_bounds__(256) k_zero16(uint16_t *__restrict__ p, int64_
 // host launchers
 // ---------------------------------------------------------------------------
 static inline dim3 grid1(int64_t n) { return dim3((unsigned)ceil_div(n, 256)); }
+static inline dim3 grid16(int64_t n) { return dim3((unsigned)ceil_div(n, 16)); }  // rows_reduce: 16 outputs per block
 
 void zero_fill(float *p, int64_t n, hipStream_t st) {
   if (p && n > 0) hipLaunchKernelGGL(k_zero, grid1(n), dim3(256), 0, st, p, n);
@@ -325,22 +342,22 @@ int simple_bwd(const Shape &s, const float *gen, const void *W, const void *A, c
                        (const T *)w0, (const T *)dy, (T *)dx);
   }
   if (gg.dw0)
-    hipLaunchKernelGGL(k_dw0_simple<T>, grid1(s.D * s.k), dim3(256), 0, st, s, (const T *)x,
+    hipLaunchKernelGGL(k_dw0_simple<T>, grid16(s.D * s.k), dim3(16, 16), 0, st, s, (const T *)x,
                        (const T *)dy, gg.dw0);
   if (s.stat) return 0;  // no generator (the caller has cleared dh)
   if (s.kind == DYNCONV_HEADWISE) {
     hipLaunchKernelGGL(k_du_simple<T>, grid1(s.BT * s.N), dim3(256), 0, st, s, (const T *)x,
                        (const T *)dy, g);
-    hipLaunchKernelGGL(k_dgen_simple<T>, grid1(s.d * s.N), dim3(256), 0, st, s, (const T *)h, g, gg.dW);
+    hipLaunchKernelGGL(k_dgen_simple<T>, grid16(s.d * s.N), dim3(16, 16), 0, st, s, (const T *)h, g, gg.dW);
     if (dh)
       hipLaunchKernelGGL(k_dh_simple<T>, grid1(s.BT * s.d), dim3(256), 0, st, s, g, (const T *)W,
                          (T *)dh);
   } else {
     hipLaunchKernelGGL(k_dz_simple<T>, grid1(s.BT * s.N), dim3(256), 0, st, s, (const T *)x,
                        (const T *)dy, (const T *)U, g);
-    hipLaunchKernelGGL(k_dU_simple<T>, grid1((int64_t)s.N * s.D * s.k), dim3(256), 0, st, s, gen,
+    hipLaunchKernelGGL(k_dU_simple<T>, grid16((int64_t)s.N * s.D * s.k), dim3(16, 16), 0, st, s, gen,
                        (const T *)x, (const T *)dy, gg.dU);
-    hipLaunchKernelGGL(k_dgen_simple<T>, grid1(s.d * s.N), dim3(256), 0, st, s, (const T *)h, g, gg.dA);
+    hipLaunchKernelGGL(k_dgen_simple<T>, grid16(s.d * s.N), dim3(16, 16), 0, st, s, (const T *)h, g, gg.dA);
     if (dh)
       hipLaunchKernelGGL(k_dh_simple<T>, grid1(s.BT * s.d), dim3(256), 0, st, s, g, (const T *)A,
                          (T *)dh);
