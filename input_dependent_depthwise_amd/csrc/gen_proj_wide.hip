@@ -41,10 +41,10 @@ namespace {
 
 constexpr int kKT = 64;  // k per step
 
-template <int NT, int RG, int KS, int CG>
+template <int NT, int RG, int KS>
 struct WideCfg {
-  static constexpr int NTH = 64 * RG * KS * CG;  // threads per block
-  static constexpr int NTW = NT / CG;            // column tiles per wave
+  static constexpr int NTH = 64 * RG * KS;       // threads per block
+  static constexpr int NTW = NT;                 // column tiles per wave
   static constexpr int BM = RG * 32;             // rows per block
   static constexpr int NP = NT * 32;             // columns per slab (zeros past the weights)
   static constexpr int LDW = NP + 32;            // LDS row stride (bf16)
@@ -54,8 +54,7 @@ struct WideCfg {
   static constexpr int CH = KS * kKT * CPR;      // chunks per stage
   static constexpr int CPT = (CH + NTH - 1) / NTH;  // chunks per thread
   static constexpr size_t LDS = (size_t)2 * STAGE * 2;
-  static_assert(RG * KS == 4, "4 waves per column group");
-  static_assert(NT % CG == 0, "whole column tiles per wave");
+  static_assert(RG * KS == 4, "4 waves per block");
   // the K parts' sums pass through the (then free) stages at the end
   static_assert(KS == 1 || LDS >= (size_t)(KS - 1) * RG * NT * 16 * 64 * 4, "reduction buffer");
 };
@@ -70,17 +69,17 @@ struct Cols {
   float *out;     // the generator values
 };
 
-template <int NT, int RG, int KS, int CG>
-__global__ void __launch_bounds__(64 * RG * KS * CG, 1)
+template <int NT, int RG, int KS>
+__global__ void __launch_bounds__(64 * RG * KS, 1)
 k_gen_proj_wide(const bf16 *__restrict__ h, Cols cols, int64_t M, int K, int n_slabs) {
-  using C = WideCfg<NT, RG, KS, CG>;
+  using C = WideCfg<NT, RG, KS>;
   constexpr int NTW = C::NTW;
   extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
   bf16 *bs = reinterpret_cast<bf16 *>(lds_raw);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rg = wave % RG, ks = (wave / RG) % KS, cg = wave / (RG * KS);
+  const int rg = wave % RG, ks = wave / RG;
   const int slab = (int)(blockIdx.x % n_slabs);
   const int64_t row0 = (int64_t)(blockIdx.x / n_slabs) * C::BM;
   const int col0 = slab * C::NP;
@@ -128,7 +127,7 @@ k_gen_proj_wide(const bf16 *__restrict__ h, Cols cols, int64_t M, int K, int n_s
   // rows 8 (gi / 2) + 4 p + (lr / 4) (p = 0, 1), columns 32 n + 16 (gi % 2) +
   // 4 (lr % 4) .. +3; lane l then holds B[8 (l / 32) + i][32 n + l % 32]
   const int lr = lane & 15, gi = lane >> 4;
-  const int boff = (8 * (gi >> 1) + (lr >> 2)) * C::LDW + 16 * (gi & 1) + 4 * (lr & 3) + 32 * NTW * cg;
+  const int boff = (8 * (gi >> 1) + (lr >> 2)) * C::LDW + 16 * (gi & 1) + 4 * (lr & 3);
   auto bfrags = [&](bf16x8(&b)[NTW], int buf, int q) {
 #pragma unroll
     for (int n = 0; n < NTW; ++n) {
@@ -195,7 +194,6 @@ k_gen_proj_wide(const bf16 *__restrict__ h, Cols cols, int64_t M, int K, int n_s
   if (st + 4 < SH) step(st + 4, a1, 0);
 
   if constexpr (KS > 1) {
-    static_assert(CG == 1, "K parts with one column group");
     // K parts 1 .. KS-1 hand their sums to part 0, added in part order
     float *red = reinterpret_cast<float *>(lds_raw);
     auto slot = [&](int part, int n, int i) { return ((((part - 1) * RG + rg) * NT + n) * 16 + i) * 64 + lane; };
@@ -218,7 +216,7 @@ k_gen_proj_wide(const bf16 *__restrict__ h, Cols cols, int64_t M, int K, int n_s
   // D: lane holds D[8 b + 4 (lane / 32) + r][lane % 32] in element 4 b + r
 #pragma unroll
   for (int n = 0; n < NTW; ++n) {
-    const int col = col0 + 32 * (NTW * cg + n) + (lane & 31);
+    const int col = col0 + 32 * n + (lane & 31);
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
@@ -230,12 +228,12 @@ k_gen_proj_wide(const bf16 *__restrict__ h, Cols cols, int64_t M, int K, int n_s
   }
 }
 
-template <int NT, int RG, int KS, int CG>
+template <int NT, int RG, int KS>
 void launch(const bf16 *h, const Cols &cols, int64_t M, int K, hipStream_t st) {
-  using C = WideCfg<NT, RG, KS, CG>;
+  using C = WideCfg<NT, RG, KS>;
   const size_t lds = C::LDS;
   const int n_slabs = (int)ceil_div(cols.N0, C::NP);
-  hipLaunchKernelGGL((k_gen_proj_wide<NT, RG, KS, CG>), dim3((unsigned)(ceil_div(M, C::BM) * n_slabs)),
+  hipLaunchKernelGGL((k_gen_proj_wide<NT, RG, KS>), dim3((unsigned)(ceil_div(M, C::BM) * n_slabs)),
                      dim3(C::NTH), lds, st, h, cols, M, K, n_slabs);
 }
 
@@ -244,9 +242,9 @@ void launch(const bf16 *h, const Cols &cols, int64_t M, int K, hipStream_t st) {
 template <int NT>
 void launch_nt(const bf16 *h, const Cols &cols, int64_t M, int K, hipStream_t st) {
   if (ceil_div(M, 128) >= 256)
-    launch<NT, 4, 1, 1>(h, cols, M, K, st);
+    launch<NT, 4, 1>(h, cols, M, K, st);
   else
-    launch<NT, 2, 2, 1>(h, cols, M, K, st);
+    launch<NT, 2, 2>(h, cols, M, K, st);
 }
 
 // Tile kernel for 193..256 generator columns and for the fused form: 8 waves
