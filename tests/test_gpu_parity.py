@@ -317,7 +317,7 @@ def test_decode_steps_match_forward(w):
         assert torch.equal(state[:, state.shape[1] - last.shape[1]:], last)
 
 
-@pytest.mark.parametrize("kind", ["lowrank", "headwise"])
+@pytest.mark.parametrize("kind", ["lowrank", "headwise", "headwise_wide"])
 def test_near_size_limit_per_sequence(kind):
     """Tensors just under the 2 GiB limit of the fused kernels' 32-bit byte
     offsets.  The oracle cannot run at this size; a property that holds at any
@@ -331,8 +331,10 @@ def test_near_size_limit_per_sequence(kind):
     T, k = 2048, 4
     if kind == "lowrank":
         d, D, rank, n_heads = 768, 2304, 16, 0
-    else:
+    elif kind == "headwise":
         d, D, rank, n_heads = 512, 3072, 0, 24
+    else:  # 256 generator columns (projection tile, wide dM) and heads of 68 channels
+        d, D, rank, n_heads = 512, 4352, 0, 64
     B = ((1 << 31) - 64 - 1) // (T * D * 2)  # largest batch with B*T*D*2 below the limit
     assert B * T * D * 2 < (1 << 31) - 64
     _note(f"[limit] {kind} B={B} T={T} d={d} D={D} bytes per tensor={B * T * D * 2}")
