@@ -287,7 +287,17 @@ DECODE = [SMALL[0], SMALL[7], SMALL[6], SMALL[12], SMALL[9], SMALL[5], SMALL[10]
           # more than 1024 (sequence, 256-channel) blocks: four sequences per block, the
           # last block with one (161 = 4 * 40 + 1)
           Workload("dec_grouped_lr", B=161, T=6, d=64, D=2048, k=4, kind=LOWRANK, rank=16, seed=41),
-          Workload("dec_grouped_hw_k3", B=161, T=5, d=64, D=2048, k=3, kind=HEADWISE, n_heads=16, seed=42)]
+          Workload("dec_grouped_hw_k3", B=161, T=5, d=64, D=2048, k=3, kind=HEADWISE, n_heads=16, seed=42),
+          # the row-wise generator pass: 256 generator columns with 68-channel heads
+          # straddling the 256-channel blocks; fp32 rows of 32 and 128 columns; four
+          # fp32 sequences per block
+          Workload("dec_hw_hd68_N256", B=3, T=40, d=64, D=4352, k=4, kind=HEADWISE, n_heads=64, seed=43),
+          Workload("dec_fp32_lr_r32_k3", B=5, T=30, d=48, D=256, k=3, kind=LOWRANK, rank=32, dtype="fp32",
+                   seed=44),
+          Workload("dec_fp32_hw_N128", B=2, T=30, d=40, D=512, k=4, kind=HEADWISE, n_heads=32, dtype="fp32",
+                   seed=45),
+          Workload("dec_grouped_fp32_lr", B=161, T=4, d=32, D=2048, k=2, kind=LOWRANK, rank=8, dtype="fp32",
+                   seed=46)]
 
 
 @pytest.mark.parametrize("w", DECODE, ids=[w.name for w in DECODE])
