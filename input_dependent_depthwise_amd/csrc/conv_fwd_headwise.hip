@@ -33,21 +33,42 @@ namespace {
 // the positions come from the per-token table, four tokens per scalar load
 // issued a step ahead (the table is padded, so reads just past the last
 // token stay inside it; their values are never used).
+//
+// Folding (n_fold > 0): the last channel group holds at most 256 channels
+// and the batch an even number of sequences.  Its waves then fold the batch:
+// lanes 0..31 walk the first half of the rows, lanes 32..63 the same channels
+// at the same positions of the second half (rows + BT/2, whole sequences
+// further on), so no wave walks with half its lanes idle.  Runs 0 ..
+// n_fold-1 have a wave for every group (the folded one last), the later runs
+// one for each full group.
 template <int K, bool S2, bool VAR>
 __global__ void __launch_bounds__(256)
 k_fwd_hw_ring(Shape s, const float *__restrict__ u, const bf16 *__restrict__ w0, const bf16 *__restrict__ x,
-              bf16 *__restrict__ y, int n_vg, int n_runs, int tpw) {
+              bf16 *__restrict__ y, int n_vg, int n_runs, int tpw, int n_fold) {
   constexpr int PD = 4;
   constexpr int HS = K <= 4 ? 4 : 8;  // x history slots (and tokens per unrolled block)
   const int lane = threadIdx.x & 63;
   // wave-uniform (scalar) run bounds and sequence position
   const int gw = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (gw >= n_vg * n_runs) return;  // whole waves only; no block-wide synchronisation
-  const int run = gw / n_vg, vg = gw - run * n_vg;
+  const int nv = n_fold > 0 ? n_vg - 1 : n_vg;  // waves of a run past the folded ones
+  if (gw >= n_fold * n_vg + (n_runs - n_fold) * nv) return;  // whole waves only; no block-wide synchronisation
+  int run, vg;
+  if (gw < n_fold * n_vg) {
+    run = gw / n_vg;
+    vg = gw - run * n_vg;
+  } else {
+    const int g2 = gw - n_fold * n_vg;
+    run = n_fold + g2 / nv;
+    vg = g2 - (run - n_fold) * nv;
+  }
   const int D = (int)s.D, BT = (int)s.BT, N = s.N, T = (int)s.T;  // BT*D, BT*N*2 < 2^30 (host-checked)
-  const int c0 = vg * 512 + lane * 8;
+  const bool fold = n_fold > 0 && vg == n_vg - 1;
+  const int cl = fold ? lane & 31 : lane;                  // the lane's place in its half
+  const int hoff = fold ? (lane >> 5) * (BT >> 1) : 0;     // row offset of the lane's half
+  const int BTw = fold ? BT >> 1 : BT;                     // rows of the walk
+  const int c0 = vg * 512 + cl * 8;
   const bool act = c0 < D;
-  const int t_lo = run * tpw, t_hi = min(BT, t_lo + tpw);
+  const int t_lo = run * tpw, t_hi = min(BTw, t_lo + tpw);
   const int ea = act ? c0 / s.hd : 0;
   const int eb = S2 ? min(ea + 1, s.n_heads - 1) : ea;
   int second = 0;  // channels of the later head
@@ -78,10 +99,10 @@ k_fwd_hw_ring(Shape s, const float *__restrict__ u, const bf16 *__restrict__ w0,
   }
 
   auto xoff = [&](int t) -> uint32_t {
-    return (act && t >= 0 && t < t_hi) ? (uint32_t)(t * D + c0) * 2u : kOutside;
+    return (act && t >= 0 && t < t_hi) ? (uint32_t)((t + hoff) * D + c0) * 2u : kOutside;
   };
   auto uoff = [&](int t, int e, int j) -> uint32_t {
-    return (act && t < t_hi) ? (uint32_t)(t * N + e * K + j) * 4u : kOutside;
+    return (act && t < t_hi) ? (uint32_t)((t + hoff) * N + e * K + j) * 4u : kOutside;
   };
   uint4 xr[PD];
   float ua[PD][K], ub[PD][K];
@@ -318,19 +339,23 @@ static bool ring_ok(const Shape &s) {
 template <int K, bool S2>
 static void launch_ring(const Shape &s, const float *u, const void *w0, const void *x, void *y, hipStream_t st) {
   const int n_vg = (int)ceil_div(s.D, 512);
+  // the last group folds the batch when it holds at most 256 channels and
+  // the rows split into two halves of whole sequences
+  const bool fold = !s.packed && s.B % 2 == 0 && s.D - (int64_t)(n_vg - 1) * 512 <= 256;
   // about three waves per SIMD (two for 5..8 taps, which hold that many),
   // runs of a multiple of 4 tokens
-  int tpw = (int)ceil_div(s.BT * n_vg, (K <= 4 ? 3 : 2) * 4 * 256);
+  int tpw = (int)ceil_div(s.BT * (2 * n_vg - (fold ? 1 : 0)), 2 * (K <= 4 ? 3 : 2) * 4 * 256);
   tpw = std::max(16, (tpw + 3) & ~3);
   const int n_runs = (int)ceil_div(s.BT, tpw);
-  const int waves = n_vg * n_runs;
+  const int n_fold = fold ? (int)ceil_div(s.BT / 2, tpw) : 0;
+  const int waves = n_fold * n_vg + (n_runs - n_fold) * (fold ? n_vg - 1 : n_vg);
   const dim3 grid((unsigned)ceil_div(waves, 4)), block(256);
   if (s.seqpos)
     hipLaunchKernelGGL((k_fwd_hw_ring<K, S2, true>), grid, block, 0, st, s, u, (const bf16 *)w0, (const bf16 *)x,
-                       (bf16 *)y, n_vg, n_runs, tpw);
+                       (bf16 *)y, n_vg, n_runs, tpw, n_fold);
   else
     hipLaunchKernelGGL((k_fwd_hw_ring<K, S2, false>), grid, block, 0, st, s, u, (const bf16 *)w0, (const bf16 *)x,
-                       (bf16 *)y, n_vg, n_runs, tpw);
+                       (bf16 *)y, n_vg, n_runs, tpw, n_fold);
 }
 
 template <typename T>

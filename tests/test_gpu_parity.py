@@ -99,7 +99,16 @@ SMALL = [
     # 200 generator columns on the 256-column projection tile (a zero column
     # tail), d_model 136 (a partial 32-k step), 50 heads of 8
     Workload("hw_bf16_N200_d136", B=2, T=150, d=136, D=400, k=4, kind=HEADWISE, n_heads=50, seed=63),
+    # the head-wise forward folds the batch in the last channel group when at
+    # most half a wave of channels is left there and the batch holds an even
+    # number of sequences: four sequences (the halves pair sequence 0 with 2
+    # and 1 with 3), 128-channel heads with 16 lanes left, 24-channel heads
+    # with 2 lanes left
+    Workload("hw_bf16_hd68_fold_B4", B=4, T=130, d=96, D=544, k=4, kind=HEADWISE, n_heads=8, seed=64),
+    Workload("hw_bf16_hd128_fold", B=2, T=211, d=64, D=640, k=4, kind=HEADWISE, n_heads=5, seed=65),
+    Workload("hw_bf16_hd24_fold_k3", B=2, T=150, d=64, D=528, k=3, kind=HEADWISE, n_heads=22, seed=66),
 ]
+_BY_NAME = {w.name: w for w in SMALL}
 
 
 def _run_and_compare(w: Workload, use_cache=True):
@@ -223,7 +232,7 @@ def test_causality(w):
         assert not torch.equal(y0[:, t + 1:], y1[:, t + 1:]), t
 
 
-@pytest.mark.parametrize("w", [SMALL[0], SMALL[7]], ids=["hw", "lr"])
+@pytest.mark.parametrize("w", [SMALL[0], SMALL[7], _BY_NAME["hw_bf16_hd68_fold_B4"]], ids=["hw", "lr", "hw_fold"])
 def test_batch_isolation(w):
     """Changing one sequence's h, x and dy leaves the other sequences' y, dx
     and dh bitwise unchanged (nothing crosses batch rows)."""
