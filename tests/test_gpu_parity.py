@@ -107,6 +107,14 @@ SMALL = [
     Workload("hw_bf16_hd68_fold_B4", B=4, T=130, d=96, D=544, k=4, kind=HEADWISE, n_heads=8, seed=64),
     Workload("hw_bf16_hd128_fold", B=2, T=211, d=64, D=640, k=4, kind=HEADWISE, n_heads=5, seed=65),
     Workload("hw_bf16_hd24_fold_k3", B=2, T=150, d=64, D=528, k=3, kind=HEADWISE, n_heads=22, seed=66),
+    # quad heads (4 mod 8 channels) with 4 taps and more than 128 generator
+    # columns: the backward conv writes the heads within one span straight
+    # into g and only the heads across span boundaries go through partials
+    # (64 heads of 68 as in the Mamba-2 input conv; 40 heads of 68 with a
+    # partial last span; 36 heads of 132)
+    Workload("hw_bf16_hd68_N256", B=2, T=200, d=64, D=4352, k=4, kind=HEADWISE, n_heads=64, seed=67),
+    Workload("hw_bf16_hd68_N160", B=1, T=333, d=96, D=2720, k=4, kind=HEADWISE, n_heads=40, seed=68),
+    Workload("hw_bf16_hd132_N144", B=2, T=150, d=72, D=4752, k=4, kind=HEADWISE, n_heads=36, seed=69),
 ]
 _BY_NAME = {w.name: w for w in SMALL}
 
