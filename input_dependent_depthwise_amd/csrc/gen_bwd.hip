@@ -704,17 +704,18 @@ __global__ void __launch_bounds__(256) k_finalize(Red r0, Red r1, Red r2) {
   const bool vec = n % 4 == 0;
   if (idx < n && vec) {
     const float *src = r->part + idx;
-    int p = sub;
-    for (; p + 7 * lp < np; p += 8 * lp) {
+    // eight partials per batch, all loads issued before the adds (the last
+    // batch masked, so a partial count that is not a multiple of 8 lp does
+    // not end in a chain of one-at-a-time loads)
+    for (int p = sub; p < np; p += 8 * lp) {
       float4 a[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) a[u] = *reinterpret_cast<const float4 *>(src + (int64_t)(p + u * lp) * n);
+      for (int u = 0; u < 8; ++u)
+        a[u] = p + u * lp < np ? *reinterpret_cast<const float4 *>(src + (int64_t)(p + u * lp) * n)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v.x += a[u].x, v.y += a[u].y, v.z += a[u].z, v.w += a[u].w;
-    }
-    for (; p < np; p += lp) {
-      const float4 a = *reinterpret_cast<const float4 *>(src + (int64_t)p * n);
-      v.x += a.x, v.y += a.y, v.z += a.z, v.w += a.w;
+      for (int u = 0; u < 8; ++u)
+        if (p + u * lp < np) v.x += a[u].x, v.y += a[u].y, v.z += a[u].z, v.w += a[u].w;
     }
   } else if (idx < n) {
     float w[4] = {0.f, 0.f, 0.f, 0.f};
