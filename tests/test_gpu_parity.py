@@ -107,6 +107,10 @@ SMALL = [
     Workload("hw_bf16_hd68_fold_B4", B=4, T=130, d=96, D=544, k=4, kind=HEADWISE, n_heads=8, seed=64),
     Workload("hw_bf16_hd128_fold", B=2, T=211, d=64, D=640, k=4, kind=HEADWISE, n_heads=5, seed=65),
     Workload("hw_bf16_hd24_fold_k3", B=2, T=150, d=64, D=528, k=3, kind=HEADWISE, n_heads=22, seed=66),
+    # folded groups with sequences shorter than the filter: one token each
+    # (four sequences), and three tokens with 4 taps
+    Workload("hw_bf16_fold_T1_B4", B=4, T=1, d=32, D=96, k=4, kind=HEADWISE, n_heads=8, seed=70),
+    Workload("hw_bf16_fold_T3_hd68", B=2, T=3, d=32, D=544, k=4, kind=HEADWISE, n_heads=8, seed=71),
     # quad heads (4 mod 8 channels) with 4 taps and more than 128 generator
     # columns: the backward conv writes the heads within one span straight
     # into g and only the heads across span boundaries go through partials
