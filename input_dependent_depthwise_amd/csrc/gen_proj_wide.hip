@@ -250,26 +250,33 @@ void launch_nt(const bf16 *h, const Cols &cols, int64_t M, int K, hipStream_t st
 // Tile kernel for 193..256 generator columns and for the fused form: 8 waves
 // (two per SIMD) over 128 rows x one 256-column slab, wave w on rows 64 (w & 1)
 // .. +63 and columns 64 (w >> 1) .. +63 (2 x 2 fragments of 32 x 32, so every
-// fragment read from LDS serves two MFMAs).  Per step of 32 k the block stages
-// the h tile [128][32] and the weight tile [32][256] in LDS (double-buffered,
-// one barrier per step); every thread loads three 16-byte pieces per step
-// into a ring of eight register sets, so eight steps are in flight.  A
-// fragments are 16-byte reads of h rows (row pitch 80 bytes: the eight rows of
-// a read pass fall on distinct banks); B fragments are two ds_read_b64_tr_b16
-// (row pitch 544 bytes).  Blocks run over the XCDs so that the slabs of one
-// row block share an XCD (and its L2 copy of those rows of h).
-constexpr int kPA = 40;   // LDS row of the h tile: 32 k + pad, bf16
+// fragment read from LDS serves two MFMAs).  Per step of KT k (64 for slabs
+// from one source, 32 for the two-source slab) the block stages the h tile
+// [128][KT] and the weight tile [KT][256] in LDS (double-buffered, one
+// barrier per step); every thread loads 3 KT/32 16-byte pieces per step into
+// a ring of register sets (four, or eight of the smaller steps), so that many
+// steps are in flight.  A fragments are 16-byte reads of h rows (row pitch 80
+// or 144 bytes: the eight rows of a read pass fall on distinct banks); B
+// fragments are two ds_read_b64_tr_b16 (row pitch 544 bytes).  Blocks run
+// over the XCDs so that the slabs of one row block share an XCD (and its L2
+// copy of those rows of h).
 constexpr int kPB = 272;  // LDS row of the weight tile (one k): 256 columns + pad, bf16
 // TWO: the launch's columns may come from both sources (each piece is loaded
 // from both, one of the two loads falling outside its buffer); else every
 // column of the launch lies in W0.  The launch covers the columns from c_lo
 // on; columns below cols.N0 go to xb when it is given.  R register sets.
-template <bool TWO, int R>
+// KT: k per step (32, or 64: twice the pieces per thread and the MFMAs
+// between two barriers; h row pitch 144 bytes, again eight distinct bank
+// groups per read pass).
+template <bool TWO, int R, int KT>
 __global__ void __launch_bounds__(512, 1)
 k_proj_tile(const bf16 *__restrict__ h, Cols cols, int64_t M, int K, int c_lo, int n_slabs, int n_items,
             int slots) {
+  constexpr int kPA = KT + 8;       // LDS row of the h tile: KT k + pad, bf16
+  constexpr int NA = KT / 32;       // h pieces per thread and step
+  constexpr int NB = KT / 16;       // weight pieces per thread and step
   __shared__ __attribute__((aligned(16))) bf16 as_[2][128 * kPA];
-  __shared__ __attribute__((aligned(16))) bf16 bs_[2][32 * kPB];
+  __shared__ __attribute__((aligned(16))) bf16 bs_[2][KT * kPB];
   const int item = (int)(blockIdx.x & 7) * slots + (int)(blockIdx.x >> 3);
   if (item >= n_items) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -282,35 +289,44 @@ k_proj_tile(const bf16 *__restrict__ h, Cols cols, int64_t M, int K, int c_lo, i
   const auto rh = make_rsrc(h + row0 * K, (uint32_t)((int64_t)nrows * K * 2));
   const auto rw0 = make_rsrc(cols.W0, (uint32_t)((int64_t)K * cols.N0 * 2));
   const auto rw1 = make_rsrc(cols.W1, TWO ? (uint32_t)((int64_t)K * cols.N1 * 2) : 0u);
-  const int S = (K + 31) / 32;
+  const int S = (K + KT - 1) / KT;
   const int n_loop = (S + R - 1) / R * R;
 
-  // pieces: 0 -> h (row tid/4, k 8 (tid%4)); 1, 2 -> weight (k e/32, column
-  // 8 (e%32) of the slab, e = tid + 512 (c - 1)); a weight chunk lies wholly
-  // in one source or past both (zeros)
-  const int a_row = tid >> 2, a_k = (tid & 3) * 8;
-  const uint32_t a_base = (uint32_t)((a_row * K + a_k) * 2);
-  int b_r[2], b_c[2];
+  // pieces: 0 .. NA-1 -> h (row e/(KT/8), k 8 (e%(KT/8)), e = tid + 512 a);
+  // NA .. -> weight (k e/32, column 8 (e%32) of the slab, e = tid + 512 b); a
+  // weight chunk lies wholly in one source or past both (zeros)
+  int a_row[NA], a_k[NA];
+  uint32_t a_base[NA];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
+  for (int a = 0; a < NA; ++a) {
+    const int e = tid + 512 * a;
+    a_row[a] = e / (KT / 8);
+    a_k[a] = (e % (KT / 8)) * 8;
+    a_base[a] = (uint32_t)((a_row[a] * K + a_k[a]) * 2);
+  }
+  int b_r[NB], b_c[NB];
+#pragma unroll
+  for (int c = 0; c < NB; ++c) {
     const int e = tid + 512 * c;
     b_r[c] = e >> 5;
     b_c[c] = (e & 31) * 8;
   }
-  uint4 rr[R][3];
+  uint4 rr[R][NA + NB];
   auto load = [&](int set, int st) {
-    const int k0 = st * 32;
-    rr[set][0] = buf_load16(rh, k0 + a_k < K ? a_base + (uint32_t)(k0 * 2) : kOutside);
+    const int k0 = st * KT;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int a = 0; a < NA; ++a)
+      rr[set][a] = buf_load16(rh, k0 + a_k[a] < K ? a_base[a] + (uint32_t)(k0 * 2) : kOutside);
+#pragma unroll
+    for (int c = 0; c < NB; ++c) {
       const int k = k0 + b_r[c], gc = col0 + b_c[c];
       const bool live = k < K;
-      rr[set][1 + c] = buf_load16(rw0, live && gc < cols.N0 ? (uint32_t)(k * cols.N0 + gc) * 2u : kOutside);
+      rr[set][NA + c] = buf_load16(rw0, live && gc < cols.N0 ? (uint32_t)(k * cols.N0 + gc) * 2u : kOutside);
       if constexpr (TWO) {
         const uint4 b1 =
             buf_load16(rw1, live && gc >= cols.N0 && gc < N ? (uint32_t)(k * cols.N1 + gc - cols.N0) * 2u : kOutside);
-        rr[set][1 + c] = make_uint4(rr[set][1 + c].x | b1.x, rr[set][1 + c].y | b1.y, rr[set][1 + c].z | b1.z,
-                                    rr[set][1 + c].w | b1.w);
+        rr[set][NA + c] = make_uint4(rr[set][NA + c].x | b1.x, rr[set][NA + c].y | b1.y, rr[set][NA + c].z | b1.z,
+                                     rr[set][NA + c].w | b1.w);
       }
     }
   };
@@ -332,15 +348,16 @@ k_proj_tile(const bf16 *__restrict__ h, Cols cols, int64_t M, int K, int c_lo, i
 
   auto step = [&](int set, int st) {
     const int buf = set & 1;
-    *reinterpret_cast<uint4 *>(&as_[buf][a_row * kPA + a_k]) = rr[set][0];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) *reinterpret_cast<uint4 *>(&bs_[buf][b_r[c] * kPB + b_c[c]]) = rr[set][1 + c];
+    for (int a = 0; a < NA; ++a) *reinterpret_cast<uint4 *>(&as_[buf][a_row[a] * kPA + a_k[a]]) = rr[set][a];
+#pragma unroll
+    for (int c = 0; c < NB; ++c) *reinterpret_cast<uint4 *>(&bs_[buf][b_r[c] * kPB + b_c[c]]) = rr[set][NA + c];
     __syncthreads();
     load(set, st + R);
     const unsigned char *ab = as_b + buf * (128 * kPA * 2) + a_rd;
-    const unsigned char *bb = bs_b + buf * (32 * kPB * 2) + b_rd;
+    const unsigned char *bb = bs_b + buf * (KT * kPB * 2) + b_rd;
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
+    for (int kh = 0; kh < KT / 16; ++kh) {
       bf16x8 af[2], bfr[2];
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
@@ -389,13 +406,13 @@ k_proj_tile(const bf16 *__restrict__ h, Cols cols, int64_t M, int K, int c_lo, i
 }
 
 // columns [c_lo, c_hi) in slabs of 256
-template <bool TWO, int R>
+template <bool TWO, int R, int KT = 32>
 void launch_tile(const bf16 *h, const Cols &cols, int64_t M, int K, int c_lo, int c_hi, hipStream_t st) {
   const int n_slabs = (int)ceil_div(c_hi - c_lo, 256);
   const int n_items = (int)(ceil_div(M, 128) * n_slabs);
   const int slots = (int)ceil_div(n_items, 8);
   if (n_items == 0) return;
-  hipLaunchKernelGGL((k_proj_tile<TWO, R>), dim3((unsigned)(8 * slots)), dim3(512), 0, st, h, cols, M, K, c_lo,
+  hipLaunchKernelGGL((k_proj_tile<TWO, R, KT>), dim3((unsigned)(8 * slots)), dim3(512), 0, st, h, cols, M, K, c_lo,
                      n_slabs, n_items, slots);
 }
 
@@ -412,7 +429,7 @@ int gen_proj_wide(const Shape &s, const void *h, const void *M, float *out, hipS
   const Cols cols{(const bf16 *)M, nullptr, s.N, 0, nullptr, out};
   const int K = (int)s.d;
   if (s.N > 192) {
-    launch_tile<false, 8>(hh, cols, s.BT, K, 0, s.N, st);
+    launch_tile<false, 4, 64>(hh, cols, s.BT, K, 0, s.N, st);
     trace_end(tr, st);
     return 0;
   }
@@ -440,7 +457,7 @@ int proj_fused(const Shape &s, const void *h, const void *Wp, const void *M, voi
   // the producing projection's whole slabs read Wp alone; the rest (a slab
   // holding both weights' columns, then the generator's) read both sources
   const int whole = (int)(s.D / 256 * 256);
-  launch_tile<false, 8>((const bf16 *)h, cols, s.BT, (int)s.d, 0, whole, st);
+  launch_tile<false, 4, 64>((const bf16 *)h, cols, s.BT, (int)s.d, 0, whole, st);
   launch_tile<true, 4>((const bf16 *)h, cols, s.BT, (int)s.d, whole, (int)s.D + s.N, st);
   trace_end(tr, st);
   return 0;
