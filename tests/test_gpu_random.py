@@ -1,6 +1,7 @@
 """GPU parity on seeded random shapes: the HIP path (through the C ABI)
-against the fp64 oracle, element by element, on 300 problems drawn from a
-fixed generator.
+against the fp64 oracle, element by element, on 300 training-step problems
+drawn from a fixed generator, 80 decode runs and 80 fused-projection
+forwards drawn the same way.
 
 The draw covers the combinations the hand-picked cases take one at a time:
 both generator kinds, fp32 and bf16 I/O, 1 to 8 taps, ranks 1 to 64, head
@@ -92,3 +93,60 @@ def test_random_draw_is_valid():
             assert 1 <= w.rank <= 64
         if cu is not None:
             assert w.B == 1 and cu[0] == 0 and cu[-1] == w.T and all(a <= b for a, b in zip(cu, cu[1:]))
+
+
+N_DECODE = 80
+N_PROJ = 80
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(N_DECODE))
+def test_random_decode(i):
+    """dynconv_decode from a zeroed history, one call per position, against
+    the oracle's forward rows (up to 24 positions), on the sweep's
+    one-row-per-sequence problems; the history then holds the last k-1 rows
+    of x bitwise."""
+    import torch
+
+    import input_dependent_depthwise_amd as dc
+    import oracle
+
+    w, _, _ = _draw(2000 + i)
+    w = w.with_(name=f"rdec{i:03d}", T=min(w.T, 24))
+    print(f"[random decode] {w.name} B={w.B} T={w.T} d={w.d} D={w.D} k={w.k} {w.kind} heads={w.n_heads} "
+          f"rank={w.rank} {w.dtype} bias={w.bias_std > 0}", flush=True)
+    inp = workloads.generate(w, with_dy=False)
+    ref = oracle.forward(gu.oracle_shape(w), inp["h"], inp["x"], W=inp.get("W"), A=inp.get("A"), U=inp.get("U"),
+                         w0=inp.get("w0"))["y"]
+    dev = gu.to_dev(inp)
+    B, T, D = dev["x"].shape
+    state = torch.zeros(B, w.k - 1, D, dtype=dev["x"].dtype, device="cuda") if w.k > 1 else None
+    kw = dict(k=w.k, W=dev.get("W"), A=dev.get("A"), U=dev.get("U"), w0=dev.get("w0"), n_heads=w.n_heads)
+    ys = [dc.dynconv_decode(dev["h"][:, t].clone(), dev["x"][:, t].clone(), state, **kw) for t in range(T)]
+    torch.cuda.synchronize()
+    err = gu.max_rel_err(torch.stack(ys, 1).float().cpu().numpy(), np.asarray(ref).reshape(B, T, D))
+    assert err <= gu.TOL[w.dtype], (w.name, err)
+    if w.k > 1:
+        last = dev["x"][:, max(0, T - (w.k - 1)):T]
+        assert torch.equal(state[:, state.shape[1] - last.shape[1]:], last)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(N_PROJ))
+def test_random_proj(i):
+    """dynconv_fwd_proj: x = h Wp against the oracle's projection (normwise
+    and within the output rounding per element), y against the oracle's
+    forward on the x the GPU wrote, the cache against the oracle's generator
+    values; packed rows included."""
+    import oracle
+    from tests import test_gpu_proj as tp
+
+    w, _, cu = _draw(3000 + i)
+    w = w.with_(name=f"rproj{i:03d}")
+    print(f"[random proj] {w.name} B={w.B} T={w.T} d={w.d} D={w.D} k={w.k} {w.kind} heads={w.n_heads} "
+          f"rank={w.rank} {w.dtype} docs={cu}", flush=True)
+    inp, Wp, x, y, cache = tp._run(w, cu)
+    s = gu.oracle_shape(w, cu)
+    tp._check_x(w, x, oracle.proj(s, inp["h"], Wp))
+    ref = oracle.forward(s, inp["h"], x.cpu(), W=inp.get("W"), A=inp.get("A"), U=inp.get("U"), w0=inp.get("w0"))
+    gu.compare(w, {"y": y, "cache": cache}, {"y": ref["y"], "cache": ref["gen"]})
