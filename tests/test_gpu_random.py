@@ -1,7 +1,7 @@
 """GPU parity on seeded random shapes: the HIP path (through the C ABI)
 against the fp64 oracle, element by element, on 300 training-step problems
-drawn from a fixed generator, 80 decode runs and 80 fused-projection
-forwards drawn the same way.
+drawn from a fixed generator, and 80 decode runs, 80 fused-projection
+forwards and 40 static-filter steps drawn the same way.
 
 The draw covers the combinations the hand-picked cases take one at a time:
 both generator kinds, fp32 and bf16 I/O, 1 to 8 taps, ranks 1 to 64, head
@@ -150,3 +150,22 @@ def test_random_proj(i):
     tp._check_x(w, x, oracle.proj(s, inp["h"], Wp))
     ref = oracle.forward(s, inp["h"], x.cpu(), W=inp.get("W"), A=inp.get("A"), U=inp.get("U"), w0=inp.get("w0"))
     gu.compare(w, {"y": y, "cache": cache}, {"y": ref["y"], "cache": ref["gen"]})
+
+
+N_STATIC = 40
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(N_STATIC))
+def test_random_static(i):
+    """The static filter (no generator, w = w0) on the sweep's widths, taps,
+    lengths, batches and packed rows, against the oracle's head-wise layer
+    with a zero generator."""
+    from tests import test_gpu_static as ts
+
+    w, _, cu = _draw(4000 + i)
+    w = ts._w(f"rstat{i:03d}", w.B, w.T, w.D, w.k, dtype=w.dtype, seed=7000 + i)
+    print(f"[random static] {w.name} B={w.B} T={w.T} D={w.D} k={w.k} {w.dtype} docs={cu}", flush=True)
+    inp = ts._inputs(w)
+    got = ts._gpu(w, inp, cu)
+    gu.compare(w, got, ts._oracle(w, inp, cu), keys=["y", "dx", "dw0"])
