@@ -51,7 +51,13 @@
  * Outputs must not overlap any input or each other.  The workspace must
  * not be used by anything else until the enqueued work has finished.
  * Results are bitwise deterministic for fixed inputs and shapes (no float
- * atomics; every reduction runs in a fixed order).  The library is
+ * atomics; every reduction runs in a fixed order).  A batch whose tensors
+ * are too large for the tuned kernels' 32-bit offsets (a 2 GiB tensor)
+ * runs as consecutive chunks of whole sequences, each the largest the
+ * tuned kernels take; the per-sequence outputs are those of a call on that
+ * chunk alone, the weight gradients the chunks' sums added in chunk order,
+ * and the workspace that of the largest chunk.  Packed rows run whole.
+ * The library is
  * thread-safe.  Its global state is the one-shot event pair that
  * dynconv_trace_next arms, kept per host thread, and the static scratch of
  * dynconv_fwd_noalloc (one array per GPU, with a mutex-guarded table of its

@@ -151,6 +151,38 @@ Plan plan(const Shape &s, int dtype, int pass, bool cached) {
   return pl;
 }
 
+// Problems larger than the tuned kernels' 32-bit offsets allow run as
+// consecutive chunks of whole sequences, each the largest that the tuned
+// kernels take, one after another on the stream (the workspace is reused;
+// the backward adds each chunk's weight-gradient sums to the previous
+// chunks', in chunk order).  Packed rows, and shapes the tuned kernels do not
+// take at any batch size, run whole.
+inline Shape sub_shape(const Shape &s, int64_t nb) {
+  Shape c = s;
+  c.B = nb;
+  c.BT = nb * s.T;
+  return c;
+}
+inline bool tuned(const Shape &s, int dtype, int pass) {
+  if (dtype != DYNCONV_BF16 || !vec_rows(s, dtype)) return false;
+  if (pass == 1) return fast_bwd(s, dtype);
+  return s.kind == DYNCONV_HEADWISE ? fwd_headwise_ring_ok(s) : fast_lowrank(s, dtype);
+}
+int64_t chunk_seqs(const Shape &s, int dtype, int pass) {
+  if (s.packed || s.B <= 1 || tuned(s, dtype, pass) || !tuned(sub_shape(s, 1), dtype, pass)) return s.B;
+  int64_t lo = 1, hi = s.B;  // tuned at lo, not at hi (size limits only tighten as B grows)
+  while (hi - lo > 1) {
+    const int64_t mid = lo + (hi - lo) / 2;
+    if (tuned(sub_shape(s, mid), dtype, pass)) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+// the workspace of a call: that of its largest chunk
+Plan plan_call(const Shape &s, int dtype, int pass, bool cached) {
+  return plan(sub_shape(s, chunk_seqs(s, dtype, pass)), dtype, pass, cached);
+}
+
 inline int launch_status() {
   return hipGetLastError() == hipSuccess ? DYNCONV_OK : DYNCONV_E_HIP;
 }
@@ -213,7 +245,7 @@ int fwd_validate(const dynconv_problem *p, const dynconv_gen *g, const void *h, 
   const void *ptrs[] = {h, x, y, gen_cache, workspace};
   for (const void *q : ptrs)
     if (q && !aligned16(q)) return DYNCONV_E_ALIGN;
-  pl = plan(s, p->dtype, 0, gen_cache != nullptr);
+  pl = plan_call(s, p->dtype, 0, gen_cache != nullptr);
   if (check_ws && (workspace_bytes < pl.total || (pl.total > 0 && !workspace))) return DYNCONV_E_WORKSPACE;
   const int eb = p->dtype == DYNCONV_BF16 ? 2 : 4;
   const Sizes z = sizes(s, eb, p);
@@ -277,6 +309,24 @@ int fwd_launch(const dynconv_problem *p, Shape s, int dtype, const dynconv_gen *
   return launch_status();
 }
 
+// The forward over chunks of whole sequences (one chunk when the tuned
+// kernels take the whole batch).
+int fwd_chunks(const dynconv_problem *p, const Shape &s, const dynconv_gen *g, const void *h, const void *x, void *y,
+               void *gen_cache, void *workspace, hipStream_t stream, const void *Wp = nullptr) {
+  const int64_t nb = chunk_seqs(s, p->dtype, 0);
+  const int64_t eb = p->dtype == DYNCONV_BF16 ? 2 : 4;
+  for (int64_t b0 = 0; b0 < s.B; b0 += nb) {
+    const Shape c = sub_shape(s, std::min<int64_t>(nb, s.B - b0));
+    const int64_t r0 = b0 * s.T;  // first row of the chunk
+    const Plan pl = plan(c, p->dtype, 0, gen_cache != nullptr);
+    const int rc = fwd_launch(p, c, p->dtype, g, h ? (const char *)h + r0 * s.d * eb : nullptr,
+                              (const char *)x + r0 * s.D * eb, (char *)y + r0 * s.D * eb,
+                              gen_cache ? (char *)gen_cache + r0 * s.N * 4 : nullptr, workspace, pl, stream, Wp);
+    if (rc) return rc;
+  }
+  return DYNCONV_OK;
+}
+
 // --- the static scratch of dynconv_fwd_noalloc --------------------------
 // Every GPU the library runs on holds one copy of this array (loaded with
 // the library's device code) until the process ends.  In host code its name
@@ -327,6 +377,61 @@ void trace_end(bool armed, hipStream_t st) {
 
 using namespace dynconv;
 
+// Enqueues a validated backward over one chunk of whole sequences (or the
+// whole problem): acc adds the chunk's weight-gradient sums to what the
+// outputs hold.
+int bwd_launch(const dynconv_problem *p, Shape s, const dynconv_gen *g, const void *h, const void *x, const void *dy,
+               const void *gen_cache, void *dx, void *dh, const dynconv_gen_grad *gg, void *workspace,
+               const Plan &pl, bool acc, hipStream_t stream) {
+  int rc;
+  if (s.packed) {
+    uint16_t *sp = (uint16_t *)((char *)workspace + pl.seqpos);
+    seqpos_fill(p->cu_seqlens, p->n_seqs, s.BT, sp, stream);
+    s.seqpos = sp;
+  }
+  const float *cache = (const float *)gen_cache;
+  if (s.stat) {
+    float *c = (float *)((char *)workspace + pl.zero);
+    zero_fill(c, s.k, stream);
+    cache = c;
+    if (dh) zero_fill_bytes(dh, (size_t)s.BT * s.d * (p->dtype == DYNCONV_BF16 ? 2 : 4), stream);
+    dh = nullptr;
+  } else if (!cache) {
+    float *c = (float *)((char *)workspace + pl.cache);
+    if ((rc = gen_proj(s, p->dtype, g, h, c, workspace, pl, stream))) return rc;
+    cache = c;
+  }
+  char *ws = (char *)workspace;
+  if (fast_bwd(s, p->dtype)) {
+    const BwdLayout L = bwd_layout(s);
+    const GenBwdLayout G = s.stat ? GenBwdLayout{} : gen_bwd_layout(s);
+    float *gpart = (float *)(ws + pl.gpart), *dUp = (float *)(ws + pl.dup), *dw0p = (float *)(ws + pl.dw0p);
+    rc = s.kind == DYNCONV_HEADWISE
+             ? bwd_headwise(s, L, cache, g->w0, x, dy, dx, gpart, dw0p, stream)
+             : bwd_lowrank(s, L, cache, g->U, g->w0, x, dy, dx, gpart, dUp, dw0p, stream);
+    if (rc) return rc;
+    const void *M = s.kind == DYNCONV_HEADWISE ? g->W : g->A;
+    float *dMp = (float *)(ws + pl.dmp);
+    if (!s.stat && (rc = gen_bwd(s, gpart, L.n_slices, L.R, L.Dt, h, M, (bf16 *)(ws + pl.g),
+                                 (bf16 *)(ws + pl.mp), dh, dMp, stream)))
+      return rc;
+    const int64_t Dk = s.D * s.k, dN = s.d * s.N;
+    float *dM = s.stat ? nullptr : (s.kind == DYNCONV_HEADWISE ? gg->dW : gg->dA);
+    if ((rc = finalize(dUp, s.kind == DYNCONV_LOWRANK ? gg->dU : nullptr, (int64_t)s.N * Dk, L.n_ranges,
+                       dw0p, gg->dw0, Dk, L.n_ranges, dMp, dM, dN, G.n_ranges, acc, stream)))
+      return rc;
+    return launch_status();
+  }
+  if (acc) return DYNCONV_E_LIMIT;  // (chunks are formed only where the tuned kernels run)
+  float *gbuf = (float *)(ws + pl.g);
+  if (p->dtype == DYNCONV_BF16)
+    rc = simple_bwd<bf16>(s, cache, g->W, g->A, g->U, g->w0, h, x, dy, dx, dh, *gg, gbuf, stream);
+  else
+    rc = simple_bwd<float>(s, cache, g->W, g->A, g->U, g->w0, h, x, dy, dx, dh, *gg, gbuf, stream);
+  if (rc) return rc;
+  return launch_status();
+}
+
 extern "C" {
 
 int dynconv_abi_version(void) { return DYNCONV_ABI_VERSION; }
@@ -370,7 +475,7 @@ size_t dynconv_workspace_bytes(const dynconv_problem *p, const dynconv_gen *g, i
   Shape s;
   const int base = pass & ~DYNCONV_WS_CACHED;
   if ((base != 0 && base != 1) || check_problem(p, g, s) != DYNCONV_OK) return 0;
-  return plan(s, p->dtype, base, (pass & DYNCONV_WS_CACHED) != 0).total;
+  return plan_call(s, p->dtype, base, (pass & DYNCONV_WS_CACHED) != 0).total;
 }
 
 int dynconv_fwd(const dynconv_problem *p, const dynconv_gen *g, const void *h, const void *x,
@@ -380,7 +485,7 @@ int dynconv_fwd(const dynconv_problem *p, const dynconv_gen *g, const void *h, c
   Plan pl;
   int rc = fwd_validate(p, g, h, x, y, gen_cache, workspace, workspace_bytes, true, s, pl);
   if (rc || s.BT == 0) return rc;
-  return fwd_launch(p, s, p->dtype, g, h, x, y, gen_cache, workspace, pl, stream);
+  return fwd_chunks(p, s, g, h, x, y, gen_cache, workspace, stream);
 }
 
 int dynconv_fwd_proj(const dynconv_problem *p, const dynconv_gen *g, const void *h, const void *Wp, void *x, void *y,
@@ -404,7 +509,7 @@ int dynconv_fwd_proj(const dynconv_problem *p, const dynconv_gen *g, const void 
   const Range outs[] = {{y, z.x}, {gen_cache, gen_cache ? z.cache : 0}, {workspace, pl.total}};
   for (const Range &o : outs)
     if (overlap(o, wp)) return DYNCONV_E_ALIAS;
-  return fwd_launch(p, s, p->dtype, g, h, x, y, gen_cache, workspace, pl, stream, Wp);
+  return fwd_chunks(p, s, g, h, x, y, gen_cache, workspace, stream, Wp);
 }
 
 int dynconv_fwd_noalloc(const dynconv_problem *p, const dynconv_gen *g, const void *h, const void *x, void *y,
@@ -416,7 +521,7 @@ int dynconv_fwd_noalloc(const dynconv_problem *p, const dynconv_gen *g, const vo
   if (pl.total > kScratchBytes) return DYNCONV_E_SCRATCH;
   void *ws = nullptr;
   if ((rc = scratch_ptr(&ws))) return rc;
-  return fwd_launch(p, s, p->dtype, g, h, x, y, gen_cache, ws, pl, stream);
+  return fwd_chunks(p, s, g, h, x, y, gen_cache, ws, stream);
 }
 
 int dynconv_decode(const dynconv_problem *p, const dynconv_gen *g, const void *h, const void *x, void *state,
@@ -482,7 +587,7 @@ int dynconv_bwd(const dynconv_problem *p, const dynconv_gen *g, const void *h, c
   const void *ptrs[] = {h, x, dy, gen_cache, dx, dh, workspace, gg->dW, gg->dA, gg->dU, gg->dw0};
   for (const void *q : ptrs)
     if (q && !aligned16(q)) return DYNCONV_E_ALIGN;
-  const Plan pl = plan(s, p->dtype, 1, gen_cache != nullptr || s.stat);
+  const Plan pl = plan_call(s, p->dtype, 1, gen_cache != nullptr || s.stat);
   if (workspace_bytes < pl.total || (pl.total > 0 && !workspace)) return DYNCONV_E_WORKSPACE;
   const int eb = p->dtype == DYNCONV_BF16 ? 2 : 4;
   const Sizes z = sizes(s, eb, p);
@@ -499,51 +604,19 @@ int dynconv_bwd(const dynconv_problem *p, const dynconv_gen *g, const void *h, c
   for (int a = 0; a < n_out; ++a)
     for (int b = a + 1; b < n_out; ++b)
       if (overlap(outs[a], outs[b])) return DYNCONV_E_ALIAS;
-  if (s.packed) {
-    uint16_t *sp = (uint16_t *)((char *)workspace + pl.seqpos);
-    seqpos_fill(p->cu_seqlens, p->n_seqs, s.BT, sp, stream);
-    s.seqpos = sp;
-  }
-  const float *cache = (const float *)gen_cache;
-  if (s.stat) {
-    float *c = (float *)((char *)workspace + pl.zero);
-    zero_fill(c, s.k, stream);
-    cache = c;
-    if (dh) zero_fill_bytes(dh, (size_t)s.BT * s.d * (p->dtype == DYNCONV_BF16 ? 2 : 4), stream);
-    dh = nullptr;
-  } else if (!cache) {
-    float *c = (float *)((char *)workspace + pl.cache);
-    if ((rc = gen_proj(s, p->dtype, g, h, c, workspace, pl, stream))) return rc;
-    cache = c;
-  }
-  char *ws = (char *)workspace;
-  if (fast_bwd(s, p->dtype)) {
-    const BwdLayout L = bwd_layout(s);
-    const GenBwdLayout G = s.stat ? GenBwdLayout{} : gen_bwd_layout(s);
-    float *gpart = (float *)(ws + pl.gpart), *dUp = (float *)(ws + pl.dup), *dw0p = (float *)(ws + pl.dw0p);
-    rc = s.kind == DYNCONV_HEADWISE
-             ? bwd_headwise(s, L, cache, g->w0, x, dy, dx, gpart, dw0p, stream)
-             : bwd_lowrank(s, L, cache, g->U, g->w0, x, dy, dx, gpart, dUp, dw0p, stream);
+  const int64_t nb = chunk_seqs(s, p->dtype, 1);
+  const int64_t eb64 = eb;
+  for (int64_t b0 = 0; b0 < s.B; b0 += nb) {
+    const Shape c = sub_shape(s, std::min<int64_t>(nb, s.B - b0));
+    const int64_t r0 = b0 * s.T;  // first row of the chunk
+    const Plan pc = plan(c, p->dtype, 1, gen_cache != nullptr || s.stat);
+    rc = bwd_launch(p, c, g, h ? (const char *)h + r0 * s.d * eb64 : nullptr, (const char *)x + r0 * s.D * eb64,
+                    (const char *)dy + r0 * s.D * eb64,
+                    gen_cache ? (const char *)gen_cache + r0 * s.N * 4 : nullptr, (char *)dx + r0 * s.D * eb64,
+                    dh ? (char *)dh + r0 * s.d * eb64 : nullptr, gg, workspace, pc, b0 > 0, stream);
     if (rc) return rc;
-    const void *M = s.kind == DYNCONV_HEADWISE ? g->W : g->A;
-    float *dMp = (float *)(ws + pl.dmp);
-    if (!s.stat && (rc = gen_bwd(s, gpart, L.n_slices, L.R, L.Dt, h, M, (bf16 *)(ws + pl.g),
-                                 (bf16 *)(ws + pl.mp), dh, dMp, stream)))
-      return rc;
-    const int64_t Dk = s.D * s.k, dN = s.d * s.N;
-    float *dM = s.stat ? nullptr : (s.kind == DYNCONV_HEADWISE ? gg->dW : gg->dA);
-    if ((rc = finalize(dUp, s.kind == DYNCONV_LOWRANK ? gg->dU : nullptr, (int64_t)s.N * Dk, L.n_ranges,
-                       dw0p, gg->dw0, Dk, L.n_ranges, dMp, dM, dN, G.n_ranges, stream)))
-      return rc;
-    return launch_status();
   }
-  float *gbuf = (float *)(ws + pl.g);
-  if (p->dtype == DYNCONV_BF16)
-    rc = simple_bwd<bf16>(s, cache, g->W, g->A, g->U, g->w0, h, x, dy, dx, dh, *gg, gbuf, stream);
-  else
-    rc = simple_bwd<float>(s, cache, g->W, g->A, g->U, g->w0, h, x, dy, dx, dh, *gg, gbuf, stream);
-  if (rc) return rc;
-  return launch_status();
+  return DYNCONV_OK;
 }
 
 }  // extern "C"

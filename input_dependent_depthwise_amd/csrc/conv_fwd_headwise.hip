@@ -390,6 +390,8 @@ int fwd_headwise(const Shape &s, const float *u, const void *w0, const void *x, 
   return 0;
 }
 
+bool fwd_headwise_ring_ok(const Shape &s) { return ring_ok(s); }
+
 template int fwd_headwise<float>(const Shape &, const float *, const void *, const void *, void *,
                                  hipStream_t);
 template int fwd_headwise<bf16>(const Shape &, const float *, const void *, const void *, void *,

@@ -677,6 +677,7 @@ struct Red {
   int np;
   int lp;         // lanes per output quad (1, 2, 4 or 8): each sums every lp-th partial
   int64_t lanes;  // threads of this reduction, a whole number of waves
+  int acc;        // 1: add the sum to what out holds (a later chunk of sequences), 0: overwrite
 };
 
 // Four consecutive outputs per group of lp adjacent lanes.  Lane `sub` of a
@@ -732,10 +733,14 @@ __global__ void __launch_bounds__(256) k_finalize(Red r0, Red r1, Red r2) {
   }
   if (sub != 0 || idx >= n || !r->out) return;
   if (vec) {
+    if (r->acc) {
+      const float4 o = *reinterpret_cast<const float4 *>(r->out + idx);
+      v.x = o.x + v.x, v.y = o.y + v.y, v.z = o.z + v.z, v.w = o.w + v.w;
+    }
     *reinterpret_cast<float4 *>(r->out + idx) = v;
   } else {
     const float w[4] = {v.x, v.y, v.z, v.w};
-    for (int c = 0; c < 4 && idx + c < n; ++c) r->out[idx + c] = w[c];
+    for (int c = 0; c < 4 && idx + c < n; ++c) r->out[idx + c] = r->acc ? r->out[idx + c] + w[c] : w[c];
   }
 }
 
@@ -894,16 +899,17 @@ int gen_bwd(const Shape &s, const float *gpart, int n_slices, int R, int Dt, con
 }
 
 // lanes per output quad: enough that each lane sums at most 8 partials
-static gbwd::Red make_red(const float *p, float *o, int64_t n, int np) {
-  gbwd::Red r{p, o, o ? n : 0, np, 1, 0};
+static gbwd::Red make_red(const float *p, float *o, int64_t n, int np, bool acc) {
+  gbwd::Red r{p, o, o ? n : 0, np, 1, 0, acc ? 1 : 0};
   while (r.lp < 8 && r.lp * 8 < np) r.lp *= 2;
   r.lanes = ceil_div(ceil_div(r.n, 4) * r.lp, 64) * 64;
   return r;
 }
 
 int finalize(const float *p0, float *o0, int64_t n0, int np0, const float *p1, float *o1, int64_t n1,
-             int np1, const float *p2, float *o2, int64_t n2, int np2, hipStream_t st) {
-  const gbwd::Red r0 = make_red(p0, o0, n0, np0), r1 = make_red(p1, o1, n1, np1), r2 = make_red(p2, o2, n2, np2);
+             int np1, const float *p2, float *o2, int64_t n2, int np2, bool acc, hipStream_t st) {
+  const gbwd::Red r0 = make_red(p0, o0, n0, np0, acc), r1 = make_red(p1, o1, n1, np1, acc),
+                  r2 = make_red(p2, o2, n2, np2, acc);
   const int64_t lanes = r0.lanes + r1.lanes + r2.lanes;
   if (lanes == 0) return 0;
   const bool tr = trace_begin(DYNCONV_K_FINALIZE, st);

@@ -56,6 +56,8 @@ int fwd_headwise(const Shape &s, const float *u, const void *w0, const void *x, 
 
 // --- fused low-rank forward on matrix cores (conv_fwd_lowrank.hip), bf16 ---
 bool fwd_lowrank_supported(const Shape &s);
+// the head-wise forward's ring kernel takes the shape (bf16)
+bool fwd_headwise_ring_ok(const Shape &s);
 int fwd_lowrank(const Shape &s, const float *z, const void *U, const void *w0, const void *x, void *y,
                 hipStream_t st);
 
@@ -106,8 +108,9 @@ size_t gen_bwd_mp_bytes(const Shape &s);
 size_t gen_bwd_part_bytes(const Shape &s);
 int gen_bwd(const Shape &s, const float *gpart, int n_slices, int R, int Dt, const void *h,
             const void *M, bf16 *g, bf16 *Mp, void *dh, float *dMp, hipStream_t st);
-// out_i[e] = sum_p part_i[p][e]; an output may be NULL to skip it.
+// out_i[e] = sum_p part_i[p][e] (acc: out_i[e] += that sum); an output may be
+// NULL to skip it.
 int finalize(const float *p0, float *o0, int64_t n0, int np0, const float *p1, float *o1, int64_t n1,
-             int np1, const float *p2, float *o2, int64_t n2, int np2, hipStream_t st);
+             int np1, const float *p2, float *o2, int64_t n2, int np2, bool acc, hipStream_t st);
 
 }  // namespace dynconv

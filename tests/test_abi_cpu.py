@@ -455,3 +455,24 @@ def test_static_sizes(L):
     assert dc.dynconv_gen_cache_bytes(p, g) == 0
     assert dc.dynconv_workspace_bytes(p, g, 0) >= 4 * p.k  # the k zero generator values
     assert dc.dynconv_workspace_bytes(p, g, 1) > 0
+
+
+def test_large_batches_run_in_chunks_of_sequences(L):
+    """A batch whose tensors exceed the tuned kernels' 2 GiB offset limit runs
+    as chunks of whole sequences: the workspace is that of the largest chunk
+    (15 sequences of the Mamba-2 shape, the most whose x stays below 2 GiB),
+    whatever the batch up to the boundary's own limit (2^31 elements per
+    tensor: 30 sequences); batches that fit run whole."""
+    def ws(B, pass_):
+        return dc.dynconv_workspace_bytes(prob(B=B, T=16384, d=2048, D=4352), gen_hw(n_heads=64), pass_)
+    for pass_ in (0, 1, 1 | dc.DYNCONV_WS_CACHED):
+        assert 15 * 16384 * 4352 * 2 < (1 << 31) - 64 < 16 * 16384 * 4352 * 2
+        assert ws(16, pass_) == ws(15, pass_) == ws(30, pass_), pass_
+        assert ws(31, pass_) == 0, pass_  # beyond 2^31 elements per tensor
+        assert ws(2, pass_) < ws(15, pass_), pass_
+    # a packed row is never split: planned whole (here on the plain kernels:
+    # the cache slot and the fp32 generator gradient, B*T*N*4 bytes each, and
+    # the position table)
+    p = packed(T=16 * 16384, D=4352, d=2048)
+    BT, N = 16 * 16384, 256
+    assert dc.dynconv_workspace_bytes(p, gen_hw(n_heads=64), 1) >= 2 * BT * N * 4 + BT * 2

@@ -479,3 +479,52 @@ def test_packed_autograd_wrapper():
     assert torch.equal(y.detach(), ref["y"])
     assert torch.equal(leaves["x"].grad, ref["dx"])
     assert torch.equal(leaves["h"].grad, ref["dh"])
+
+
+@pytest.mark.parametrize("kind", ["headwise", "lowrank"])
+def test_large_batch_runs_in_chunks(kind):
+    """Batches whose tensors pass the tuned kernels' 2 GiB offset limit run as
+    chunks of whole sequences on those kernels (the largest chunk that fits,
+    then the rest).  Every per-sequence output equals, bitwise, a run of that
+    chunk alone, and each weight gradient is the first chunk's plus the
+    second's (one fp32 addition, in chunk order)."""
+    import input_dependent_depthwise_amd as dc
+    k = 4
+    if kind == "headwise":  # Mamba-2 channels: 15 sequences per chunk
+        T, d, D, B, first = 16384, 512, 4352, 16, 15
+        gen_cols = 64 * k
+    else:  # 150M QKV channels: 227 sequences per chunk
+        T, d, D, B, first = 2048, 768, 2304, 230, 227
+        gen_cols = 16
+    assert first * T * D * 2 < (1 << 31) - 64 <= (first + 1) * T * D * 2 and B > first
+    _note(f"[chunks] {kind} B={B} T={T} d={d} D={D} bytes per tensor={B * T * D * 2}")
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    bf = torch.bfloat16
+    h = torch.randn(B, T, d, device="cuda", generator=gen).to(bf)
+    x = torch.randn(B, T, D, device="cuda", generator=gen).to(bf)
+    dy = torch.randn(B, T, D, device="cuda", generator=gen).to(bf)
+    w0 = (0.1 * torch.randn(D, k, device="cuda", generator=gen)).to(bf)
+    if kind == "headwise":
+        wk = dict(W=(0.02 * torch.randn(d, gen_cols, device="cuda", generator=gen)).to(bf), n_heads=64)
+        grads = ("dW", "dw0")
+    else:
+        wk = dict(A=(0.02 * torch.randn(d, gen_cols, device="cuda", generator=gen)).to(bf),
+                  U=(0.02 * torch.randn(gen_cols, D * k, device="cuda", generator=gen)).to(bf))
+        grads = ("dA", "dU", "dw0")
+
+    def run(hh, xx, dd):
+        y, cache = dc.dynconv_fwd(hh, xx, k=k, w0=w0, want_cache=True, **wk)
+        g = dc.dynconv_bwd(hh, xx, dd, k=k, w0=w0, gen_cache=cache, need_dh=True, need_dw0=True, **wk)
+        torch.cuda.synchronize()
+        return {"y": y, "cache": cache.view(hh.shape[0], T, -1), **g}
+
+    full = run(h, x, dy)
+    parts = [run(h[a:b].contiguous(), x[a:b].contiguous(), dy[a:b].contiguous()) for a, b in ((0, first), (first, B))]
+    for key in ("y", "cache", "dx", "dh"):
+        assert torch.isfinite(full[key].float()).all(), key
+        assert torch.equal(full[key][:first], parts[0][key]), (kind, key, "first chunk")
+        assert torch.equal(full[key][first:], parts[1][key]), (kind, key, "second chunk")
+    for key in grads:
+        assert torch.equal(full[key], parts[0][key] + parts[1][key]), (kind, key)
+    del h, x, dy, full, parts
+    torch.cuda.empty_cache()
