@@ -12,8 +12,8 @@
 //   dU[q,c*k+j] = sum_t z[t,q] G[t,c,j]          -> one fp32 partial per token range
 //   dw0[c,j]  = sum_t G[t,c,j]                   -> one fp32 partial per token range
 //
-// Work split.  A block (4 waves for rank <= 16, else 8) owns 64 or 128
-// channels and a range of 32-token tiles; wave w owns 16 of the channels.  Per tile the block stages x (rows
+// Work split.  A block (4 waves for rank <= 16, for ranks 33..64 and for
+// 5..8 taps, else 8) owns 64 or 128 channels and a range of 32-token tiles; wave w owns 16 of the channels.  Per tile the block stages x (rows
 // t0-k+1 .. t0+31), dy and z (rows t0 .. t0+31+k-1) in LDS.  Every product is
 // a v_mfma_f32_16x16x32_bf16; a lane (n = lane%16, g = lane/16) holds tokens
 // n and 16+n of the tile and channels 4g .. 4g+3 of the wave's 16:
@@ -44,13 +44,15 @@ namespace dynconv {
 namespace bwdlr {
 
 constexpr int kCW = 16;          // channels per wave
-// Waves per block: 4 (64 channels) when rank <= 16, else 8 (128 channels).
+// Waves per block: 4 (64 channels) when rank <= 16, else 8 (128 channels),
+// except ranks 33..64 and 5..8 taps (below).
 // Two 4-wave blocks share a CU, so one block's barriers overlap the other's
 // work; with a larger rank the per-slice dz partials (rank floats per token
 // and slice) grow too much for the narrower slices.  Filters of 5..8 taps
-// take 4-wave blocks of one wave per SIMD: their U fragments and dU
-// accumulators need more registers than two waves per SIMD leave.
-inline int waves_for(const Shape &s) { return (s.rank <= 16 || s.k > 4) ? 4 : 8; }
+// and ranks 33..64 take 4-wave blocks of one wave per SIMD: their U
+// fragments and dU accumulators need more registers than two waves per SIMD
+// leave.
+inline int waves_for(const Shape &s) { return (s.rank <= 16 || s.rank > 32 || s.k > 4) ? 4 : 8; }
 constexpr int kGRow = 40;        // LDS row of the token-contiguous z^T tile: 32 tokens + pad (bf16)
 // G of one tap in LDS: 32 token rows of 16 channels (32 bytes), 128 bytes of
 // pad after every 8 rows and the row's four 8-byte channel quads swapped in
@@ -95,7 +97,7 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 // its document come from the per-token table, loaded with the tile's other
 // operands; every tile takes the masked path).
 template <int K, int KQ, int NQ, int kW, bool VAR>
-__global__ void __launch_bounds__(kW * 64, K <= 4 ? 2 : 1)
+__global__ void __launch_bounds__(kW * 64, K <= 4 && NQ <= 2 ? 2 : 1)
 k_bwd_lr(Params P) {
   constexpr int kDt = kW * kCW;    // channels per block
   // LDS row of the x / dy tiles (bf16 elements): 36 or 68 dwords, so that the
@@ -509,7 +511,7 @@ BwdLayout bwd_layout(const Shape &s) {
 
 bool bwd_lowrank_supported(const Shape &s) {
   // 32-bit element and byte offsets: x, dy, dx below 2 GiB
-  return s.kind == DYNCONV_LOWRANK && s.D % 16 == 0 && s.k <= 8 && s.rank >= 1 && s.rank <= 32 &&
+  return s.kind == DYNCONV_LOWRANK && s.D % 16 == 0 && s.k <= 8 && s.rank >= 1 && s.rank <= 64 &&
          s.BT * s.D * 2 < ((int64_t)1 << 31) - 64;
 }
 
@@ -558,15 +560,23 @@ int bwd_lowrank(const Shape &s, const BwdLayout &L, const float *z, const void *
     else                                                                                      \
       hipLaunchKernelGGL((bwdlr::k_bwd_lr<K_, KQ_, NQ_, W_, false>), grid, block, 0, st, P); \
   } while (0)
+// ranks 33..64 (three or four 16-row blocks): 4-wave blocks, one wave per
+// SIMD (their U fragments and dU accumulators take most of the registers)
+#define LR_WIDE(K_)                                         \
+  else if (KQ == 2 && NQ == 3) LR(K_, 2, 3, 4);             \
+  else if (KQ == 2 && NQ == 4) LR(K_, 2, 4, 4);             \
+  else if (KQ == 3 && NQ == 4) LR(K_, 3, 4, 4);
 #define LR_K(K_)                                            \
   if (KQ == 1 && NQ == 1 && kw == 4) LR(K_, 1, 1, 4);       \
   else if (KQ == 1 && NQ == 2 && kw == 8) LR(K_, 1, 2, 8);  \
   else if (KQ == 2 && NQ == 2 && kw == 8) LR(K_, 2, 2, 8);  \
+  LR_WIDE(K_)                                               \
   else rc = DYNCONV_E_LIMIT;
 #define LR_K8(K_)                                           \
   if (KQ == 1 && NQ == 1) LR(K_, 1, 1, 4);                  \
   else if (KQ == 1 && NQ == 2) LR(K_, 1, 2, 4);             \
   else if (KQ == 2 && NQ == 2) LR(K_, 2, 2, 4);             \
+  LR_WIDE(K_)                                               \
   else rc = DYNCONV_E_LIMIT;
   switch (s.k) {
     case 1: LR_K(1) break;
@@ -581,6 +591,7 @@ int bwd_lowrank(const Shape &s, const BwdLayout &L, const float *z, const void *
   }
 #undef LR_K8
 #undef LR_K
+#undef LR_WIDE
 #undef LR
   trace_end(tr, st);
   return rc;

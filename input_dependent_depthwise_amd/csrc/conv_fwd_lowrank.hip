@@ -263,7 +263,7 @@ k_fwd_lowrank(Shape s, const float *__restrict__ z, const bf16 *__restrict__ U, 
 bool fwd_lowrank_supported(const Shape &s) {
   // 32-bit element and byte offsets into x, y and z
   const int64_t lim = ((int64_t)1 << 31) - 64;
-  return s.D % 16 == 0 && s.rank + 1 <= 64 && s.k <= 8 && s.BT * s.D * 2 < lim && s.BT * s.rank * 4 < lim &&
+  return s.D % 16 == 0 && s.rank <= 64 && s.k <= 8 && s.BT * s.D * 2 < lim && s.BT * s.rank * 4 < lim &&
          (int64_t)s.rank * s.D * s.k * 2 < lim;
 }
 
@@ -294,6 +294,7 @@ int fwd_lowrank(const Shape &s, const float *z, const void *U, const void *w0, c
     case 2: LAUNCH(K_, 2); break;             \
     case 3: LAUNCH(K_, 3); break;             \
     case 4: LAUNCH(K_, 4); break;             \
+    case 5: LAUNCH(K_, 5); break;             \
     default: rc = DYNCONV_E_LIMIT;            \
   }
   switch (s.k) {
