@@ -511,7 +511,7 @@ BwdLayout bwd_layout(const Shape &s) {
 
 bool bwd_lowrank_supported(const Shape &s) {
   // 32-bit element and byte offsets: x, dy, dx below 2 GiB
-  return s.kind == DYNCONV_LOWRANK && s.D % 16 == 0 && s.k <= 8 && s.rank >= 1 && s.rank <= 64 &&
+  return s.kind == DYNCONV_LOWRANK && s.D % 8 == 0 && s.k <= 8 && s.rank >= 1 && s.rank <= 64 &&
          s.BT * s.D * 2 < ((int64_t)1 << 31) - 64;
 }
 

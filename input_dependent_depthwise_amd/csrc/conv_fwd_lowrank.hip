@@ -263,7 +263,7 @@ k_fwd_lowrank(Shape s, const float *__restrict__ z, const bf16 *__restrict__ U, 
 bool fwd_lowrank_supported(const Shape &s) {
   // 32-bit element and byte offsets into x, y and z
   const int64_t lim = ((int64_t)1 << 31) - 64;
-  return s.D % 16 == 0 && s.rank <= 64 && s.k <= 8 && s.BT * s.D * 2 < lim && s.BT * s.rank * 4 < lim &&
+  return s.D % 8 == 0 && s.rank <= 64 && s.k <= 8 && s.BT * s.D * 2 < lim && s.BT * s.rank * 4 < lim &&
          (int64_t)s.rank * s.D * s.k * 2 < lim;
 }
 

@@ -765,7 +765,8 @@ GenBwdLayout gen_bwd_layout(const Shape &s) {
   L.n_chunks = (int)ceil_div(s.d, 128);
   // about two blocks per CU; an even tile count per range (the dM loop takes
   // tiles in pairs); a range's slice of h stays below 1 GiB (32-bit offsets)
-  int tpb = (int)ceil_div(L.n_tiles, std::max<int64_t>(1, 512 / L.n_chunks));
+  // (at least one pair of tiles per range, also for an empty batch)
+  int tpb = std::max(2, (int)ceil_div(L.n_tiles, std::max<int64_t>(1, 512 / L.n_chunks)));
   tpb += tpb & 1;
   while ((int64_t)tpb * 32 * s.d * 2 >= ((int64_t)1 << 30) && tpb > 2) tpb -= 2;
   L.wide = L.Np > 128;
@@ -773,14 +774,14 @@ GenBwdLayout gen_bwd_layout(const Shape &s) {
     // one block of 8 waves per CU: about 256 (chunk, range) items; whole
     // rings of four tiles per range
     tpb = (int)ceil_div(L.n_tiles, std::max<int64_t>(1, 256 / L.n_chunks));
-    tpb = (int)ceil_div(tpb, gbwd::kWRing) * gbwd::kWRing;
+    tpb = std::max(1, (int)ceil_div(tpb, gbwd::kWRing)) * gbwd::kWRing;
     while ((int64_t)tpb * 32 * std::max<int64_t>(s.d, L.Np) * 2 >= ((int64_t)1 << 30) && tpb > gbwd::kWRing)
       tpb -= gbwd::kWRing;
   }
   L.tpb = tpb;
   L.n_ranges = (int)ceil_div(L.n_tiles, tpb);
   L.n_rb = (int)ceil_div(s.d, 256);
-  int tpr = (int)ceil_div(L.n_tiles, std::max<int64_t>(1, 512 / L.n_rb));
+  int tpr = std::max(2, (int)ceil_div(L.n_tiles, std::max<int64_t>(1, 512 / L.n_rb)));
   tpr += tpr & 1;
   while ((int64_t)tpr * 32 * std::max<int64_t>(s.d, L.Np) * 2 >= ((int64_t)1 << 30) && tpr > 2) tpr -= 2;
   L.tpr = tpr;

@@ -476,3 +476,17 @@ def test_large_batches_run_in_chunks_of_sequences(L):
     p = packed(T=16 * 16384, D=4352, d=2048)
     BT, N = 16 * 16384, 256
     assert dc.dynconv_workspace_bytes(p, gen_hw(n_heads=64), 1) >= 2 * BT * N * 4 + BT * 2
+
+
+@pytest.mark.parametrize("B,T", [(0, 300), (3, 0), (0, 0)])
+def test_empty_batch_sizes(L, B, T):
+    """Workspace sizes of empty batches for every kind, width and dtype: the
+    layouts of the tuned kernels keep at least one tile per token range (an
+    empty batch once divided by a zero tile count there)."""
+    for D in (64, 200, 360, 4352):
+        for dt in (dc.DYNCONV_BF16, dc.DYNCONV_FP32):
+            gens = [gen_lr(rank=r) for r in (1, 16, 33, 64)] + [gen_static()]
+            gens += [gen_hw(n_heads=h) for h in (1, 8, 64) if D % h == 0]
+            for g in gens:
+                for pass_ in (0, 1, 1 | dc.DYNCONV_WS_CACHED):
+                    assert dc.dynconv_workspace_bytes(prob(B=B, T=T, d=128, D=D, k=4, dtype=dt), g, pass_) >= 0
