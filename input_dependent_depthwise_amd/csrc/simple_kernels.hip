@@ -244,17 +244,53 @@ k_dgen_simple(Shape s, const T *__restrict__ h, const float *__restrict__ g, flo
   }, dM);
 }
 
-// dh[row, i] = sum_n g[row, n] M[i, n]      (M = W or A)
+// dh[t, i] = sum_n g[t, n] M[i, n] (M = W or A) as a tiled product: a block of 16 x 16
+// threads computes 64 tokens x 64 columns of d, each thread 4 x 4 of them,
+// with g and M staged in LDS 16 generator columns at a time; every output
+// sums over n in increasing order.
 template <typename T>
 __global__ void __launch_bounds__(256)
-k_dh_simple(Shape s, const float *__restrict__ g, const T *__restrict__ M, T *__restrict__ dh) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= s.BT * s.d) return;
-  const int64_t row = idx / s.d;
-  const int64_t i = idx - row * s.d;
-  float acc = 0.f;
-  for (int n = 0; n < s.N; ++n) acc = fmaf(g[row * s.N + n], to_f32(M[i * s.N + n]), acc);
-  dh[idx] = from_f32<T>(acc);
+k_dh_tiled(Shape s, const float *__restrict__ g, const T *__restrict__ M, T *__restrict__ dh) {
+  __shared__ float gs[16][64 + 4];  // [n][token]
+  __shared__ float ms[16][64 + 4];  // [n][i]
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int64_t t0 = (int64_t)blockIdx.x * 64;
+  const int64_t i0 = (int64_t)blockIdx.y * 64;
+  const int N = s.N;
+  float acc[4][4] = {};
+  for (int n0 = 0; n0 < N; n0 += 16) {
+    // each thread stages 4 values of each tile: row r = threadIdx / 16 + 16 u, column n0 + tx
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = ty + 16 * u;
+      const int n = n0 + tx;
+      const int64_t t = t0 + r, i = i0 + r;
+      gs[tx][r] = (t < s.BT && n < N) ? g[t * N + n] : 0.f;
+      ms[tx][r] = (i < s.d && n < N) ? to_f32(M[i * N + n]) : 0.f;
+    }
+    __syncthreads();
+    const int kn = min(16, N - n0);
+    for (int kk = 0; kk < kn; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) a[q] = gs[kk][4 * ty + q], b[q] = ms[kk][4 * tx + q];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[q][r] = fmaf(a[q], b[r], acc[q][r]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t t = t0 + 4 * ty + q;
+    if (t >= s.BT) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t i = i0 + 4 * tx + r;
+      if (i < s.d) dh[t * s.d + i] = from_f32<T>(acc[q][r]);
+    }
+  }
 }
 
 // Packed documents: per token t, its position in its document and the tokens
@@ -297,6 +333,10 @@ __global__ void __launch_bounds__(256) k_zero16(uint16_t *__restrict__ p, int64_
 // ---------------------------------------------------------------------------
 static inline dim3 grid1(int64_t n) { return dim3((unsigned)ceil_div(n, 256)); }
 static inline dim3 grid16(int64_t n) { return dim3((unsigned)ceil_div(n, 16)); }  // rows_reduce: 16 outputs per block
+// k_dh_tiled: 64 tokens (grid x) by 64 columns of d (grid y) per block
+static inline dim3 dh_grid(const Shape &s) {
+  return dim3((unsigned)ceil_div(s.BT, 64), (unsigned)ceil_div(s.d, 64));
+}
 
 void zero_fill(float *p, int64_t n, hipStream_t st) {
   if (p && n > 0) hipLaunchKernelGGL(k_zero, grid1(n), dim3(256), 0, st, p, n);
@@ -350,7 +390,7 @@ int simple_bwd(const Shape &s, const float *gen, const void *W, const void *A, c
                        (const T *)dy, g);
     hipLaunchKernelGGL(k_dgen_simple<T>, grid16(s.d * s.N), dim3(16, 16), 0, st, s, (const T *)h, g, gg.dW);
     if (dh)
-      hipLaunchKernelGGL(k_dh_simple<T>, grid1(s.BT * s.d), dim3(256), 0, st, s, g, (const T *)W,
+      hipLaunchKernelGGL(k_dh_tiled<T>, dh_grid(s), dim3(256), 0, st, s, g, (const T *)W,
                          (T *)dh);
   } else {
     hipLaunchKernelGGL(k_dz_simple<T>, grid1(s.BT * s.N), dim3(256), 0, st, s, (const T *)x,
@@ -359,7 +399,7 @@ int simple_bwd(const Shape &s, const float *gen, const void *W, const void *A, c
                        (const T *)x, (const T *)dy, gg.dU);
     hipLaunchKernelGGL(k_dgen_simple<T>, grid16(s.d * s.N), dim3(16, 16), 0, st, s, (const T *)h, g, gg.dA);
     if (dh)
-      hipLaunchKernelGGL(k_dh_simple<T>, grid1(s.BT * s.d), dim3(256), 0, st, s, g, (const T *)A,
+      hipLaunchKernelGGL(k_dh_tiled<T>, dh_grid(s), dim3(256), 0, st, s, g, (const T *)A,
                          (T *)dh);
   }
   return 0;
