@@ -16,19 +16,53 @@ namespace dynconv {
 
 // ---------------------------------------------------------------------------
 // out[t, n] = sum_i a[t, i] * m[i, n]      (u = h W, or z = h A)
+// A tiled product: a block of 16 x 16 threads computes 64 rows x 64
+// columns, each thread 4 x 4 of them, with a and m staged in LDS 16 values
+// of i at a time; every output sums over i in increasing order.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ void __launch_bounds__(256)
 k_gen_proj(const T *__restrict__ a, const T *__restrict__ m, float *__restrict__ out, int64_t rows,
            int K, int N) {
-  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (g >= rows * N) return;
-  const int64_t t = g / N;
-  const int n = (int)(g - t * N);
-  const T *at = a + t * K;
-  float acc = 0.f;
-  for (int i = 0; i < K; ++i) acc = fmaf(to_f32(at[i]), to_f32(m[(int64_t)i * N + n]), acc);
-  out[g] = acc;
+  __shared__ float as[16][64 + 4];  // [i][row]
+  __shared__ float ms[16][64 + 4];  // [i][column]
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int64_t t0 = (int64_t)blockIdx.x * 64;
+  const int n0 = (int)blockIdx.y * 64;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += 16) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int r = ty + 16 * u;
+      const int64_t t = t0 + r;
+      as[tx][r] = (t < rows && k0 + tx < K) ? to_f32(a[t * K + k0 + tx]) : 0.f;
+      // m: 16 rows of i, 64 columns; thread (ty, tx) loads columns tx + 16 u of row k0 + ty
+      const int n = n0 + tx + 16 * u;
+      ms[ty][tx + 16 * u] = (k0 + ty < K && n < N) ? to_f32(m[(int64_t)(k0 + ty) * N + n]) : 0.f;
+    }
+    __syncthreads();
+    const int kn = min(16, K - k0);
+    for (int kk = 0; kk < kn; ++kk) {
+      float x[4], y[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) x[q] = as[kk][4 * ty + q], y[q] = ms[kk][4 * tx + q];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[q][r] = fmaf(x[q], y[r], acc[q][r]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t t = t0 + 4 * ty + q;
+    if (t >= rows) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int n = n0 + 4 * tx + r;
+      if (n < N) out[t * N + n] = acc[q][r];
+    }
+  }
 }
 
 // the producing projection: x[t, c] = sum_i h[t, i] * Wp[i, c], written in T
@@ -350,7 +384,8 @@ void zero_fill_bytes(void *p, size_t nbytes, hipStream_t st) {
 template <typename T>
 int simple_gen_proj(const Shape &s, const void *h, const void *M, float *out, hipStream_t st) {
   if (s.BT * s.N == 0) return 0;
-  hipLaunchKernelGGL(k_gen_proj<T>, grid1(s.BT * s.N), dim3(256), 0, st, (const T *)h, (const T *)M,
+  hipLaunchKernelGGL(k_gen_proj<T>, dim3((unsigned)ceil_div(s.BT, 64), (unsigned)ceil_div(s.N, 64)), dim3(256), 0, st,
+                     (const T *)h, (const T *)M,
                      out, s.BT, (int)s.d, s.N);
   return 0;
 }
