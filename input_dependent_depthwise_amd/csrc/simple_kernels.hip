@@ -123,6 +123,60 @@ k_conv_fwd_simple(Shape s, const float *__restrict__ gen, const T *__restrict__ 
   store_vec(y + row * s.D + c0, acc);
 }
 
+// The low-rank forward with the filter of the thread's V channels formed
+// for all K taps at once: per rank q, one z value and the V*K contiguous
+// values of U row q (K 16-byte loads), each tap summing over q in increasing
+// order and then adding the bias, as filter_tap does.
+template <typename T, int K>
+__global__ void __launch_bounds__(256)
+k_conv_fwd_lr(Shape s, const float *__restrict__ gen, const T *__restrict__ U, const T *__restrict__ w0,
+              const T *__restrict__ x, T *__restrict__ y) {
+  constexpr int V = Vec<T>::N;
+  const int64_t nvec = s.D / V;
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= s.BT * nvec) return;
+  const int64_t row = g / nvec;
+  const int64_t c0 = (g - row * nvec) * V;
+  float w[V * K];
+#pragma unroll
+  for (int e = 0; e < V * K; ++e) w[e] = 0.f;
+  const float *zr = gen + row * s.N;
+  const T *ub = U + c0 * K;
+  for (int q = 0; q < s.N; ++q) {
+    const float zq = zr[q];
+    const T *uq = ub + (int64_t)q * s.D * K;
+#pragma unroll
+    for (int m = 0; m < K; ++m) {  // values V m .. V m + V - 1 of the segment
+      float uv[V];
+      load_vec(uq + V * m, uv);
+#pragma unroll
+      for (int i = 0; i < V; ++i) w[V * m + i] = fmaf(zq, uv[i], w[V * m + i]);
+    }
+  }
+  if (w0) {
+#pragma unroll
+    for (int m = 0; m < K; ++m) {
+      float bv[V];
+      load_vec(w0 + c0 * K + V * m, bv);
+#pragma unroll
+      for (int i = 0; i < V; ++i) w[V * m + i] += bv[i];
+    }
+  }
+  // segment value e is channel c0 + e / K, tap e % K
+  const int pos = seq_pos(s, row);
+  float acc[V];
+  load_vec(x + row * s.D + c0, acc);
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    if (j > pos) break;
+    float xv[V];
+    load_vec(x + (row - j) * s.D + c0, xv);
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = fmaf(w[i * K + j], xv[i], acc[i]);
+  }
+  store_vec(y + row * s.D + c0, acc);
+}
+
 // ---------------------------------------------------------------------------
 // dx[row, c] = dy[row, c] + sum_j [t+j<=T-1] w[row+j, c, j] dy[row+j, c]
 // ---------------------------------------------------------------------------
@@ -393,7 +447,19 @@ int simple_gen_proj(const Shape &s, const void *h, const void *M, float *out, hi
 template <typename T>
 int simple_fwd_conv(const Shape &s, const float *gen, const void *U, const void *w0, const void *x,
                     void *y, hipStream_t st) {
-  if (s.D % Vec<T>::N == 0) {
+  if (s.D % Vec<T>::N == 0 && s.kind == DYNCONV_LOWRANK) {
+    const int64_t n = s.BT * (s.D / Vec<T>::N);
+    switch (s.k) {
+#define LRK(K_)                                                                                             \
+  case K_:                                                                                                  \
+    hipLaunchKernelGGL((k_conv_fwd_lr<T, K_>), grid1(n), dim3(256), 0, st, s, gen, (const T *)U, (const T *)w0, \
+                       (const T *)x, (T *)y);                                                               \
+    break;
+      LRK(1) LRK(2) LRK(3) LRK(4) LRK(5) LRK(6) LRK(7) LRK(8)
+#undef LRK
+      default: return DYNCONV_E_LIMIT;
+    }
+  } else if (s.D % Vec<T>::N == 0) {
     const int64_t n = s.BT * (s.D / Vec<T>::N);
     hipLaunchKernelGGL(k_conv_fwd_simple<T>, grid1(n), dim3(256), 0, st, s, gen, (const T *)U,
                        (const T *)w0, (const T *)x, (T *)y);
