@@ -203,6 +203,64 @@ k_conv_dx_simple(Shape s, const float *__restrict__ gen, const T *__restrict__ U
   store_vec(dx + row * s.D + c0, acc);
 }
 
+// The low-rank dx with the filters of all K taps formed together: tap j uses
+// the z row of token row + j, so per rank q the thread reads K z values and
+// the V*K contiguous values of U row q once (K 16-byte loads); each filter
+// value sums over q in increasing order and then adds the bias, as
+// filter_tap does.  Rows past the sequence end are never read (rem).
+template <typename T, int K>
+__global__ void __launch_bounds__(256)
+k_conv_dx_lr(Shape s, const float *__restrict__ gen, const T *__restrict__ U, const T *__restrict__ w0,
+             const T *__restrict__ dy, T *__restrict__ dx) {
+  constexpr int V = Vec<T>::N;
+  const int64_t nvec = s.D / V;
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= s.BT * nvec) return;
+  const int64_t row = g / nvec;
+  const int64_t c0 = (g - row * nvec) * V;
+  const int rem = seq_rem(s, row);
+  float w[V * K];  // value e: channel c0 + e / K, tap e % K
+#pragma unroll
+  for (int e = 0; e < V * K; ++e) w[e] = 0.f;
+  const T *ub = U + c0 * K;
+  for (int q = 0; q < s.N; ++q) {
+    float zq[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) zq[j] = j <= rem ? gen[(row + j) * s.N + q] : 0.f;
+    const T *uq = ub + (int64_t)q * s.D * K;
+#pragma unroll
+    for (int m = 0; m < K; ++m) {
+      float uv[V];
+      load_vec(uq + V * m, uv);
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const int e = V * m + i;
+        w[e] = fmaf(zq[e % K], uv[i], w[e]);
+      }
+    }
+  }
+  if (w0) {
+#pragma unroll
+    for (int m = 0; m < K; ++m) {
+      float bv[V];
+      load_vec(w0 + c0 * K + V * m, bv);
+#pragma unroll
+      for (int i = 0; i < V; ++i) w[V * m + i] += bv[i];
+    }
+  }
+  float acc[V];
+  load_vec(dy + row * s.D + c0, acc);
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    if (j > rem) break;
+    float gv[V];
+    load_vec(dy + (row + j) * s.D + c0, gv);
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = fmaf(w[i * K + j], gv[i], acc[i]);
+  }
+  store_vec(dx + row * s.D + c0, acc);
+}
+
 // The same two convolutions for any D, one thread per element (rows that are
 // not whole 16-byte vectors cannot be read as such).
 template <typename T>
@@ -474,7 +532,19 @@ template <typename T>
 int simple_bwd(const Shape &s, const float *gen, const void *W, const void *A, const void *U,
                const void *w0, const void *h, const void *x, const void *dy, void *dx, void *dh,
                const dynconv_gen_grad &gg, float *g, hipStream_t st) {
-  if (s.D % Vec<T>::N == 0) {
+  if (s.D % Vec<T>::N == 0 && s.kind == DYNCONV_LOWRANK) {
+    const int64_t nv = s.BT * (s.D / Vec<T>::N);
+    switch (s.k) {
+#define LRK(K_)                                                                                             \
+  case K_:                                                                                                  \
+    hipLaunchKernelGGL((k_conv_dx_lr<T, K_>), grid1(nv), dim3(256), 0, st, s, gen, (const T *)U, (const T *)w0, \
+                       (const T *)dy, (T *)dx);                                                             \
+    break;
+      LRK(1) LRK(2) LRK(3) LRK(4) LRK(5) LRK(6) LRK(7) LRK(8)
+#undef LRK
+      default: return DYNCONV_E_LIMIT;
+    }
+  } else if (s.D % Vec<T>::N == 0) {
     const int64_t nv = s.BT * (s.D / Vec<T>::N);
     hipLaunchKernelGGL(k_conv_dx_simple<T>, grid1(nv), dim3(256), 0, st, s, gen, (const T *)U,
                        (const T *)w0, (const T *)dy, (T *)dx);
