@@ -331,6 +331,48 @@ k_dz_simple(Shape s, const T *__restrict__ x, const T *__restrict__ dy, const T 
   g[idx] = acc;
 }
 
+// The same dz for rows of whole 16-byte vectors and K taps: per V channels
+// one load of dy, one per tap of x and K 16-byte loads of U row q; the
+// products are added in the same order (channel, then tap) as above.
+template <typename T, int K>
+__global__ void __launch_bounds__(256)
+k_dz_vec(Shape s, const T *__restrict__ x, const T *__restrict__ dy, const T *__restrict__ U,
+         float *__restrict__ g) {
+  constexpr int V = Vec<T>::N;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= s.BT * s.N) return;
+  const int64_t row = idx / s.N;
+  const int q = (int)(idx - row * s.N);
+  const int pos = seq_pos(s, row);
+  const T *Uq = U + (int64_t)q * s.D * K;
+  float acc = 0.f;
+  for (int64_t c0 = 0; c0 < s.D; c0 += V) {
+    float dv[V], xv[K][V], uv[K * V];
+    load_vec(dy + row * s.D + c0, dv);
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      if (j <= pos) {
+        load_vec(x + (row - j) * s.D + c0, xv[j]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < V; ++i) xv[j][i] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < K; ++m) {
+      float t[V];
+      load_vec(Uq + c0 * K + V * m, t);
+#pragma unroll
+      for (int i = 0; i < V; ++i) uv[V * m + i] = t[i];
+    }
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+#pragma unroll
+      for (int j = 0; j < K; ++j) acc = fmaf(dv[i] * xv[j][i], uv[i * K + j], acc);
+  }
+  g[idx] = acc;
+}
+
 
 // Sums over rows for 16 outputs per block: thread (tx, ty) of a 16 x 16
 // block adds term(o, row) for output o = 16 blockIdx.x + tx over rows ty,
@@ -564,8 +606,21 @@ int simple_bwd(const Shape &s, const float *gen, const void *W, const void *A, c
       hipLaunchKernelGGL(k_dh_tiled<T>, dh_grid(s), dim3(256), 0, st, s, g, (const T *)W,
                          (T *)dh);
   } else {
-    hipLaunchKernelGGL(k_dz_simple<T>, grid1(s.BT * s.N), dim3(256), 0, st, s, (const T *)x,
-                       (const T *)dy, (const T *)U, g);
+    if (s.D % Vec<T>::N == 0) {
+      switch (s.k) {
+#define DZK(K_)                                                                                             \
+  case K_:                                                                                                  \
+    hipLaunchKernelGGL((k_dz_vec<T, K_>), grid1(s.BT * s.N), dim3(256), 0, st, s, (const T *)x, (const T *)dy, \
+                       (const T *)U, g);                                                                    \
+    break;
+        DZK(1) DZK(2) DZK(3) DZK(4) DZK(5) DZK(6) DZK(7) DZK(8)
+#undef DZK
+        default: return DYNCONV_E_LIMIT;
+      }
+    } else {
+      hipLaunchKernelGGL(k_dz_simple<T>, grid1(s.BT * s.N), dim3(256), 0, st, s, (const T *)x,
+                         (const T *)dy, (const T *)U, g);
+    }
     hipLaunchKernelGGL(k_dU_simple<T>, grid16((int64_t)s.N * s.D * s.k), dim3(16, 16), 0, st, s, gen,
                        (const T *)x, (const T *)dy, gg.dU);
     hipLaunchKernelGGL(k_dgen_simple<T>, grid16(s.d * s.N), dim3(16, 16), 0, st, s, (const T *)h, g, gg.dA);
