@@ -395,19 +395,44 @@ __device__ __forceinline__ void rows_reduce(int64_t n_out, int64_t rows, F term,
   }
 }
 
-// low-rank: dU[q, c*k+j] = sum_rows z[row, q] G[row, c, j]
+// low-rank: dU[q, c*k+j] = sum_rows z[row, q] G[row, c, j], with each
+// G[row, c, j] formed once for 16 ranks: block (16,
+// 16) takes 16 consecutive (c, j) columns (tx) and ranks q0 .. q0 + 15 (grid
+// y); thread row group ty adds rows ty, ty + 16, ... in ascending order, and
+// the 16 row groups are added in order at the end, as rows_reduce does.
 template <typename T>
 __global__ void __launch_bounds__(256)
-k_dU_simple(Shape s, const float *__restrict__ z, const T *__restrict__ x, const T *__restrict__ dy,
-            float *__restrict__ dU) {
+k_dU_rows(Shape s, const float *__restrict__ z, const T *__restrict__ x, const T *__restrict__ dy,
+          float *__restrict__ dU) {
+  __shared__ float part[16][16][17];  // [row group][rank][column]
+  const int tx = threadIdx.x, ty = threadIdx.y;
   const int64_t Dk = s.D * s.k;
-  rows_reduce((int64_t)s.N * Dk, s.BT, [&](int64_t idx, int64_t row) {
-    const int q = (int)(idx / Dk);
-    const int64_t m = idx - (int64_t)q * Dk;
+  const int64_t m = (int64_t)blockIdx.x * 16 + tx;
+  const int q0 = (int)blockIdx.y * 16;
+  const int nq = min(16, s.N - q0);
+  float acc[16];
+#pragma unroll
+  for (int qq = 0; qq < 16; ++qq) acc[qq] = 0.f;
+  if (m < Dk) {
     const int64_t c = m / s.k;
     const int j = (int)(m - c * s.k);
-    return z[row * s.N + q] * gtap(s, x, dy, row, c, j);
-  }, dU);
+    for (int64_t row = ty; row < s.BT; row += 16) {
+      const float G = gtap(s, x, dy, row, c, j);
+      const float *zr = z + row * s.N + q0;
+#pragma unroll
+      for (int qq = 0; qq < 16; ++qq)
+        if (qq < nq) acc[qq] += zr[qq] * G;
+    }
+  }
+#pragma unroll
+  for (int qq = 0; qq < 16; ++qq) part[ty][qq][tx] = acc[qq];
+  __syncthreads();
+  // thread (tx, ty) finishes rank q0 + ty of column m
+  if (m < Dk && ty < nq) {
+    float t = 0.f;
+    for (int r = 0; r < 16; ++r) t += part[r][ty][tx];
+    dU[(int64_t)(q0 + ty) * Dk + m] = t;
+  }
 }
 
 // dw0[c, j] = sum_rows G[row, c, j]
@@ -621,8 +646,8 @@ int simple_bwd(const Shape &s, const float *gen, const void *W, const void *A, c
       hipLaunchKernelGGL(k_dz_simple<T>, grid1(s.BT * s.N), dim3(256), 0, st, s, (const T *)x,
                          (const T *)dy, (const T *)U, g);
     }
-    hipLaunchKernelGGL(k_dU_simple<T>, grid16((int64_t)s.N * s.D * s.k), dim3(16, 16), 0, st, s, gen,
-                       (const T *)x, (const T *)dy, gg.dU);
+    hipLaunchKernelGGL(k_dU_rows<T>, dim3((unsigned)ceil_div((int64_t)s.D * s.k, 16), (unsigned)ceil_div(s.N, 16)),
+                       dim3(16, 16), 0, st, s, gen, (const T *)x, (const T *)dy, gg.dU);
     hipLaunchKernelGGL(k_dgen_simple<T>, grid16(s.d * s.N), dim3(16, 16), 0, st, s, (const T *)h, g, gg.dA);
     if (dh)
       hipLaunchKernelGGL(k_dh_tiled<T>, dh_grid(s), dim3(256), 0, st, s, g, (const T *)A,
