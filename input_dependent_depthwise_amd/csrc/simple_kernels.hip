@@ -315,6 +315,31 @@ k_du_simple(Shape s, const T *__restrict__ x, const T *__restrict__ dy, float *_
   g[idx] = acc;
 }
 
+// The same du for heads of whole 16-byte vectors: 16-byte loads of dy and of
+// x at lag j, the products added in the same channel order.
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_du_vec(Shape s, const T *__restrict__ x, const T *__restrict__ dy, float *__restrict__ g) {
+  constexpr int V = Vec<T>::N;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= s.BT * s.N) return;
+  const int64_t row = idx / s.N;
+  const int n = (int)(idx - row * s.N);
+  const int e = n / s.k, j = n - e * s.k;
+  float acc = 0.f;
+  if (j <= seq_pos(s, row)) {
+    const T *dr = dy + row * s.D, *xr = x + (row - j) * s.D;
+    for (int64_t c0 = (int64_t)e * s.hd; c0 < (int64_t)(e + 1) * s.hd; c0 += V) {
+      float dv[V], xv[V];
+      load_vec(dr + c0, dv);
+      load_vec(xr + c0, xv);
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc += dv[i] * xv[i];
+    }
+  }
+  g[idx] = acc;
+}
+
 // low-rank: g[row, q] = dz = sum_{c,j} G[row, c, j] U[q, c*k+j]
 template <typename T>
 __global__ void __launch_bounds__(256)
@@ -624,8 +649,11 @@ int simple_bwd(const Shape &s, const float *gen, const void *W, const void *A, c
                        (const T *)dy, gg.dw0);
   if (s.stat) return 0;  // no generator (the caller has cleared dh)
   if (s.kind == DYNCONV_HEADWISE) {
-    hipLaunchKernelGGL(k_du_simple<T>, grid1(s.BT * s.N), dim3(256), 0, st, s, (const T *)x,
-                       (const T *)dy, g);
+    if (s.hd % Vec<T>::N == 0)
+      hipLaunchKernelGGL(k_du_vec<T>, grid1(s.BT * s.N), dim3(256), 0, st, s, (const T *)x, (const T *)dy, g);
+    else
+      hipLaunchKernelGGL(k_du_simple<T>, grid1(s.BT * s.N), dim3(256), 0, st, s, (const T *)x,
+                         (const T *)dy, g);
     hipLaunchKernelGGL(k_dgen_simple<T>, grid16(s.d * s.N), dim3(16, 16), 0, st, s, (const T *)h, g, gg.dW);
     if (dh)
       hipLaunchKernelGGL(k_dh_tiled<T>, dh_grid(s), dim3(256), 0, st, s, g, (const T *)W,
